@@ -1,0 +1,343 @@
+"""Plain, slow, float64 CPU oracle of the DSA indexer -> top-k -> sparse MLA path
+with GLM-5.2 cross-layer IndexShare.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's CPU
+baseline leg may import this module.  It shares no code with the HIP library
+and imports nothing from it.
+
+What it follows (the pages do not print the formulas; readings are marked):
+  * GLM-5.2 IndexShare page, section 1 "What DSA does before sharing": per query,
+    a light indexer scores the prefix tokens, the top-k positions are kept, and
+    the main attention runs only over those positions.
+  * Same page, section 2 "What IndexShare changes", the layer-pattern figure and
+    the "What is actually shared?" table: full layers compute and cache the top-k
+    indices; shared layers reuse the nearest preceding full layer's indices (only
+    the indices are shared) and still compute their own attention.
+  * Megatron-Bridge GLM-5 DSA pull request, commit fixing top-k for short packed
+    sequences: when fewer candidates than index_topk exist, take them all and pad
+    to the fixed index_topk width with -1.
+  * Same pull request, commit on the wrong-dimension-count parse: the MLA latent
+    row is kv_lora_rank 512 + qk_rope_head_dim 64 = 576 values.
+  * MaxText "add glm5.2 indexshare" pull request, description and review thread:
+    per-layer full/shared list, F layers active, S layers reuse the donor.
+  Reading (the pages do not print it): index score
+      I[t, s] = sum_h w[t, h] * max(0, q[t, h, :] . k[s, g(h), :]),
+  g(h) = h when there is one key head per query head, else 0.  Top-k ties go to
+  the lower position and the kept positions are listed in ascending order.
+  Sparse MLA is the absorbed form: keys are whole latent rows (Dc + Dr values),
+  values are their first Dc values.
+
+Parity pins live in tests/test_oracle_pins.py.  Parity against values printed on
+the pages is unpinned: the pages print no score, index or attention values.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# ------------------------------------------------------------------ input decoding
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64: a bf16 is the top half of a float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return u.view(np.float32).astype(np.float64)
+
+
+def _e4m3fn_table() -> np.ndarray:
+    """Value of every OCP e4m3fn code: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    Exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; there is no
+    infinity, so the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    vals = np.empty(256, np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            vals[code] = np.nan
+        elif e == 0:
+            vals[code] = sign * m * 2.0 ** -9
+        else:
+            vals[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return vals
+
+
+E4M3FN = _e4m3fn_table()
+
+
+def decode(stored: np.ndarray, dtype: str, scale: np.ndarray | None = None) -> np.ndarray:
+    """Stored input -> float64.  fp8 values are multiplied by their per-vector scale."""
+    if dtype == "f32":
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(stored)
+    if dtype == "fp8":
+        v = E4M3FN[np.asarray(stored, dtype=np.uint8)]
+        if scale is not None:
+            v = v * np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None]
+        return v
+    raise ValueError(dtype)
+
+
+# ------------------------------------------------------------------ indexer score
+
+
+def index_scores_loop(q: np.ndarray, k: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Index score by explicit loops (tiny inputs only).
+
+    q [T, H, D], k [S, Hk, D], w [T, H] (float64) -> I [T, S].
+    """
+    T, H, D = q.shape
+    S, Hk, _ = k.shape
+    out = np.zeros((T, S))
+    for t in range(T):
+        for s in range(S):
+            acc = 0.0
+            for h in range(H):
+                g = h if Hk == H else 0
+                dot = 0.0
+                for d in range(D):
+                    dot += q[t, h, d] * k[s, g, d]
+                acc += w[t, h] * max(dot, 0.0)
+            out[t, s] = acc
+    return out
+
+
+def index_scores_row(q_row: np.ndarray, k: np.ndarray, w_row: np.ndarray,
+                     key_start: int, key_end: int) -> np.ndarray:
+    """Index scores of one query over its candidates [key_start, key_end).
+
+    q_row [H, D], k [S, Hk, D], w_row [H] (float64) -> [key_end - key_start].
+    """
+    H = q_row.shape[0]
+    kk = k[key_start:key_end]                                   # [n, Hk, D]
+    if kk.shape[1] == H:
+        dots = np.einsum("hd,shd->sh", q_row, kk)
+    else:
+        dots = kk[:, 0, :] @ q_row.T                            # [n, H]
+    return np.maximum(dots, 0.0) @ w_row
+
+
+def index_scores(q: np.ndarray, k: np.ndarray, w: np.ndarray,
+                 key_start: np.ndarray, key_end: np.ndarray) -> np.ndarray:
+    """q [B,T,H,D], k [B,S,Hk,D], w [B,T,H] -> I [B,T,S], NaN outside each candidate range."""
+    B, T = q.shape[:2]
+    S = k.shape[1]
+    out = np.full((B, T, S), np.nan)
+    for b in range(B):
+        for t in range(T):
+            ks, ke = int(key_start[b, t]), int(key_end[b, t])
+            out[b, t, ks:ke] = index_scores_row(q[b, t], k[b], w[b, t], ks, ke)
+    return out
+
+
+# ------------------------------------------------------------------ top-k
+
+
+def topk_row(scores: np.ndarray, key_start: int, key_end: int, k: int):
+    """Top-k of one row by a full stable sort.
+
+    ``scores`` holds the candidates' scores in position order (length
+    key_end - key_start; a longer array is cut to it).  Returns (indices int32
+    [k], tau): the chosen absolute positions in ascending order followed by -1,
+    and the k-th largest score (None when every candidate is taken).
+    """
+    n = max(key_end - key_start, 0)
+    s = np.asarray(scores, dtype=np.float64)[:n]
+    out = np.full(k, -1, np.int32)
+    if n <= k:
+        out[:n] = np.arange(key_start, key_end, dtype=np.int32)
+        return out, None
+    pos = np.arange(key_start, key_end, dtype=np.int64)
+    order = np.lexsort((pos, -s))           # score descending, then position ascending
+    keep = order[:k]
+    tau = s[order[k - 1]]
+    out[:] = np.sort(pos[keep]).astype(np.int32)
+    return out, float(tau)
+
+
+def topk(scores: np.ndarray, key_start: np.ndarray, key_end: np.ndarray, k: int):
+    """scores [B,T,S] (absolute positions) -> (indices [B,T,k] int32, tau [B,T] with NaN where n <= k)."""
+    B, T = scores.shape[:2]
+    idx = np.full((B, T, k), -1, np.int32)
+    tau = np.full((B, T), np.nan)
+    for b in range(B):
+        for t in range(T):
+            ks, ke = int(key_start[b, t]), int(key_end[b, t])
+            i, tt = topk_row(scores[b, t, ks:ke], ks, ke, k)
+            idx[b, t] = i
+            if tt is not None:
+                tau[b, t] = tt
+    return idx, tau
+
+
+# ------------------------------------------------------------------ sparse MLA
+
+
+def sparse_mla_row(q_row: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float, Dc: int):
+    """Attention of one query over the listed latent rows (gather form).
+
+    q_row [Hm, R], kv [S, R], idx [k] (entries outside [0, S) are skipped).
+    Returns (o [Hm, Dc], lse [Hm]); an empty selection gives o = 0, lse = -inf.
+    """
+    S = kv.shape[0]
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[(sel >= 0) & (sel < S)]
+    Hm = q_row.shape[0]
+    if sel.size == 0:
+        return np.zeros((Hm, Dc)), np.full(Hm, -np.inf)
+    c = kv[sel]                                                 # [J, R]
+    z = sm_scale * (q_row @ c.T)                                # [Hm, J]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e / l) @ c[:, :Dc]
+    lse = (m + np.log(l))[:, 0]
+    return o, lse
+
+
+def sparse_mla_dense_masked_row(q_row: np.ndarray, kv: np.ndarray, idx: np.ndarray,
+                                sm_scale: float, Dc: int):
+    """Same attention in the dense-masked form: logits over all S rows, -inf off the selection.
+
+    (The MaxText path carries the selection as an indexer mask over the prefix.)
+    Each position counts once even if listed twice.
+    """
+    S = kv.shape[0]
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[(sel >= 0) & (sel < S)]
+    Hm = q_row.shape[0]
+    mask = np.zeros(S, bool)
+    mask[sel] = True
+    if not mask.any():
+        return np.zeros((Hm, Dc)), np.full(Hm, -np.inf)
+    z = sm_scale * (q_row @ kv.T)                               # [Hm, S]
+    z = np.where(mask[None, :], z, -np.inf)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    return (e / l) @ kv[:, :Dc], (m + np.log(l))[:, 0]
+
+
+def sparse_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float, Dc: int):
+    """q [B,T,Hm,R], kv [B,S,R], idx [B,T,k] -> (o [B,T,Hm,Dc], lse [B,T,Hm])."""
+    B, T, Hm, _ = q.shape
+    o = np.zeros((B, T, Hm, Dc))
+    lse = np.zeros((B, T, Hm))
+    for b in range(B):
+        for t in range(T):
+            o[b, t], lse[b, t] = sparse_mla_row(q[b, t], kv[b], idx[b, t], sm_scale, Dc)
+    return o, lse
+
+
+# ------------------------------------------------------------------ IndexShare
+
+
+class NoDonorError(ValueError):
+    """A shared layer has no preceding full layer and no valid cached indices."""
+
+
+class StaleCacheError(ValueError):
+    """Cached indices were produced for another call (tag or shape mismatch)."""
+
+
+def parse_pattern(pattern: str, n_layers: int):
+    """Repeat a full/shared pattern string such as "FSSS" over n_layers layers."""
+    p = pattern.upper()
+    if not p or set(p) - {"F", "S"}:
+        raise ValueError(pattern)
+    return ["full" if p[i % len(p)] == "F" else "shared" for i in range(n_layers)]
+
+
+def donor_map(types, cache_valid: bool = False):
+    """donor[l] = the nearest full layer j <= l.  A leading shared layer takes the
+    cached indices (donor -1) if ``cache_valid``; otherwise it has no donor."""
+    donors, last = [], None
+    for l, ty in enumerate(types):
+        if ty == "full":
+            last = l
+        elif ty != "shared":
+            raise ValueError(ty)
+        if last is None:
+            if not cache_valid:
+                raise NoDonorError(f"layer {l} is shared and has no preceding full layer")
+            donors.append(-1)
+        else:
+            donors.append(last)
+    return donors
+
+
+def served_group_sizes(types):
+    """Number of layers (itself included) that use each full layer's indices."""
+    donors = donor_map(types)
+    return [sum(1 for d in donors if d == l) for l, ty in enumerate(types) if ty == "full"]
+
+
+def group_forward(layers, types, key_start, key_end, topk_k, sm_scale, Dc, cache=None, tag=0):
+    """Whole layer group.
+
+    ``layers[l]`` is a dict of float64 inputs: 'mla_q' [B,T,Hm,R], 'kv' [B,S,R]
+    and, on full layers, 'idx_q' [B,T,H,D], 'idx_k' [B,S,Hk,D], 'w' [B,T,H].
+    ``cache`` is None or a dict {'indices', 'tag'} carried from an earlier call.
+    Returns dict(indices=[per layer], out=[...], lse=[...], donors=[...], cache=...).
+    """
+    donors = donor_map(types, cache_valid=cache is not None)
+    if types and types[0] == "shared":
+        if cache is None:
+            raise NoDonorError("first layer is shared and there is no cached indices")
+        if cache["tag"] != tag or cache["indices"].shape != (key_end.shape[0], key_end.shape[1], topk_k):
+            raise StaleCacheError("cached indices belong to another call")
+    cur = None if cache is None else cache["indices"]
+    res = {"indices": [], "out": [], "lse": [], "donors": donors}
+    for l, ty in enumerate(types):
+        L = layers[l]
+        if ty == "full":
+            sc = index_scores(L["idx_q"], L["idx_k"], L["w"], key_start, key_end)
+            cur, _ = topk(sc, key_start, key_end, topk_k)
+        o, lse = sparse_mla(L["mla_q"], L["kv"], cur, sm_scale, Dc)
+        res["indices"].append(cur)
+        res["out"].append(o)
+        res["lse"].append(lse)
+    res["cache"] = {"indices": cur, "tag": tag}
+    return res
+
+
+def group_stats(types, key_start, key_end, *, H, D, Hk, idx_bytes, idx_scaled, topk_k,
+                Hm, Dc, Dr, mla_bytes, S):
+    """Analytic work of one group call (counts, not timings).
+
+    indexer_flops  = 2*H*D per (query, candidate) pair, per full layer
+    indexer_bytes  = index q + w (+ q scales) + index k of each item's prefix
+                     (+ k scales) + fp32 scores written, per full layer
+    topk_bytes     = fp32 scores read + int32 indices written, per full layer
+    attn_flops     = 2*Hm*(2*Dc + Dr) per (query, selected row), per layer
+    attn_bytes     = gathered rows + q read + out written, per layer
+    """
+    ks = np.asarray(key_start, np.int64)
+    ke = np.asarray(key_end, np.int64)
+    n = np.maximum(ke - ks, 0)
+    rows = n.size
+    B = ke.shape[0]
+    sum_n = int(n.sum())
+    sum_j = int(np.minimum(n, topk_k).sum())
+    prefix = int(np.minimum(ke.max(axis=1), S).sum()) if rows else 0
+    n_full = sum(1 for t in types if t == "full")
+    n_sh = len(types) - n_full
+    sc = 4 if idx_scaled else 0
+    idx_b = rows * H * (D * idx_bytes + 4 + sc) + prefix * Hk * (D * idx_bytes + sc) + 4 * sum_n
+    R = Dc + Dr
+    return {
+        "n_full": n_full,
+        "n_shared": n_sh,
+        "indexer_flops": float(n_full * 2 * H * D * sum_n),
+        "indexer_bytes": float(n_full * idx_b),
+        "topk_bytes": float(n_full * (4 * sum_n + 4 * rows * topk_k)),
+        "attn_flops": float(len(types) * 2 * Hm * (2 * Dc + Dr) * sum_j),
+        "attn_bytes": float(len(types) * (sum_j * R * mla_bytes + rows * Hm * R * mla_bytes
+                                          + rows * Hm * Dc * mla_bytes)),
+        "batch": B,
+    }
