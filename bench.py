@@ -1,0 +1,222 @@
+"""Throughput of one IndexShare layer group on one MI355X.
+
+A step is one dsa_group_forward over the workload's whole layer list (indexer
+scores -> top-k -> sparse MLA on full layers, sparse MLA with the cached indices
+on shared layers) for one batch of synthetic queries whose inputs are already
+resident in HBM.  Prints one JSON line:
+  value          query tokens/s per 4-layer group = B*T / (step time) * n_layers / 4
+  roofline       the dominant kernel (sparse MLA on a prefill workload): algorithmic
+                 FLOPs per launch / mean launch time (HIP events recorded by the
+                 library around each launch on the timed stream) vs bf16 MFMA peak
+  kernels        the same for every kernel family (indexer vs MFMA peak, top-k vs HBM)
+  cpu_baseline   the CPU oracle on a bounded sample of query rows of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s per 4-layer F/S group (indexer+top-k+sparse MLA); MFMA% & HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the dominant kernel (KiB per dispatch), measured on the
+# same command and scaled by the copy-kernel calibration; None until taken for the current kernel.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill4k_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    return ap.parse_args()
+
+
+def upload(w, inputs, torch):
+    def dev(a, dt):
+        if dt == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda().view(torch.float8_e4m3fn)
+
+    out = []
+    odt = torch.float32 if w.mla_dtype == "f32" else torch.bfloat16
+    for L in inputs:
+        d = {"q": dev(L["mla_q"], w.mla_dtype), "kv": dev(L["kv"], w.mla_dtype),
+             "out": torch.empty((w.B, w.T, w.Hm, w.Dc), device="cuda", dtype=odt),
+             "lse": torch.empty((w.B, w.T, w.Hm), device="cuda")}
+        if "idx_q" in L:
+            d["index"] = {"q": dev(L["idx_q"], w.idx_dtype), "k": dev(L["idx_k"], w.idx_dtype),
+                          "w": dev(L["w"], "f32")}
+            if w.idx_dtype == "fp8":
+                d["index"]["q_scale"] = dev(L["idx_q_scale"], "f32")
+                d["index"]["k_scale"] = dev(L["idx_k_scale"], "f32")
+        out.append(d)
+    return out
+
+
+def cpu_baseline(w, inputs, rows):
+    """The oracle, as it stands, on `rows` query rows spread over the workload (all layers)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    types = ["full" if c == "F" else "shared" for c in w.layers]
+    ke, ks = w.key_end(), w.key_start()
+    picks = [(b, t) for b in range(w.B) for t in range(w.T)]
+    sel = [picks[i] for i in np.linspace(0, len(picks) - 1, min(rows, len(picks))).astype(int)]
+    dec = [{} for _ in inputs]
+    t0 = time.perf_counter()
+    for l, L in enumerate(inputs):
+        dec[l]["kv"] = {}
+        if types[l] == "full":
+            dec[l]["k"] = {}
+    done = 0
+    for (b, t) in sel:
+        idx = None
+        for l, L in enumerate(inputs):
+            if types[l] == "full":
+                if b not in dec[l]["k"]:
+                    dec[l]["k"][b] = O.decode(L["idx_k"][b], w.idx_dtype, L.get("idx_k_scale", [None] * w.B)[b]
+                                              if "idx_k_scale" in L else None)
+                qs = L["idx_q_scale"][b, t] if "idx_q_scale" in L else None
+                q = O.decode(L["idx_q"][b, t], w.idx_dtype, qs)
+                row = O.index_scores_row(q, dec[l]["k"][b], L["w"][b, t].astype(np.float64),
+                                         int(ks[b, t]), int(ke[b, t]))
+                idx, _ = O.topk_row(row, int(ks[b, t]), int(ke[b, t]), w.topk)
+            if b not in dec[l]["kv"]:
+                dec[l]["kv"][b] = O.decode(L["kv"][b], w.mla_dtype)
+            O.sparse_mla_row(O.decode(L["mla_q"][b, t], w.mla_dtype), dec[l]["kv"][b], idx, w.sm_scale, w.Dc)
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt * w.n_layers / 4.0, "unit": "query tokens/s", "cores": int(blas),
+            "kind": "oracle",
+            "sample": f"{done} query rows evenly spaced over the {w.B}x{w.T} rows of {w.name}, all "
+                      f"{w.n_layers} layers, float64 NumPy, {dt:.1f} s (input decoding included)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
+              f"MI355X; sharding is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from dsa_indexer_top_lightning_amd import binding as B
+    from dsa_indexer_top_lightning_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    inputs = synth.build_inputs(w)
+    dev = upload(w, inputs, torch)
+    ke_host, ks_host = w.key_end(), w.key_start()
+    ke = torch.from_numpy(ke_host).cuda()
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    types = ["full" if c == "F" else "shared" for c in w.layers]
+    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr, key_end=ke)
+    ws = torch.empty(max(B.workspace_bytes(shape, B.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
+    cache = B.IndexCache(w.B, w.T, w.topk)
+    mdt = B.F32 if w.mla_dtype == "f32" else B.BF16
+    idt = {"f32": B.F32, "bf16": B.BF16, "fp8": B.FP8_E4M3}[w.idx_dtype]
+    stats = B.group_stats_compute(shape, idt, mdt, types, ks_host, ke_host)
+    stream = torch.cuda.current_stream()
+
+    n = len(types)
+    steps = args.steps
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6 * n)]
+        for e in evs:
+            e.record(stream)           # creates the HIP event; the library re-records it
+        return evs
+
+    for _ in range(args.warmup):
+        B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream)
+    events = [new_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(steps):
+        B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream,
+                        events=[e.cuda_event for e in events[s]])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_step = elapsed / steps * 1e3
+
+    # per-kernel mean durations from the library's event records on the timed stream
+    def mean_ms(slot, layers):
+        v = [events[s][6 * l + slot].elapsed_time(events[s][6 * l + slot + 1]) for s in range(steps) for l in layers]
+        return float(np.mean(v)) if v else None
+
+    full_layers = [l for l in range(n) if types[l] == "full"]
+    t_idx = mean_ms(0, full_layers)
+    t_topk = mean_ms(2, full_layers)
+    t_attn = mean_ms(4, range(n))
+    idx_flops = stats.indexer_flops / max(len(full_layers), 1)
+    attn_flops = stats.attn_flops / n
+    attn_bytes = stats.attn_bytes / n
+    topk_bytes = stats.topk_bytes / max(len(full_layers), 1)
+    idx_peak = PEAK_FP8_TFLOPS if w.idx_dtype == "fp8" else PEAK_BF16_TFLOPS
+    kernels = {
+        "indexer": {"ms": t_idx, "tflops": idx_flops / (t_idx * 1e-3) / 1e12 if t_idx else None,
+                    "peak_tflops": idx_peak, "gbs": stats.indexer_bytes / max(len(full_layers), 1) / (t_idx * 1e-3) / 1e9
+                    if t_idx else None},
+        "topk": {"ms": t_topk, "gbs": topk_bytes / (t_topk * 1e-3) / 1e9 if t_topk else None,
+                 "peak_gbs": PEAK_HBM_GBS},
+        "sparse_mla": {"ms": t_attn, "tflops": attn_flops / (t_attn * 1e-3) / 1e12,
+                       "gbs": attn_bytes / (t_attn * 1e-3) / 1e9, "peak_tflops": PEAK_BF16_TFLOPS},
+    }
+    prefill = w.T > 1
+    if prefill:
+        ach = attn_flops / (t_attn * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / PEAK_BF16_TFLOPS, "traffic": MEASURED_TRAFFIC_BYTES, "kernel": "mla_mfma",
+                "algorithmic_per_launch": attn_flops}
+    else:
+        ach = attn_bytes / (t_attn * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                "traffic": MEASURED_TRAFFIC_BYTES, "kernel": "mla_mfma", "algorithmic_per_launch": attn_bytes}
+
+    tokens = w.B * w.T
+    value = tokens / (elapsed / steps) * n / 4.0
+    res = {
+        "metric": METRIC, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.mla_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "queries_per_item": w.T, "prefix": w.S, "layers": w.layers,
+                   "index_heads": w.H, "index_dim": w.D, "index_key_heads": w.Hk, "index_dtype": w.idx_dtype,
+                   "topk": w.topk, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

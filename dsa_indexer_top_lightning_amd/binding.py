@@ -1,0 +1,239 @@
+"""ctypes binding of libdsa.so (include/dsa.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module turns
+torch tensors into pointers and sizes, passes the current HIP stream and raises
+on a non-OK status.  It never computes results itself and has no fallback: if
+the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsa.h")
+
+F32, BF16, FP8_E4M3 = 0, 1, 2
+FULL, SHARED = 0, 1
+OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP = 0, 1, 2, 3
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_NO_DONOR",
+          4: "DSA_ERR_STALE_CACHE", 5: "DSA_ERR_WORKSPACE_TOO_SMALL", 6: "DSA_ERR_HIP"}
+
+
+class Shape(C.Structure):
+    _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("s_cap", C.c_int64),
+                ("H", C.c_int32), ("D", C.c_int32), ("Hk", C.c_int32), ("topk", C.c_int32),
+                ("Hm", C.c_int32), ("Dc", C.c_int32), ("Dr", C.c_int32),
+                ("key_start", C.c_void_p), ("key_end", C.c_void_p)]
+
+
+class TopkCache(C.Structure):
+    _fields_ = [("indices", C.c_void_p), ("B", C.c_int32), ("T", C.c_int32), ("topk", C.c_int32),
+                ("valid", C.c_int32), ("donor_layer", C.c_int32), ("tag", C.c_uint64)]
+
+
+class IndexIO(C.Structure):
+    _fields_ = [("idx_dtype", C.c_int), ("q", C.c_void_p), ("q_scale", C.c_void_p), ("k", C.c_void_p),
+                ("k_scale", C.c_void_p), ("w", C.c_void_p)]
+
+
+class LayerIO(C.Structure):
+    _fields_ = [("index", C.POINTER(IndexIO)), ("q", C.c_void_p), ("kv", C.c_void_p), ("out", C.c_void_p),
+                ("lse", C.c_void_p)]
+
+
+class GroupStats(C.Structure):
+    _fields_ = [("n_full", C.c_int32), ("n_shared", C.c_int32), ("n_launches", C.c_int32),
+                ("indexer_flops", C.c_double), ("indexer_bytes", C.c_double), ("topk_bytes", C.c_double),
+                ("attn_flops", C.c_double), ("attn_bytes", C.c_double)]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+_SIGS = {
+    "dsa_indexer_scores": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
+    "dsa_topk_select": (C.c_int, [C.POINTER(Shape), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t,
+                                  C.c_void_p]),
+    "dsa_sparse_mla_attention": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                           C.c_void_p]),
+    "dsa_group_forward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int32, C.c_void_p, C.POINTER(LayerIO),
+                                    C.c_float, C.POINTER(TopkCache), C.c_uint64, C.c_void_p, C.c_size_t,
+                                    C.c_void_p, C.POINTER(GroupStats), C.c_void_p]),
+    "dsa_group_stats_compute": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int, C.c_int32, C.c_void_p, C.c_void_p,
+                                          C.c_void_p, C.POINTER(GroupStats)]),
+    "dsa_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), C.c_int]),
+    "dsa_status_string": (C.c_char_p, [C.c_int]),
+    "dsa_last_error": (C.c_char_p, []),
+    "dsa_abi_version": (C.c_int, []),
+}
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/dsa.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(dsa_\w+)\s*\(", text, re.M)))
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().dsa_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise DsaError(status, last_error())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _dev_ptr(t) -> int | None:
+    if t is not None and t.device.type != "cuda":
+        raise ValueError("tensors passed to the library must live on the GPU")
+    return _ptr(t)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_shape(B, T, s_cap, *, H=0, D=0, Hk=0, topk=0, Hm=0, Dc=0, Dr=0, key_start=None, key_end=None) -> Shape:
+    return Shape(B, T, s_cap, H, D, Hk, topk, Hm, Dc, Dr, _dev_ptr(key_start), _dev_ptr(key_end))
+
+
+def workspace_bytes(shape: Shape, op: int) -> int:
+    return int(lib().dsa_workspace_bytes(C.byref(shape), op))
+
+
+# ---------------------------------------------------------------- entry points
+
+def indexer_scores(q, k, w, scores, *, q_scale=None, k_scale=None, key_start=None, key_end=None, stream=None):
+    """dsa_indexer_scores.  q [B,T,H,D], k [B,S,Hk,D], w [B,T,H], scores [B,T,ld] fp32 (written in place)."""
+    B, T, H, D = q.shape
+    S, Hk = k.shape[1], k.shape[2]
+    shape = make_shape(B, T, S, H=H, D=D, Hk=Hk, key_start=key_start, key_end=key_end)
+    _check(lib().dsa_indexer_scores(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(q_scale), _dev_ptr(k),
+                                    _dev_ptr(k_scale), _dev_ptr(w), _dev_ptr(scores), scores.shape[-1],
+                                    _stream(stream)))
+    return scores
+
+
+def topk_select(scores, out, s_cap, *, key_start=None, key_end=None, workspace=None, stream=None):
+    """dsa_topk_select.  scores [B,T,ld] fp32, out [B,T,topk] int32 (written in place)."""
+    B, T, K = out.shape
+    shape = make_shape(B, T, s_cap, topk=K, key_start=key_start, key_end=key_end)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_topk_select(C.byref(shape), _dev_ptr(scores), scores.shape[-1], _dev_ptr(out),
+                                 _dev_ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def sparse_mla_attention(q, kv, topk_indices, sm_scale, out, lse=None, *, Dc, workspace=None, stream=None):
+    """dsa_sparse_mla_attention.  q [B,T,Hm,Dc+Dr], kv [B,S,Dc+Dr], topk_indices [B,T,k], out [B,T,Hm,Dc]."""
+    B, T, Hm, R = q.shape
+    S = kv.shape[1]
+    shape = make_shape(B, T, S, topk=topk_indices.shape[-1], Hm=Hm, Dc=Dc, Dr=R - Dc)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_sparse_mla_attention(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(kv),
+                                          _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
+                                          _dev_ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+class IndexCache:
+    """Caller-owned cached top-k indices (dsa_topk_cache) with its device buffer."""
+
+    def __init__(self, B, T, topk, device="cuda"):
+        self.indices = torch.full((B, T, topk), -1, dtype=torch.int32, device=device)
+        self.c = TopkCache(self.indices.data_ptr(), 0, 0, 0, 0, -1, 0)
+
+    @property
+    def valid(self):
+        return bool(self.c.valid)
+
+
+def group_forward(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale, cache: IndexCache, tag: int,
+                  workspace, *, events=None, stream=None):
+    """dsa_group_forward.  ``layers`` is a list of dicts with keys q, kv, out, lse and, on full
+    layers, index = dict(q, k, w, q_scale, k_scale).  Returns GroupStats."""
+    n = len(indexer_types)
+    types = (C.c_int * n)(*[FULL if t in ("full", FULL) else SHARED for t in indexer_types])
+    idx_ios = []
+    arr = (LayerIO * n)()
+    for l, L in enumerate(layers):
+        io = None
+        if L.get("index") is not None:
+            I = L["index"]
+            io = IndexIO(dtype_code(I["q"]), _dev_ptr(I["q"]), _dev_ptr(I.get("q_scale")), _dev_ptr(I["k"]),
+                         _dev_ptr(I.get("k_scale")), _dev_ptr(I["w"]))
+            idx_ios.append(io)
+        arr[l] = LayerIO(C.pointer(io) if io is not None else None, _dev_ptr(L["q"]), _dev_ptr(L["kv"]),
+                         _dev_ptr(L["out"]), _dev_ptr(L.get("lse")))
+    ev = None
+    if events is not None:
+        ev = (C.c_void_p * len(events))(*events)
+    stats = GroupStats()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_group_forward(C.byref(shape), mla_dtype, n, types, arr, float(sm_scale), C.byref(cache.c),
+                                   tag, _dev_ptr(workspace), ws_bytes, ev, C.byref(stats), _stream(stream)))
+    return stats
+
+
+def group_stats_compute(shape: Shape, idx_dtype: int, mla_dtype: int, indexer_types, key_start_host=None,
+                        key_end_host=None) -> GroupStats:
+    """dsa_group_stats_compute (pure host).  Key ranges as host int32 arrays (numpy) or None."""
+    import numpy as np
+    n = len(indexer_types)
+    types = (C.c_int * n)(*[FULL if t in ("full", FULL) else SHARED for t in indexer_types])
+    ks = None if key_start_host is None else np.ascontiguousarray(key_start_host, dtype=np.int32)
+    ke = None if key_end_host is None else np.ascontiguousarray(key_end_host, dtype=np.int32)
+    out = GroupStats()
+    _check(lib().dsa_group_stats_compute(C.byref(shape), idx_dtype, mla_dtype, n, types,
+                                         None if ks is None else ks.ctypes.data,
+                                         None if ke is None else ke.ctypes.data, C.byref(out)))
+    return out

@@ -1,0 +1,85 @@
+// Internal launch interface between the C-ABI host layer (dsa_api.cpp) and the
+// gfx950 kernels.  Not installed; the public interface is include/dsa.h.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstddef>
+#include <cstdint>
+
+namespace dsa {
+
+enum Dtype : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+struct IndexerParams {
+  int B, T, H, D, Hk;
+  int64_t s_cap;
+  const int32_t* key_start;  // nullable
+  const int32_t* key_end;    // nullable
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  const float* k_scale;
+  const float* w;
+  float* scores;
+  int64_t ld;
+};
+
+struct TopkParams {
+  int B, T, topk;
+  int64_t s_cap;
+  const int32_t* key_start;
+  const int32_t* key_end;
+  const float* scores;
+  int64_t ld;
+  int32_t* out;
+};
+
+struct MlaParams {
+  int B, T, Hm, Dc, Dr, topk;
+  int64_t s_cap;
+  const void* q;
+  const void* kv;
+  const int32_t* idx;
+  float sm_scale;
+  void* out;
+  float* lse;
+};
+
+// Each launcher assumes its arguments were validated by the host layer.
+hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches);
+size_t topk_workspace_bytes(int B, int T, int topk, int64_t s_cap);
+hipError_t launch_topk(const TopkParams& p, void* ws, size_t ws_bytes, hipStream_t st, int* n_launches);
+bool mla_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);
+size_t mla_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt);
+hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                             int* n_launches);
+
+// Dynamic LDS above 64 KiB must be allowed per kernel.  `high` remembers the
+// largest size already allowed for that kernel; a failure is returned and the
+// runtime's last-error slot is cleared so it does not leak into later calls.
+inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomic<size_t>& high) {
+  if (bytes <= 65536 || bytes <= high.load()) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return e;
+  }
+  size_t cur = high.load();
+  while (bytes > cur && !high.compare_exchange_weak(cur, bytes)) {
+  }
+  return hipSuccess;
+}
+
+// Clamp a query's candidate range to [0, s_cap].
+__device__ __forceinline__ void clamp_range(const int32_t* ks_arr, const int32_t* ke_arr, int64_t row,
+                                            int64_t s_cap, int64_t& ks, int64_t& ke) {
+  int64_t a = ks_arr ? (int64_t)ks_arr[row] : 0;
+  int64_t e = ke_arr ? (int64_t)ke_arr[row] : s_cap;
+  a = a < 0 ? 0 : (a > s_cap ? s_cap : a);
+  e = e < a ? a : (e > s_cap ? s_cap : e);
+  ks = a;
+  ke = e;
+}
+
+}  // namespace dsa

@@ -1,0 +1,267 @@
+// Lightning-indexer scores on gfx950.
+//
+//   scores[b,t,s] = sum_h w[b,t,h] * max(0, q~[b,t,h,:] . k~[b,s,g(h),:])
+//
+// for every candidate key s of query (b,t) (GLM-5.2 IndexShare page, section 1
+// "What DSA does before sharing": the indexer scores the prefix tokens of each
+// query).  The pages print no formula; the per-head ReLU and scalar head weight
+// follow the Megatron-Bridge pull request's naming of the indexer weights
+// (per-head index q/k projections and a per-head scalar `weights_proj`).
+//
+// Two kernels:
+//  * indexer_mfma: bf16 or fp8 (OCP e4m3fn) with D == 128.  A workgroup owns a
+//    64-query x 64-key tile of one batch item and loops over the heads: each head
+//    is a 64x64x128 contraction on the matrix cores (v_mfma_f32_32x32x16_bf16, or
+//    v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) from LDS-staged
+//    tiles, followed by the fused ReLU * weight reduction in fp32 registers.
+//  * indexer_generic: any dtype / D, one thread per key, fp32 FMA.  Used for the
+//    fp32 inputs and for shapes the MFMA kernel does not cover.
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// OCP e4m3fn code -> float (exact).
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  float v;
+  if (e == 0xF && m == 7) v = __builtin_nanf("");
+  else if (e == 0) v = (float)m * 0x1p-9f;
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80) ? -v : v;
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, int64_t i) {
+  if constexpr (DT == F32) return static_cast<const float*>(base)[i];
+  else if constexpr (DT == BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[i]);
+  else return e4m3_to_f32(static_cast<const uint8_t*>(base)[i]);
+}
+
+// ----------------------------------------------------------------- generic kernel
+// grid: x = query row (b*T + t), y = block of 256 key positions.  Dynamic LDS:
+// H*D decoded query values (times q_scale) and H weights.
+template <int DT>
+__global__ __launch_bounds__(256) void indexer_generic(IndexerParams p) {
+  extern __shared__ float lds[];
+  const int64_t row = blockIdx.x;
+  int64_t ks, ke;
+  clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
+  const int64_t s = (int64_t)blockIdx.y * 256 + threadIdx.x;
+  const int64_t sblk = (int64_t)blockIdx.y * 256;
+  if (sblk >= ke || sblk + 256 <= ks) return;  // whole block outside the range
+  const int H = p.H, D = p.D, Hk = p.Hk;
+  float* qs = lds;
+  float* ws = lds + H * D;
+  for (int i = threadIdx.x; i < H * D; i += 256) {
+    float v = load_elem<DT>(p.q, row * H * D + i);
+    if constexpr (DT == FP8) v *= p.q_scale[row * H + i / D];
+    qs[i] = v;
+  }
+  for (int i = threadIdx.x; i < H; i += 256) ws[i] = p.w[row * H + i];
+  __syncthreads();
+  if (s < ks || s >= ke) return;
+  const int64_t b = row / p.T;
+  const int64_t krow = (b * p.s_cap + s) * Hk;
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    const int g = (Hk == H) ? h : 0;
+    const int64_t kb = (krow + g) * D;
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot = fmaf(qs[h * D + d], load_elem<DT>(p.k, kb + d), dot);
+    if constexpr (DT == FP8) dot *= p.k_scale[krow + g];
+    acc = fmaf(ws[h], fmaxf(dot, 0.f), acc);
+  }
+  p.scores[row * p.ld + s] = acc;
+}
+
+// ----------------------------------------------------------------- MFMA kernel
+constexpr int TM = 64;   // queries per tile
+constexpr int TN = 64;   // keys per tile
+constexpr int HD = 128;  // index head dim handled by the MFMA kernel
+
+template <int DT>
+struct MfmaCfg {
+  static constexpr int ESZ = (DT == BF16) ? 2 : 1;
+  static constexpr int RB = HD * ESZ;        // bytes per row
+  static constexpr int RS = RB + 16;         // padded LDS row stride (bank-conflict free b128 reads)
+  static constexpr int CHUNKS = RB / 16;     // 16-byte chunks per row
+};
+
+// grid: x = key tile, y = query tile, z = batch item.  256 threads = 4 waves,
+// wave w computes rows [32*(w&1), +32) x keys [32*(w>>1), +32) of the tile.
+// Dynamic LDS: Q tile, K tile, weights [H][TM] (times q_scale for fp8), key scales [Hk][TN].
+template <int DT>
+__global__ __launch_bounds__(256) void indexer_mfma(IndexerParams p) {
+  using C = MfmaCfg<DT>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* qt = smem;
+  unsigned char* kt = smem + TM * C::RS;
+  float* wl = reinterpret_cast<float*>(smem + (TM + TN) * C::RS);
+  float* ksl = wl + p.H * TM;
+  __shared__ int32_t rks[TM], rke[TM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * TM;
+  const int64_t s0 = (int64_t)blockIdx.x * TN;
+  const int H = p.H, Hk = p.Hk, T = p.T;
+
+  // ranges of the tile's rows; skip tiles with no candidate cell
+  int live = 0;
+  if (tid < TM) {
+    const int t = t0 + tid;
+    int64_t ks = 0, ke = 0;
+    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, p.s_cap, ks, ke);
+    rks[tid] = (int32_t)ks;
+    rke[tid] = (int32_t)ke;
+    live = (t < T) && (ks < s0 + TN) && (ke > s0) && (ks < ke);
+  }
+  if (!__syncthreads_or(live)) return;
+
+  // weights (x q_scale) for all heads of the tile's rows; key scales
+  for (int i = tid; i < H * TM; i += 256) {
+    const int h = i / TM, r = i % TM, t = t0 + r;
+    float v = 0.f;
+    if (t < T) {
+      const int64_t qi = ((int64_t)b * T + t) * H + h;
+      v = p.w[qi];
+      if constexpr (DT == FP8) v *= p.q_scale[qi];
+    }
+    wl[i] = v;
+  }
+  if constexpr (DT == FP8) {
+    for (int i = tid; i < Hk * TN; i += 256) {
+      const int g = i / TN, c = i % TN;
+      const int64_t s = s0 + c;
+      ksl[i] = (s < p.s_cap) ? p.k_scale[((int64_t)b * p.s_cap + s) * Hk + g] : 0.f;
+    }
+  }
+
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, lg = lane >> 5;
+  f32x16 tot;
+  for (int r = 0; r < 16; ++r) tot[r] = 0.f;
+
+  const unsigned char* qg = static_cast<const unsigned char*>(p.q);
+  const unsigned char* kg = static_cast<const unsigned char*>(p.k);
+
+  for (int h = 0; h < H; ++h) {
+    const int g = (Hk == H) ? h : 0;
+    // stage Q_h tile and (if it changes) K_g tile
+    for (int c = tid; c < TM * C::CHUNKS; c += 256) {
+      const int r = c / C::CHUNKS, ch = c % C::CHUNKS, t = t0 + r;
+      i32x4 v = {0, 0, 0, 0};
+      if (t < T) v = *reinterpret_cast<const i32x4*>(qg + ((((int64_t)b * T + t) * H + h) * HD) * C::ESZ + ch * 16);
+      *reinterpret_cast<i32x4*>(qt + r * C::RS + ch * 16) = v;
+    }
+    if (Hk == H || h == 0) {
+      for (int c = tid; c < TN * C::CHUNKS; c += 256) {
+        const int r = c / C::CHUNKS, ch = c % C::CHUNKS;
+        const int64_t s = s0 + r;
+        i32x4 v = {0, 0, 0, 0};
+        if (s < p.s_cap) v = *reinterpret_cast<const i32x4*>(kg + ((((int64_t)b * p.s_cap + s) * Hk + g) * HD) * C::ESZ + ch * 16);
+        *reinterpret_cast<i32x4*>(kt + r * C::RS + ch * 16) = v;
+      }
+    }
+    __syncthreads();
+
+    f32x16 acc;
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    const unsigned char* qrow = qt + (32 * wm + lr) * C::RS;
+    const unsigned char* krow = kt + (32 * wn + lr) * C::RS;
+    if constexpr (DT == BF16) {
+#pragma unroll
+      for (int st = 0; st < HD / 16; ++st) {
+        const int off = (16 * st + 8 * lg) * 2;
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + off);
+        bf16x8 bb = *reinterpret_cast<const bf16x8*>(krow + off);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < HD / 64; ++st) {
+        const int off = 64 * st + 32 * lg;
+        i32x8 a, bb;
+        i32x4 a0 = *reinterpret_cast<const i32x4*>(qrow + off), a1 = *reinterpret_cast<const i32x4*>(qrow + off + 16);
+        i32x4 b0 = *reinterpret_cast<const i32x4*>(krow + off), b1 = *reinterpret_cast<const i32x4*>(krow + off + 16);
+        a[0] = a0[0]; a[1] = a0[1]; a[2] = a0[2]; a[3] = a0[3]; a[4] = a1[0]; a[5] = a1[1]; a[6] = a1[2]; a[7] = a1[3];
+        bb[0] = b0[0]; bb[1] = b0[1]; bb[2] = b0[2]; bb[3] = b0[3]; bb[4] = b1[0]; bb[5] = b1[1]; bb[6] = b1[2]; bb[7] = b1[3];
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc, 0, 0, 0, 127, 0, 127);
+      }
+    }
+    // fused ReLU * weight: result row m = 8*(r/4) + 4*lg + r%4, column n = lr
+    const float* wrow = wl + h * TM + 32 * wm + 4 * lg;
+    float kscale = 1.f;
+    if constexpr (DT == FP8) kscale = ksl[g * TN + 32 * wn + lr];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float wv = wrow[8 * (r >> 2) + (r & 3)];
+      tot[r] = fmaf(wv, fmaxf(acc[r] * kscale, 0.f), tot[r]);
+    }
+    __syncthreads();
+  }
+
+  const int64_t s = s0 + 32 * wn + lr;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = 32 * wm + 8 * (r >> 2) + 4 * lg + (r & 3);
+    const int t = t0 + m;
+    if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = tot[r];
+  }
+}
+
+template <auto K>
+hipError_t ensure_lds(size_t bytes) {
+  static std::atomic<size_t> high{0};
+  return allow_dynamic_lds(reinterpret_cast<const void*>(K), bytes, high);
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches) {
+  if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;
+  const bool mfma = (dt == BF16 || dt == FP8) && p.D == HD;
+  if (mfma) {
+    const int rs = (dt == BF16) ? MfmaCfg<BF16>::RS : MfmaCfg<FP8>::RS;
+    const size_t lds = (size_t)(TM + TN) * rs + (size_t)p.H * TM * 4 + (dt == FP8 ? (size_t)p.Hk * TN * 4 : 0);
+    dim3 grid((unsigned)((p.s_cap + TN - 1) / TN), (unsigned)((p.T + TM - 1) / TM), (unsigned)p.B);
+    hipError_t e;
+    if (dt == BF16) {
+      if ((e = ensure_lds<indexer_mfma<BF16>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(indexer_mfma<BF16>, grid, dim3(256), lds, st, p);
+    } else {
+      if ((e = ensure_lds<indexer_mfma<FP8>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(indexer_mfma<FP8>, grid, dim3(256), lds, st, p);
+    }
+  } else {
+    const size_t lds = ((size_t)p.H * p.D + p.H) * 4;
+    dim3 grid((unsigned)((int64_t)p.B * p.T), (unsigned)((p.s_cap + 255) / 256));
+    hipError_t e;
+    switch (dt) {
+      case F32:
+        if ((e = ensure_lds<indexer_generic<F32>>(lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(indexer_generic<F32>, grid, dim3(256), lds, st, p);
+        break;
+      case BF16:
+        if ((e = ensure_lds<indexer_generic<BF16>>(lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(indexer_generic<BF16>, grid, dim3(256), lds, st, p);
+        break;
+      default:
+        if ((e = ensure_lds<indexer_generic<FP8>>(lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(indexer_generic<FP8>, grid, dim3(256), lds, st, p);
+        break;
+    }
+  }
+  if (n_launches) ++*n_launches;
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,224 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) DSA lightning indexer -> top-k -> sparse
+ * MLA path with GLM-5.2 cross-layer IndexShare.
+ *
+ * What the calls compute (the pages describe the method; they print no formula,
+ * so the readings are stated where they are used):
+ *   GLM-5.2 IndexShare page, section 1 "What DSA does before sharing": for each
+ *   query a light indexer scores the prefix tokens, the top-k positions are kept,
+ *   and the main attention runs only over them.  Section 2 "What IndexShare
+ *   changes" and the table "What is actually shared?": full layers compute and
+ *   cache the top-k indices, shared layers reuse the nearest preceding full
+ *   layer's indices and still compute their own attention.
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are
+ *     dense, row-major, in the layouts given below.  Pointers marked "host" are
+ *     host memory.  The library keeps no pointer past the call and frees nothing.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream) and
+ *     the call returns without waiting.  Device faults surface at the caller's
+ *     next synchronisation.
+ *   - All argument checks run on the host before anything is enqueued: a call
+ *     that returns an error has enqueued nothing.  No call aborts, exits or
+ *     throws; dsa_last_error() gives a thread-local message for the last error.
+ *   - Query (b, t) owns a candidate range [key_start[b*T+t], key_end[b*T+t]) of
+ *     absolute key positions.  Device code clamps each range to [0, s_cap] so
+ *     a bad range cannot address memory outside the tensors; the result for
+ *     such a row is the result for the clamped range.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,         /* null or inconsistent pointer / size / shape */
+  DSA_ERR_UNSUPPORTED = 2,         /* valid request this build has no kernel for */
+  DSA_ERR_NO_DONOR = 3,            /* a shared layer has no full layer and no cached indices */
+  DSA_ERR_STALE_CACHE = 4,         /* cached indices belong to another call (tag/shape) */
+  DSA_ERR_WORKSPACE_TOO_SMALL = 5, /* ws_bytes < dsa_workspace_bytes(...) */
+  DSA_ERR_HIP = 6                  /* a HIP runtime call failed (message in dsa_last_error) */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 /* OCP e4m3fn */ } dsa_dtype;
+typedef enum { DSA_FULL = 0, DSA_SHARED = 1 } dsa_layer_type;
+typedef enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_GROUP = 3 } dsa_op;
+
+/* Problem shape (host struct).  Fields a call does not use are ignored. */
+typedef struct {
+  int32_t B, T;          /* batch items, queries per item (B*T query rows) */
+  int64_t s_cap;         /* key capacity per item: index keys and latent rows hold s_cap rows */
+  int32_t H, D, Hk;      /* index query heads, index head dim, index key heads (H or 1) */
+  int32_t topk;          /* index_topk: width of every topk_indices row */
+  int32_t Hm, Dc, Dr;    /* MLA heads, latent rank (value dims), rope dims; a latent row has Dc+Dr values */
+  const int32_t* key_start; /* device int32 [B*T], or NULL for 0 */
+  const int32_t* key_end;   /* device int32 [B*T] (exclusive), or NULL for s_cap */
+} dsa_shape;
+
+/*
+ * Lightning-indexer scores of every candidate key (section 1 of the IndexShare
+ * page; reading of the score: the pages name the per-head index q/k and a
+ * per-head scalar weight but print no formula):
+ *     scores[b,t,s] = sum_h w[b,t,h] * max(0, q~[b,t,h,:] . k~[b,s,g(h),:])
+ * for s in [key_start, key_end); g(h) = h when Hk == H, else 0.  q~ and k~ are
+ * the stored values, times q_scale / k_scale for fp8.
+ *   q       [B,T,H,D]   idx_dtype          q_scale [B,T,H]  fp32 (fp8 only, else NULL)
+ *   k       [B,s_cap,Hk,D] idx_dtype       k_scale [B,s_cap,Hk] fp32 (fp8 only)
+ *   w       [B,T,H]     fp32
+ *   scores  [B,T,ld_scores] fp32, ld_scores >= s_cap; only candidate cells are written.
+ * Arithmetic: exact products, fp32 accumulation (MFMA for bf16/fp8 with D == 128).
+ * Supported: D % 16 == 0 and D <= 256; H <= 128; Hk in {1, H}.
+ */
+dsa_status dsa_indexer_scores(const dsa_shape* shape, dsa_dtype idx_dtype,
+                              const void* q, const float* q_scale,
+                              const void* k, const float* k_scale,
+                              const float* w, float* scores, int64_t ld_scores,
+                              void* stream);
+
+/*
+ * Top-k selection per query row (section 1 of the IndexShare page; the -1 padding
+ * follows the Megatron-Bridge pull request's commit that fixes top-k for packed
+ * sequences shorter than index_topk).  For each row the topk candidates with the
+ * largest score are kept; among equal scores the lower position wins (-0.0 and
+ * +0.0 are equal).  The kept absolute positions are written in ascending order.
+ * A row with n = key_end - key_start <= topk keeps all n candidates and fills
+ * the remaining topk - n slots with -1.  NaN scores give an unspecified (but
+ * in-range) selection.
+ *   scores        [B,T,ld_scores] fp32 (only the candidate cells are read)
+ *   topk_indices  [B,T,topk] int32
+ *   workspace     device scratch of ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_TOPK)
+ */
+dsa_status dsa_topk_select(const dsa_shape* shape, const float* scores, int64_t ld_scores,
+                           int32_t* topk_indices, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * Sparse MLA attention over the selected latent rows (section 1 of the IndexShare
+ * page; the latent row of kv_lora_rank 512 + rope 64 = 576 values is in the
+ * Megatron-Bridge pull request's commit on the rope-dim parse).  Absorbed form:
+ * keys are the whole Dc+Dr row, values its first Dc entries.  For each (b,t,h):
+ *     z_j = sm_scale * q[b,t,h,:] . kv[b,idx_j,:],  p = softmax(z),
+ *     out[b,t,h,:] = sum_j p_j kv[b,idx_j,:Dc],     lse[b,t,h] = log sum_j exp(z_j)
+ * over the entries idx_j of topk_indices[b,t,:] that lie in [0, s_cap); other
+ * entries (-1 padding) are skipped.  A row with no valid entry gives out = 0 and
+ * lse = -inf.  Each listed entry counts once per occurrence.
+ *   q    [B,T,Hm,Dc+Dr] mla_dtype     kv  [B,s_cap,Dc+Dr] mla_dtype
+ *   out  [B,T,Hm,Dc]    mla_dtype     lse [B,T,Hm] fp32 or NULL
+ * Arithmetic: fp32 softmax and accumulation; bf16 MFMA for bf16 with Dc == 512,
+ * Dr == 64 and Hm % 64 == 0, fp32 FMA otherwise.  Supported: mla_dtype F32 or
+ * BF16, Dc % 8 == 0, Dr % 8 == 0, Dc+Dr <= 1024, Hm <= 1024.
+ */
+dsa_status dsa_sparse_mla_attention(const dsa_shape* shape, dsa_dtype mla_dtype,
+                                    const void* q, const void* kv,
+                                    const int32_t* topk_indices, float sm_scale,
+                                    void* out, float* lse,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Cached top-k indices carried between layers and calls (host struct).  The
+ * indices buffer is caller-owned device memory [B,T,topk].  The host fields are
+ * written at enqueue time; the device contents follow stream order, so a handle
+ * belongs to one stream.  This plays the part of the carried indexer state of a
+ * scanned layer loop (MaxText pull request, key change 2) and of the per-micro-
+ * batch top-k holder (Megatron-Bridge pull request, cross-layer DSA commit). */
+typedef struct {
+  int32_t* indices;
+  int32_t B, T, topk;   /* shape the indices were produced for */
+  int32_t valid;        /* 0 = empty */
+  int32_t donor_layer;  /* layer index (in the producing call) that wrote them */
+  uint64_t tag;         /* caller's tag of the producing call */
+} dsa_topk_cache;
+
+/* Index inputs of a full layer (host struct, device pointers; layouts as in
+ * dsa_indexer_scores). */
+typedef struct {
+  dsa_dtype idx_dtype;
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  const float* k_scale;
+  const float* w;
+} dsa_index_io;
+
+/* Per-layer inputs and outputs (host struct, device pointers; layouts as in
+ * dsa_sparse_mla_attention).  `index` is required on full layers and ignored on
+ * shared ones. */
+typedef struct {
+  const dsa_index_io* index;
+  const void* q;
+  const void* kv;
+  void* out;
+  float* lse;
+} dsa_layer_io;
+
+/* Analytic work of a group call (counts, not timings). */
+typedef struct {
+  int32_t n_full, n_shared;
+  int32_t n_launches;      /* kernels enqueued by the call */
+  double indexer_flops;    /* 2*H*D per (query, candidate) pair, per full layer */
+  double indexer_bytes;    /* index q, w (+scales), index k of each item's prefix, fp32 scores written */
+  double topk_bytes;       /* fp32 scores read + int32 indices written */
+  double attn_flops;       /* 2*Hm*(2*Dc+Dr) per (query, selected row), per layer */
+  double attn_bytes;       /* gathered latent rows + q read + out written, per layer */
+} dsa_group_stats;
+
+/*
+ * One IndexShare layer group (section 2 of the IndexShare page and its layer-
+ * pattern figure; the list comes from indexer_types as the page's config
+ * evidence and implementation checklist ask, not from a fixed layer modulo).
+ * For l in 0..n_layers-1:
+ *   FULL:   indexer scores -> workspace, top-k -> cache->indices, and the cache
+ *           is marked valid with donor_layer = l and the call's tag.
+ *   SHARED: the cache's indices are used unchanged (no device work).
+ *   both:   sparse MLA with layer l's own q and kv and the current indices.
+ * Errors (checked for the whole list before anything is enqueued):
+ *   DSA_ERR_INVALID_ARG  a full layer without `index`, null required pointers;
+ *   DSA_ERR_NO_DONOR     the first layer is shared and cache->valid == 0 (a
+ *                        pipeline stage must not start on a shared layer without
+ *                        its source: Megatron-Bridge pull request, build-time
+ *                        stage-start check);
+ *   DSA_ERR_STALE_CACHE  the first layer is shared and the cache's tag, B, T or
+ *                        topk differ from this call (a stale holder must be
+ *                        rejected, not read: same pull request, bshd+recompute
+ *                        guard).
+ *   events: NULL, or host array of 6*n_layers hipEvent_t; when given, for layer l
+ *           events[6l+0/1] bracket the indexer, [6l+2/3] the top-k and [6l+4/5]
+ *           the attention kernels (entries of shared layers' indexer/top-k unused).
+ *   stats:  NULL or filled with n_full, n_shared and n_launches.
+ *   workspace: ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_GROUP).
+ */
+dsa_status dsa_group_forward(const dsa_shape* shape, dsa_dtype mla_dtype, int32_t n_layers,
+                             const dsa_layer_type* indexer_types, /* host [n_layers] */
+                             const dsa_layer_io* layers,          /* host [n_layers] */
+                             float sm_scale, dsa_topk_cache* cache, uint64_t tag,
+                             void* workspace, size_t ws_bytes,
+                             void* const* events, dsa_group_stats* stats, void* stream);
+
+/* Analytic counters of a group call from host copies of the key ranges (host
+ * arrays [B*T]; key_start_host may be NULL for 0, key_end_host NULL for s_cap).
+ * Pure host function. */
+dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
+                                   dsa_dtype mla_dtype, int32_t n_layers,
+                                   const dsa_layer_type* indexer_types,
+                                   const int32_t* key_start_host, const int32_t* key_end_host,
+                                   dsa_group_stats* out);
+
+/* Device scratch a call needs (bytes, 0 if none).  Pure host function; returns 0
+ * for an invalid shape. */
+size_t dsa_workspace_bytes(const dsa_shape* shape, dsa_op op);
+
+const char* dsa_status_string(dsa_status status);
+const char* dsa_last_error(void);
+int dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,161 @@
+"""The C-ABI library on a host without a GPU: symbols, status strings, host-side
+validation (every error returns before anything is enqueued), workspace sizing and
+analytic stats.  No compute call is made here."""
+import ctypes as C
+
+import numpy as np
+import pytest
+
+import oracle as O
+from dsa_indexer_top_lightning_amd import binding as b
+
+
+@pytest.fixture(scope="module")
+def L():
+    return b.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = b.header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.dsa_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code, name in b.STATUS.items():
+        assert L.dsa_status_string(code).decode() == name
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _shape(**kw):
+    base = dict(B=1, T=4, s_cap=16, H=4, D=32, Hk=4, topk=8, Hm=8, Dc=64, Dr=16)
+    base.update(kw)
+    return b.Shape(base["B"], base["T"], base["s_cap"], base["H"], base["D"], base["Hk"], base["topk"],
+                   base["Hm"], base["Dc"], base["Dr"], None, None)
+
+
+def _idx(L, shape, dt=b.BF16, q=FAKE, qs=None, k=FAKE, ks=None, w=FAKE, sc=FAKE, ld=None):
+    return L.dsa_indexer_scores(C.byref(shape), dt, q, qs, k, ks, w, sc, shape.s_cap if ld is None else ld, None)
+
+
+@pytest.mark.parametrize("kw,dt,expect", [
+    (dict(Hk=2), b.BF16, 1),
+    (dict(D=24), b.BF16, 2),
+    (dict(D=512), b.BF16, 2),
+    (dict(H=200, Hk=200), b.BF16, 2),
+    (dict(B=-1), b.BF16, 1),
+    (dict(), 7, 1),
+])
+def test_indexer_shape_errors(L, kw, dt, expect):
+    assert _idx(L, _shape(**kw), dt=dt) == expect
+    assert L.dsa_last_error().decode()
+
+
+def test_indexer_pointer_errors(L):
+    s = _shape()
+    assert _idx(L, s, q=None) == 1
+    assert _idx(L, s, dt=b.FP8_E4M3) == 1            # fp8 without scales
+    assert _idx(L, s, ld=15) == 1                     # ld < s_cap
+    assert _idx(L, s, sc=None) == 1
+    assert _idx(L, _shape(B=0), q=None, k=None, w=None, sc=None) == 0   # empty problem: nothing to do
+
+
+def test_topk_errors(L):
+    s = _shape(topk=0)
+    assert L.dsa_topk_select(C.byref(s), FAKE, 16, FAKE, None, 0, None) == 1
+    s = _shape()
+    assert L.dsa_topk_select(C.byref(s), FAKE, 8, FAKE, None, 0, None) == 1
+    assert L.dsa_topk_select(C.byref(s), FAKE, 16, None, None, 0, None) == 1
+    assert L.dsa_topk_select(None, FAKE, 16, FAKE, None, 0, None) == 1
+
+
+def test_sparse_mla_errors(L):
+    s = _shape()
+    f = L.dsa_sparse_mla_attention
+    assert f(C.byref(s), b.FP8_E4M3, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, 0, None) == 2
+    assert f(C.byref(_shape(Dc=60)), b.BF16, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, 0, None) == 2
+    assert f(C.byref(_shape(Dc=1024, Dr=64)), b.BF16, FAKE, FAKE, FAKE, 1.0, FAKE, None, None, 0, None) == 2
+    assert f(C.byref(s), b.BF16, None, FAKE, FAKE, 1.0, FAKE, None, None, 0, None) == 1
+    assert f(C.byref(s), b.BF16, FAKE, FAKE, None, 1.0, FAKE, None, None, 0, None) == 1
+    # decode-sized bf16 problem needs a split workspace
+    d = _shape(B=2, T=1, s_cap=4096, topk=2048, Hm=64, Dc=512, Dr=64)
+    need = L.dsa_workspace_bytes(C.byref(d), b.OP_SPARSE_MLA)
+    assert need > 0
+    assert f(C.byref(d), b.BF16, FAKE, FAKE, FAKE, 1.0, FAKE, None, FAKE, need - 1, None) == 5
+
+
+def _group(L, shape, types, layers, cache, tag=0, ws=FAKE, ws_bytes=None):
+    n = len(types)
+    tarr = (C.c_int * n)(*types)
+    arr = (b.LayerIO * n)(*layers)
+    if ws_bytes is None:
+        ws_bytes = L.dsa_workspace_bytes(C.byref(shape), b.OP_GROUP)
+    return L.dsa_group_forward(C.byref(shape), b.BF16, n, tarr, arr, 0.1, C.byref(cache), tag, ws, ws_bytes,
+                               None, None, None)
+
+
+def _io(with_index):
+    io = b.IndexIO(b.BF16, FAKE, None, FAKE, None, FAKE)
+    keep = [io]
+    return b.LayerIO(C.pointer(io) if with_index else None, FAKE, FAKE, FAKE, None), keep
+
+
+def test_group_no_donor_and_stale_cache(L):
+    s = _shape()
+    sh, k1 = _io(False)
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    assert _group(L, s, [b.SHARED, b.SHARED], [sh, sh], cache) == 3                 # NO_DONOR
+    assert "SHARED" in L.dsa_last_error().decode()
+    cache = b.TopkCache(FAKE, 1, 4, 8, 1, 0, 5)
+    assert _group(L, s, [b.SHARED], [sh], cache, tag=6) == 4                        # tag mismatch
+    cache = b.TopkCache(FAKE, 1, 3, 8, 1, 0, 6)
+    assert _group(L, s, [b.SHARED], [sh], cache, tag=6) == 4                        # T mismatch
+    cache = b.TopkCache(FAKE, 1, 4, 16, 1, 0, 6)
+    assert _group(L, s, [b.SHARED], [sh], cache, tag=6) == 4                        # topk mismatch
+
+
+def test_group_argument_errors(L):
+    s = _shape()
+    sh, k1 = _io(False)
+    fu, k2 = _io(True)
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    assert _group(L, s, [b.FULL, b.SHARED], [sh, sh], cache) == 1                   # full layer without index
+    assert _group(L, s, [b.FULL, 9], [fu, sh], cache) == 1                          # bad type
+    assert _group(L, s, [b.FULL], [fu], cache, ws_bytes=16) == 5                    # workspace too small
+    nocache = b.TopkCache(None, 0, 0, 0, 0, -1, 0)
+    assert _group(L, s, [b.FULL], [fu], nocache) == 1
+    assert L.dsa_group_forward(C.byref(s), b.BF16, 1, None, None, 0.1, C.byref(cache), 0, FAKE, 1 << 20,
+                               None, None, None) == 1
+    # nothing was enqueued and the handle was not touched
+    assert cache.valid == 0 and cache.donor_layer == -1
+
+
+def test_workspace_sizes(L):
+    s = _shape(B=1, T=4096, s_cap=4096, topk=2048, Hm=64, Dc=512, Dr=64)
+    assert L.dsa_workspace_bytes(C.byref(s), b.OP_GROUP) >= 4096 * 4096 * 4
+    assert L.dsa_workspace_bytes(C.byref(s), b.OP_INDEXER) == 0
+    assert L.dsa_workspace_bytes(None, b.OP_GROUP) == 0
+
+
+@pytest.mark.parametrize("types", [["full", "shared", "shared", "shared"],
+                                   ["full", "full", "full", "shared", "shared", "shared", "full", "shared"],
+                                   ["full"] * 4])
+@pytest.mark.parametrize("idx_dt,mla_dt", [("bf16", "bf16"), ("fp8", "bf16"), ("f32", "f32")])
+def test_group_stats_match_oracle_counts(types, idx_dt, mla_dt):
+    rng = np.random.default_rng(5)
+    B, T, S = 3, 50, 300
+    ke = rng.integers(1, S + 1, (B, T)).astype(np.int32)
+    ks = np.minimum(rng.integers(0, 40, (B, T)), ke - 1).astype(np.int32)
+    shape = b.Shape(B, T, S, 32, 128, 32, 64, 64, 512, 64, None, None)
+    code = {"f32": b.F32, "bf16": b.BF16, "fp8": b.FP8_E4M3}
+    st = b.group_stats_compute(shape, code[idx_dt], code[mla_dt], types, ks, ke)
+    e = {"f32": 4, "bf16": 2, "fp8": 1}
+    ref = O.group_stats(types, ks, ke, H=32, D=128, Hk=32, idx_bytes=e[idx_dt], idx_scaled=idx_dt == "fp8",
+                        topk_k=64, Hm=64, Dc=512, Dr=64, mla_bytes=e[mla_dt], S=S)
+    assert (st.n_full, st.n_shared) == (ref["n_full"], ref["n_shared"])
+    for key in ("indexer_flops", "indexer_bytes", "topk_bytes", "attn_flops", "attn_bytes"):
+        assert getattr(st, key) == pytest.approx(ref[key], rel=1e-12), key

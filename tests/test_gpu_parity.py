@@ -1,0 +1,333 @@
+"""GPU parity: each C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Bars: top-k indices bit-exact (with the GPU's own inputs: exactly; through the
+indexer: identical except inside the 1e-3 relative tie band around the k-th
+score); attention max-abs-relative error <= 1e-5 (fp32) / 2e-2 (bf16); index
+scores within 2e-5 * sum_h |w| sum_d |q k| of the float64 value (fp32
+accumulation of exact products).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dsa_indexer_top_lightning_amd import binding as b
+from dsa_indexer_top_lightning_amd import synth
+from helpers import ATTN_TOL, check_topk_row, decode_index, f32_dev, i32_dev, index_abs_bound, max_abs_rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _wl(**kw):
+    base = dict(name="t", B=1, T=64, S=64, pos0=0, layers="FSSS", H=32, D=128, Hk=32, topk=64, Hm=64, Dc=512,
+                Dr=64, idx_dtype="bf16", mla_dtype="bf16", seed=7)
+    base.update(kw)
+    return synth.Workload(**base)
+
+
+# ------------------------------------------------------------------ indexer
+
+INDEXER_CASES = {
+    "fp32_tiny": dict(B=1, T=256, S=256, H=4, D=32, Hk=4, idx_dtype="f32", mla_dtype="f32", Hm=8, Dc=64, Dr=16),
+    "bf16_ragged": dict(B=2, T=70, S=150, pos0=80, rope=True),
+    "bf16_shared_key": dict(B=2, T=70, S=150, pos0=80, Hk=1),
+    "fp8_ragged": dict(B=2, T=70, S=150, pos0=80, idx_dtype="fp8"),
+    "fp8_shared_key": dict(B=1, T=33, S=200, pos0=167, Hk=1, idx_dtype="fp8"),
+    "bf16_decode": dict(B=3, T=1, S=300, pos0=299),
+    "fp8_decode_planted": dict(B=2, T=1, S=700, pos0=699, idx_dtype="fp8", plant_frac=0.05),
+    "bf16_generic_d64": dict(B=1, T=40, S=90, pos0=50, D=64, H=8, Hk=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(INDEXER_CASES))
+@pytest.mark.parametrize("window", [False, True])
+def test_indexer_scores_match_oracle(case, window):
+    w = _wl(**INDEXER_CASES[case])
+    L = synth.build_layer_inputs(w, 0, True)
+    ke = w.key_end()
+    ks = np.maximum(ke - 37, 0).astype(np.int32) if window else w.key_start()
+    ld = w.S + 5
+    q = to_dev(L["idx_q"], w.idx_dtype)
+    k = to_dev(L["idx_k"], w.idx_dtype)
+    qs = f32_dev(L["idx_q_scale"]) if w.idx_dtype == "fp8" else None
+    kss = f32_dev(L["idx_k_scale"]) if w.idx_dtype == "fp8" else None
+    scores = torch.full((w.B, w.T, ld), float("nan"), device="cuda")
+    b.indexer_scores(q, k, f32_dev(L["w"]), scores, q_scale=qs, k_scale=kss, key_start=i32_dev(ks),
+                     key_end=i32_dev(ke))
+    got = scores.cpu().numpy()
+    q64, k64, w64 = decode_index(L, w)
+    for bb in range(w.B):
+        ref = O.index_scores(q64[bb:bb + 1], k64[bb:bb + 1], w64[bb:bb + 1], ks[bb:bb + 1], ke[bb:bb + 1])[0]
+        bound = 2e-5 * index_abs_bound(q64[bb], k64[bb], w64[bb], w.Hk) + 1e-30
+        mask = ~np.isnan(ref)
+        g = got[bb, :, :w.S]
+        assert np.isnan(g[~mask]).all(), "cells outside the candidate ranges were written"
+        assert np.isnan(got[bb, :, w.S:]).all()
+        err = np.abs(g[mask] - ref[mask])
+        assert (err <= bound[mask]).all(), f"max err {err.max()} vs bound {bound[mask][np.argmax(err)]}"
+
+
+# ------------------------------------------------------------------ top-k
+
+TOPK_CASES = [
+    # (rows B x T, s_cap, topk, kind)
+    ((2, 40), 300, 32, "normal"),
+    ((1, 64), 5000, 2048, "normal"),
+    ((1, 64), 5000, 2048, "ties"),
+    ((2, 16), 3000, 100, "zeros"),
+    ((1, 48), 4096, 2048, "mixed"),
+    ((1, 6), 40000, 2048, "mixed"),      # rows longer than the LDS key cache
+    ((3, 1), 33000, 2048, "normal"),
+]
+
+
+@pytest.mark.parametrize("rows,s_cap,k,kind", TOPK_CASES)
+def test_topk_is_bit_exact(rows, s_cap, k, kind):
+    B, T = rows
+    sc = synth.scores_for_topk(s_cap + B * T + k, B * T, s_cap, kind).reshape(B, T, s_cap)
+    rng = np.random.default_rng(s_cap + k)
+    ke = rng.integers(0, s_cap + 1, (B, T)).astype(np.int32)
+    ke[0, 0] = s_cap
+    ke[0, -1] = min(k, s_cap)             # n == k
+    if T > 2:
+        ke[0, 1] = min(k + 1, s_cap)      # n == k + 1
+    ks = np.minimum(rng.integers(0, 50, (B, T)), ke).astype(np.int32)
+    ks[0, 0] = 0
+    out = torch.full((B, T, k), -7, dtype=torch.int32, device="cuda")
+    b.topk_select(f32_dev(sc), out, s_cap, key_start=i32_dev(ks), key_end=i32_dev(ke))
+    got = out.cpu().numpy()
+    ref, _ = O.topk(sc.astype(np.float64), ks, ke, k)
+    assert np.array_equal(got, ref)
+
+
+def test_topk_short_prefix_example_on_gpu():
+    # 256 candidates, index_topk 2048: 256 ascending positions then 1792 x -1
+    sc = synth.scores_for_topk(3, 1, 256, "normal").reshape(1, 1, 256)
+    out = torch.zeros((1, 1, 2048), dtype=torch.int32, device="cuda")
+    b.topk_select(f32_dev(sc), out, 256)
+    got = out.cpu().numpy()[0, 0]
+    assert np.array_equal(got[:256], np.arange(256)) and (got[256:] == -1).all()
+
+
+# ------------------------------------------------------------------ sparse MLA
+
+def _mla_inputs(w, layer=0):
+    L = synth.build_layer_inputs(w, layer, False)
+    return L["mla_q"], L["kv"]
+
+
+def _random_indices(rng, B, T, S, k, holes=False):
+    idx = np.full((B, T, k), -1, np.int32)
+    for bb in range(B):
+        for t in range(T):
+            n = int(rng.integers(0, min(k, S) + 1)) if t % 5 else min(k, S)
+            idx[bb, t, :n] = np.sort(rng.choice(S, n, replace=False))
+            if holes and n > 4:
+                idx[bb, t, 1] = -1
+                idx[bb, t, 3] = S + 5          # out of range: skipped
+    idx[0, 0] = -1                             # empty row
+    return idx
+
+
+MLA_CASES = {
+    "fp32_generic": dict(B=1, T=30, S=256, Hm=8, Dc=64, Dr=16, topk=32, mla_dtype="f32", idx_dtype="f32"),
+    "bf16_mfma": dict(B=2, T=20, S=600, topk=256),
+    "bf16_mfma_h128": dict(B=1, T=9, S=700, topk=192, Hm=128),
+    "bf16_decode_split": dict(B=3, T=1, S=3000, topk=2048),
+    "bf16_generic_small_heads": dict(B=1, T=12, S=200, topk=64, Hm=16, Dc=128, Dr=32),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MLA_CASES))
+def test_sparse_mla_matches_oracle(case):
+    w = _wl(**MLA_CASES[case])
+    q, kv = _mla_inputs(w)
+    rng = np.random.default_rng(11)
+    idx = _random_indices(rng, w.B, w.T, w.S, w.topk, holes=True)
+    R = w.Dc + w.Dr
+    out = torch.full((w.B, w.T, w.Hm, w.Dc), float("nan"), device="cuda",
+                     dtype=torch.float32 if w.mla_dtype == "f32" else torch.bfloat16)
+    lse = torch.full((w.B, w.T, w.Hm), float("nan"), device="cuda")
+    shape = b.make_shape(w.B, w.T, w.S, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr)
+    ws = torch.empty(max(b.workspace_bytes(shape, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+    b.sparse_mla_attention(to_dev(q, w.mla_dtype), to_dev(kv, w.mla_dtype), i32_dev(idx), w.sm_scale, out, lse,
+                           Dc=w.Dc, workspace=ws)
+    got = out.float().cpu().numpy()
+    gl = lse.cpu().numpy()
+    q64, kv64 = O.decode(q, w.mla_dtype), O.decode(kv, w.mla_dtype)
+    ref, rl = O.sparse_mla(q64, kv64, idx, w.sm_scale, w.Dc)
+    tol = ATTN_TOL[w.mla_dtype]
+    assert max_abs_rel(got, ref) <= tol
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    assert np.max(np.abs(gl[fin] - rl[fin])) / np.max(np.abs(rl[fin])) <= tol
+    assert not got[0, 0].any()                                   # empty selection -> 0
+
+
+def test_sparse_mla_full_selection_equals_dense_causal():
+    # top-k >= prefix: the indexer degenerates to dense causal attention
+    w = _wl(B=1, T=48, S=48, topk=64)
+    q, kv = _mla_inputs(w)
+    idx = np.full((1, 48, 64), -1, np.int32)
+    for t in range(48):
+        idx[0, t, :t + 1] = np.arange(t + 1)
+    out = torch.empty((1, 48, 64, 512), device="cuda", dtype=torch.bfloat16)
+    b.sparse_mla_attention(to_dev(q, "bf16"), to_dev(kv, "bf16"), i32_dev(idx), w.sm_scale, out, Dc=512)
+    q64, kv64 = O.decode(q, "bf16"), O.decode(kv, "bf16")
+    qq = torch.from_numpy(q64[0]).permute(1, 0, 2)[None]
+    kk = torch.from_numpy(kv64[0])[None, None].expand(1, 64, 48, 576)
+    vv = torch.from_numpy(np.ascontiguousarray(kv64[0][:, :512]))[None, None].expand(1, 64, 48, 512)
+    dense = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True, scale=w.sm_scale)
+    ref = dense[0].permute(1, 0, 2).numpy()
+    assert max_abs_rel(out.float().cpu().numpy()[0], ref) <= ATTN_TOL["bf16"]
+
+
+# ------------------------------------------------------------------ group
+
+def _upload_group(w, inputs):
+    dev = []
+    for l, L in enumerate(inputs):
+        d = {"q": to_dev(L["mla_q"], w.mla_dtype), "kv": to_dev(L["kv"], w.mla_dtype),
+             "out": torch.empty((w.B, w.T, w.Hm, w.Dc), device="cuda",
+                                dtype=torch.float32 if w.mla_dtype == "f32" else torch.bfloat16),
+             "lse": torch.empty((w.B, w.T, w.Hm), device="cuda")}
+        if "idx_q" in L:
+            d["index"] = {"q": to_dev(L["idx_q"], w.idx_dtype), "k": to_dev(L["idx_k"], w.idx_dtype),
+                          "w": f32_dev(L["w"])}
+            if w.idx_dtype == "fp8":
+                d["index"]["q_scale"] = f32_dev(L["idx_q_scale"])
+                d["index"]["k_scale"] = f32_dev(L["idx_k_scale"])
+        dev.append(d)
+    return dev
+
+
+def _run_group(w, dev, ke_dev, ks_dev=None, cache=None, tag=1, types=None):
+    types = types or ["full" if c == "F" else "shared" for c in w.layers]
+    shape = b.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
+                         key_start=ks_dev, key_end=ke_dev)
+    ws = torch.empty(max(b.workspace_bytes(shape, b.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
+    cache = cache or b.IndexCache(w.B, w.T, w.topk)
+    mdt = b.F32 if w.mla_dtype == "f32" else b.BF16
+    stats = b.group_forward(shape, mdt, types, dev, w.sm_scale, cache, tag, ws)
+    return cache, stats
+
+
+def _check_group(w, inputs, dev, cache_idx_per_layer, rows):
+    """Compare indices (tie band) and per-layer attention on the given (b, t) rows."""
+    ke, ks = w.key_end(), w.key_start()
+    donors = O.donor_map(["full" if c == "F" else "shared" for c in w.layers])
+    ref_idx = {}
+    exact_rows = {}
+    for l in sorted(set(donors)):
+        q64, k64, w64 = decode_index(inputs[l], w)
+        ref_idx[l] = {}
+        exact_rows[l] = set()
+        for (bb, t) in rows:
+            s_row = O.index_scores_row(q64[bb, t], k64[bb], w64[bb, t], int(ks[bb, t]), int(ke[bb, t]))
+            r, tau = O.topk_row(s_row, int(ks[bb, t]), int(ke[bb, t]), w.topk)
+            ref_idx[l][(bb, t)] = r
+            if check_topk_row(cache_idx_per_layer[l][bb, t], r, s_row, int(ks[bb, t]), tau):
+                exact_rows[l].add((bb, t))
+    assert all(len(exact_rows[l]) >= 0.9 * len(rows) for l in exact_rows)
+    for l, L in enumerate(inputs):
+        got = dev[l]["out"].float().cpu().numpy()
+        kv64 = O.decode(L["kv"], w.mla_dtype)
+        use = [r for r in rows if r in exact_rows[donors[l]]]
+        g = np.stack([got[bb, t] for bb, t in use])
+        ref = np.stack([O.sparse_mla_row(O.decode(L["mla_q"][bb, t], w.mla_dtype), kv64[bb],
+                                         ref_idx[donors[l]][(bb, t)], w.sm_scale, w.Dc)[0] for bb, t in use])
+        assert max_abs_rel(g, ref) <= ATTN_TOL[w.mla_dtype], f"layer {l}"
+
+
+def test_group_tiny_fp32_workload_all_rows():
+    w = synth.WORKLOADS["tiny_prefill256_fp32"]
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    cache, stats = _run_group(w, dev, i32_dev(w.key_end()))
+    assert (stats.n_full, stats.n_shared) == (1, 3)
+    idx = cache.indices.cpu().numpy()
+    rows = [(0, t) for t in range(w.T)]
+    _check_group(w, inputs, dev, {0: idx}, rows)
+    # whole-tensor comparison against the oracle group (all rows matched exactly above)
+    layers64 = []
+    for L in inputs:
+        d = {"mla_q": O.decode(L["mla_q"], "f32"), "kv": O.decode(L["kv"], "f32")}
+        if "idx_q" in L:
+            d.update(idx_q=O.decode(L["idx_q"], "f32"), idx_k=O.decode(L["idx_k"], "f32"), w=L["w"].astype(float))
+        layers64.append(d)
+    ref = O.group_forward(layers64, ["full", "shared", "shared", "shared"], w.key_start(), w.key_end(), w.topk,
+                          w.sm_scale, w.Dc)
+    if np.array_equal(ref["indices"][0], idx):
+        for l in range(4):
+            assert max_abs_rel(dev[l]["out"].cpu().numpy(), ref["out"][l]) <= ATTN_TOL["f32"]
+
+
+@pytest.mark.parametrize("idx_dtype,Hk", [("bf16", 32), ("fp8", 32), ("bf16", 1)])
+def test_group_mid_size_all_rows(idx_dtype, Hk):
+    w = _wl(B=2, T=300, S=700, pos0=400, topk=256, idx_dtype=idx_dtype, Hk=Hk, layers="FFSSFS")
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    cache, stats = _run_group(w, dev, i32_dev(w.key_end()))
+    assert (stats.n_full, stats.n_shared) == (3, 3)
+    # the cache ends with the last full layer's (layer 4) indices; donors 0 and 1 are
+    # recomputed by single-full-layer calls on their inputs (same kernels, same bytes)
+    per_layer = {4: cache.indices.cpu().numpy()}
+    rows = [(bb, t) for bb in range(w.B) for t in range(0, w.T, 7)]
+    for donor in (0, 1):
+        c2, _ = _run_group(w, [dev[donor]], i32_dev(w.key_end()), types=["full"])
+        per_layer[donor] = c2.indices.cpu().numpy()
+    _check_group(w, inputs, dev, per_layer, rows)
+
+
+def test_group_cache_reuse_across_calls_and_errors():
+    w = _wl(B=1, T=100, S=100, topk=32, layers="FS")
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    ke = i32_dev(w.key_end())
+    cache, _ = _run_group(w, dev, ke, tag=42)
+    first = dev[1]["out"].clone()
+    assert cache.valid and cache.c.donor_layer == 0 and cache.c.tag == 42
+    # a later call starting on a shared layer reuses the handle
+    dev2 = _upload_group(w, inputs[1:])
+    _run_group(w, dev2, ke, cache=cache, tag=42, types=["shared"])
+    assert torch.equal(dev2[0]["out"], first)
+    with pytest.raises(b.DsaError) as e:
+        _run_group(w, dev2, ke, cache=cache, tag=43, types=["shared"])
+    assert e.value.status == 4
+    with pytest.raises(b.DsaError) as e:
+        _run_group(w, dev2, ke, cache=b.IndexCache(1, 100, 32), tag=42, types=["shared"])
+    assert e.value.status == 3
+
+
+def test_group_is_deterministic_and_shared_layers_match_standalone():
+    w = _wl(B=1, T=200, S=400, pos0=200, topk=128)
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    ke = i32_dev(w.key_end())
+    cache, _ = _run_group(w, dev, ke)
+    outs = [d["out"].clone() for d in dev]
+    idx = cache.indices.clone()
+    cache2, _ = _run_group(w, dev, ke)
+    assert torch.equal(cache2.indices, idx)
+    for l in range(4):
+        assert torch.equal(dev[l]["out"], outs[l])
+    # shared layer l == standalone attention with the donor's indices, bit for bit
+    shape = b.make_shape(w.B, w.T, w.S, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr)
+    mws = torch.empty(max(b.workspace_bytes(shape, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+    for l in range(1, 4):
+        o = torch.empty_like(outs[l])
+        b.sparse_mla_attention(dev[l]["q"], dev[l]["kv"], idx, w.sm_scale, o, Dc=512, workspace=mws)
+        assert torch.equal(o, outs[l])
+
+
+def test_group_prefill4k_full_size_sampled_rows():
+    w = synth.WORKLOADS["prefill4k_bf16"]
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    cache, stats = _run_group(w, dev, i32_dev(w.key_end()))
+    idx = cache.indices.cpu().numpy()
+    rng = np.random.default_rng(0)
+    ts = sorted(set([0, 1, 2, 100, 2046, 2047, 2048, 2049, 3000, 4095] + rng.integers(0, 4096, 14).tolist()))
+    _check_group(w, inputs, dev, {0: idx}, [(0, t) for t in ts])
