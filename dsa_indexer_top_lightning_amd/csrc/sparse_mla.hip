@@ -8,22 +8,29 @@
 // 576 values (Megatron-Bridge pull request, commit on the rope-dim parse); it is
 // the key, and its first 512 values are the value.
 //
-// mla_mfma (bf16, Dc = 512, Dr = 64, 64 heads per workgroup):
-//   * the workgroup's indices are compacted (valid entries, original order) into
-//     LDS; tiles of 64 selected rows are gathered from HBM with 16-byte loads
-//     (a latent row is 1152 contiguous bytes) into one row-major LDS tile, the
-//     next tile being prefetched into registers while the current one is used;
+// mla_mfma (bf16, Dc = 512, Dr = 64, 64 heads per workgroup, 4 waves):
+//   * tiles of 64 selected rows are gathered from HBM straight into LDS with
+//     16-byte global_load_lds (a latent row is 1152 contiguous bytes) into two
+//     alternating tiles; the gather of tile i+1 runs while tile i is consumed.
+//     A tile is stored chunk-major: the 16-byte chunk c of all 64 rows forms one
+//     1 KiB column (one wave load), rows XOR-permuted by the column's parity so
+//     that the matrix-core fragment reads are bank-conflict free;
 //   * wave (hh, vv) computes S^T = K Q^T for kv rows [32vv, +32) x heads
-//     [32hh, +32) on v_mfma_f32_32x32x16_bf16 (Q^T fragments live in registers
-//     for the whole kernel), the two vv waves of a head half swap their halves
-//     through LDS, and run the online softmax (exp2, fp32) for all 64 rows;
-//   * the same wave accumulates O^T[256vv..+256 dims][32 heads] += V^T P^T; the
-//     V^T fragments come straight from the row-major tile with ds_read_b64_tr_b16
+//     [32hh, +32) on v_mfma_f32_32x32x16_bf16 (Q^T fragments stay in registers
+//     for the whole kernel); the two vv waves of a head half swap their row
+//     maxima, then their bf16 probabilities, through LDS, so both hold P^T for all
+//     64 rows with one shared running max (online softmax in exp2, fp32 state);
+//     the running sum adds the bf16 probabilities actually used;
+//   * the same wave accumulates O^T[256vv .. +256 dims][32 heads] += V^T P^T; the
+//     V^T fragments come from the same tile through ds_read_b64_tr_b16
 //     (transposing LDS reads), so K and V share one LDS copy;
-//   * with several workgroups per query (decode: few queries), each writes an
-//     unnormalised partial (O, running max, sum) and mla_combine merges them in
-//     a fixed order (no float atomics: results are run-to-run identical).
+//   * with few queries (decode) each query's selection is split over several
+//     workgroups that write unnormalised partials (O, running max, sum) and
+//     mla_combine merges them in a fixed order (no float atomics: results are
+//     run-to-run identical).
 // mla_generic: any Dc/Dr/Hm, fp32 or bf16, one wave per head, fp32 FMA.
+#include <algorithm>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -37,11 +44,16 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int MT = 64;            // selected rows per tile
 constexpr int MROW = 576;         // latent row (Dc + Dr)
 constexpr int MDC = 512;          // value dims
-constexpr int MRS = 1168;         // padded LDS row stride in bytes (1152 + 16)
-constexpr int MCH = 72;           // 16-byte chunks per row
+constexpr int MRB = MROW * 2;     // bytes per latent row
+constexpr int MCH = MRB / 16;     // 16-byte chunks per row = LDS columns per tile (72)
 constexpr int MHG = 64;           // heads per workgroup
-constexpr int MPF = MT * MCH / 256;  // prefetched chunks per thread (18)
-constexpr int MAX_CHUNK = 4096;   // selected entries handled by one workgroup
+constexpr int COL_BYTES = MT * 16;               // one column: chunk c of the 64 rows
+constexpr int TILE_BYTES = MCH * COL_BYTES;      // 73728
+constexpr int COLS_PER_WAVE = MCH / 4;           // columns gathered by each wave (18)
+constexpr int LDS_XMAX = 4 * 32 * 4;             // per-wave tile maxima of 32 heads
+constexpr int LDS_XP = 4 * 8 * 64 * 4;           // per-wave P^T tile as bf16 pairs
+constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP;
+constexpr int MAX_TILES_PER_ITEM = 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -54,30 +66,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
-  union {
-    uint16_t u[8];
-    bf16x8 b;
-  } r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r.u[e] = f32_to_bf16_bits(v[e]);
-  return r.b;
-}
+// LDS tile layout: row r's 16-byte chunk c sits at byte c * 1024 + 16 * slot(r, c),
+// slot(r, c) = r ^ (4 * (c & 1)).  Adjacent columns then place a 4-row group at
+// different bank offsets, which makes the transposing V reads conflict free.
+__device__ __forceinline__ int slot(int r, int c) { return r ^ ((c & 1) << 2); }
 
-// LDS layout of mla_mfma (dynamic): tile [MT][MRS] bytes | xbuf [4 waves][16][64] f32 | idx list [chunk] i32
-constexpr int LDS_TILE = MT * MRS;
-constexpr int LDS_XBUF = 4 * 16 * 64 * 4;
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 // grid.x = (query, split) work item, heaviest queries first; grid.y = head group.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  unsigned char* tile = smem;
-  float* xbuf = reinterpret_cast<float*>(smem + LDS_TILE);
-  int32_t* idxl = reinterpret_cast<int32_t*>(smem + LDS_TILE + LDS_XBUF);
-  __shared__ uint32_t wcnt[4];
+  float* xmax = reinterpret_cast<float*>(smem + 2 * TILE_BYTES);
+  uint32_t* xp = reinterpret_cast<uint32_t*>(smem + 2 * TILE_BYTES + LDS_XMAX);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int hh = wave & 1, vv = wave >> 1;
   const int lr = lane & 31, lg = lane >> 5;
   const int64_t rows = (int64_t)p.B * p.T;
@@ -87,45 +91,32 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
   const int hg = blockIdx.y;
   const int64_t b = tok / p.T;
   const int64_t s_cap = p.s_cap;
+  const int topk = p.topk;
+  const int32_t* gidx = p.idx + tok * (int64_t)topk;
 
-  // ---- compact this split's valid indices into LDS (original order)
-  const int e0 = split * chunk;
-  const int e1 = min(p.topk, e0 + chunk);
-  const int32_t* gidx = p.idx + tok * (int64_t)p.topk;
-  int nv = 0;
-  for (int c0 = e0; c0 < e1; c0 += 256) {
-    const int e = c0 + tid;
-    int32_t v = -1;
-    if (e < e1) v = gidx[e];
-    const bool ok = (e < e1) && v >= 0 && (int64_t)v < s_cap;
-    const uint64_t m = __ballot(ok);
-    if (lane == 0) wcnt[wave] = (uint32_t)__popcll(m);
-    __syncthreads();
-    int before = nv;
-    int total = 0;
-    for (int w = 0; w < 4; ++w) {
-      total += (int)wcnt[w];
-      if (w < wave) before += (int)wcnt[w];
-    }
-    before += (int)__popcll(m & ((1ull << lane) - 1ull));
-    if (ok) idxl[before] = v;
-    nv += total;
-    __syncthreads();
+  // ---- tiles of this split up to the last one holding a valid entry: [t0, t0 + ntiles)
+  const int t0 = split * tiles_per_split;
+  const int e_lo = t0 * MT, e_hi = min(topk, (t0 + tiles_per_split) * MT);
+  int emax = -1;
+#pragma unroll 8
+  for (int e = e_lo + lane; e < e_hi; e += 64) {
+    const int32_t v = gidx[e];
+    if (v >= 0 && (int64_t)v < s_cap) emax = e;
   }
+  for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+  const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
 
-  const int head0 = hg * MHG + 32 * hh;  // first head of this wave's half
+  const int head0 = hg * MHG + 32 * hh;
   const int myhead = head0 + lr;
-  if (nv == 0) {
+  if (ntiles == 0) {
     if (nsplit == 1) {
       uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + hg * MHG) * MDC;
       for (int i = tid; i < MHG * MDC; i += 256) og[i] = 0;
       if (p.lse && vv == 0 && lg == 0) p.lse[tok * p.Hm + myhead] = -__builtin_inff();
-    } else {
-      if (vv == 0 && lg == 0) {
-        float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + myhead) * 2;
-        ml[0] = -__builtin_inff();
-        ml[1] = 0.f;
-      }
+    } else if (vv == 0 && lg == 0) {
+      float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + myhead) * 2;
+      ml[0] = -__builtin_inff();
+      ml[1] = 0.f;
     }
     return;
   }
@@ -134,27 +125,40 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
   //      q[head][16*st + 8*lg .. +7] for st = 0..35
   bf16x8 qf[MROW / 16];
   {
-    const unsigned char* qg = static_cast<const unsigned char*>(p.q) + ((tok * p.Hm + myhead) * MROW) * 2;
+    const unsigned char* qg = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + myhead) * MRB;
 #pragma unroll
     for (int st = 0; st < MROW / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qg + (16 * st + 8 * lg) * 2);
   }
 
-  const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + (b * s_cap) * (MROW * 2);
-  const int ntiles = (nv + MT - 1) / MT;
-  i32x4 stage[MPF];
-  // Padding rows of the last tile reload a valid row (masked out of the softmax),
-  // so the loads need no branch; offsets are 32-bit from the item's uniform base.
-  auto prefetch = [&](int t) {
+  const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
+  // this lane's entry of tile t: returns validity; `load_idx` is the row to gather
+  auto entry = [&](int t, int32_t& load_idx) -> bool {
+    const int e = t * MT + lane;
+    const int32_t v = e < topk ? gidx[e] : -1;
+    const bool ok = v >= 0 && (int64_t)v < s_cap;
+    load_idx = ok ? v : 0;  // an invalid entry gathers row 0 (in bounds) and is masked
+    return ok;
+  };
+  // gather a tile into buffer bf: wave w loads columns [18w, 18w + 18); in column c
+  // lane i fills slot i, i.e. row slot(i, c) (row i for even c, row i ^ 4 for odd c)
+  auto issue = [&](int bf, int32_t lidx) {
+    const int32_t lodd = __shfl(lidx, lane ^ 4, 64);
+    const unsigned char* se = kvg + (uint32_t)lidx * (uint32_t)MRB;
+    const unsigned char* so = kvg + (uint32_t)lodd * (uint32_t)MRB;
+    unsigned char* dst = smem + bf * TILE_BYTES + wv * (COLS_PER_WAVE * COL_BYTES);
+    const int c0 = wv * COLS_PER_WAVE;  // even
 #pragma unroll
-    for (int k = 0; k < MPF; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c / MCH, ch = c % MCH;
-      const int e = min(t * MT + r, nv - 1);
-      const uint32_t off = (uint32_t)idxl[e] * (uint32_t)(MROW * 2) + (uint32_t)ch * 16u;
-      stage[k] = *reinterpret_cast<const i32x4*>(kvg + off);
+    for (int j = 0; j < COLS_PER_WAVE; ++j) {
+      const unsigned char* src = ((j & 1) ? so : se) + (c0 + j) * 16;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + j * COL_BYTES), 16, 0, 0);
     }
   };
-  prefetch(0);
+
+  int32_t li_cur, li_nxt = 0;
+  bool ok_cur = entry(t0, li_cur), ok_nxt = false;
+  wait_vmem();
+  issue(0, li_cur);
+  if (ntiles > 1) ok_nxt = entry(t0 + 1, li_nxt);
 
   const float qk_scale = p.sm_scale * LOG2E;
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -164,85 +168,103 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll
-    for (int k = 0; k < MPF; ++k) {
-      const int c = tid + 256 * k;
-      const int r = c / MCH, ch = c % MCH;
-      *reinterpret_cast<i32x4*>(tile + r * MRS + ch * 16) = stage[k];
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(t + 1);
+  // K fragment of step st: row 32vv + lr, chunk 2st + lg
+  const int kbase = lg * COL_BYTES + 16 * slot(32 * vv + lr, lg);
+  // V^T reads: row rb + (li >> 2) (+8 for read #2), chunk 32vv + 4dt + 2blk + x, byte 8 * (li & 1);
+  // slot() only flips row bit 2, which is 4*lg here, so it is a per-lane constant
+  const int blk = lr >> 4, li = lr & 15, x = (li & 3) >> 1;
+  const int vbase = (32 * vv + 2 * blk + x) * COL_BYTES + 16 * slot(4 * lg + (li >> 2), x) + ((li & 1) << 3);
 
-    // S^T (own 32 kv rows x 32 heads)
+  for (int i = 0; i < ntiles; ++i) {
+    const int bf = i & 1;
+    wait_vmem();
+    __syncthreads();  // tile i is in LDS for every wave; buffer bf^1 is free
+    const uint64_t vmask = __ballot(ok_cur);
+    if (i + 1 < ntiles) {
+      issue(bf ^ 1, li_nxt);
+      ok_cur = ok_nxt;
+      if (i + 2 < ntiles) ok_nxt = entry(t0 + i + 2, li_nxt);
+    }
+    const unsigned char* tb = smem + bf * TILE_BYTES;
+
+    // S^T for own 32 kv rows x 32 heads
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const unsigned char* krow = tile + (32 * vv + lr) * MRS;
+    const unsigned char* kp = tb + kbase;
 #pragma unroll
     for (int st = 0; st < MROW / 16; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (16 * st + 8 * lg) * 2);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + st * (2 * COL_BYTES));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s, 0, 0, 0);
-    }
-    const int valid_rows = nv - t * MT;  // rows >= valid_rows of this tile are padding
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * vv + 8 * (r >> 2) + 4 * lg + (r & 3);
-      s[r] = (m < valid_rows) ? s[r] * qk_scale : -__builtin_inff();
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) xbuf[(wave * 16 + r) * 64 + lane] = s[r];
-    __syncthreads();
-    float sl[16], sh[16];  // kv rows of half 0 and half 1
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float o = xbuf[((wave ^ 2) * 16 + r) * 64 + lane];
-      sl[r] = vv == 0 ? s[r] : o;
-      sh[r] = vv == 0 ? o : s[r];
     }
     float mx = -__builtin_inff();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sl[r], sh[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid row
-    const float alpha = exp2f(m_run - m_new);
-    float rs = 0.f;
-#pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sl[r] = exp2f(sl[r] - m_new);
-      sh[r] = exp2f(sh[r] - m_new);
-      rs += sl[r] + sh[r];
+      const int m = 32 * vv + 8 * (r >> 2) + 4 * lg + (r & 3);
+      s[r] = ((vmask >> m) & 1ull) ? s[r] * qk_scale : -__builtin_inff();
+      mx = fmaxf(mx, s[r]);
     }
-    rs += __shfl_xor(rs, 32, 64);
-    l_run = l_run * alpha + rs;
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (lg == 0) xmax[wave * 32 + lr] = mx;
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(mx, xmax[(wave ^ 2) * 32 + lr]));
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    uint32_t own[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      own[r] = (uint32_t)f32_to_bf16_bits(exp2f(s[2 * r] - m_use)) |
+               ((uint32_t)f32_to_bf16_bits(exp2f(s[2 * r + 1] - m_use)) << 16);
+      xp[(wave * 8 + r) * 64 + lane] = own[r];
+    }
+    __syncthreads();
+    uint32_t h0[8], h1[8];  // P^T of kv rows [0, 32) and [32, 64), C-layout order
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t o = xp[((wave ^ 2) * 8 + r) * 64 + lane];
+      h0[r] = vv == 0 ? own[r] : o;
+      h1[r] = vv == 0 ? o : own[r];
+    }
+    float s0 = 0.f, s1 = 0.f;  // the same sums, in the same order, in both waves of the pair
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      s0 += bf16_bits_to_f32((uint16_t)(h0[r] & 0xffff)) + bf16_bits_to_f32((uint16_t)(h0[r] >> 16));
+      s1 += bf16_bits_to_f32((uint16_t)(h1[r] & 0xffff)) + bf16_bits_to_f32((uint16_t)(h1[r] >> 16));
+    }
+    s0 += __shfl_xor(s0, 32, 64);
+    s1 += __shfl_xor(s1, 32, 64);
+    const float alpha = exp2f(m_run - m_use);
+    l_run = l_run * alpha + (s0 + s1);
     m_run = m_new;
 #pragma unroll
     for (int d = 0; d < 8; ++d)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
 
-    // P^T fragments: step sg covers half sg/2, C-layout values 8*(sg%2) .. +7
+    // P^T fragments: step sg covers C-layout values 8*(sg%2) .. +7 of half sg/2
     bf16x8 pf[4];
-    pf[0] = pack_bf16x8(sl);
-    pf[1] = pack_bf16x8(sl + 8);
-    pf[2] = pack_bf16x8(sh);
-    pf[3] = pack_bf16x8(sh + 8);
-
-    // O^T[256vv + 32dt .. +32][32 heads] += V^T . P^T
-    const int blk = lr >> 4, li = lr & 15;
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg) {
-      const int kvb = 32 * (sg >> 1) + 16 * (sg & 1) + 4 * lg + (li >> 2);  // row of this lane's read #1
-      const unsigned char* r1 = tile + kvb * MRS;
-      const unsigned char* r2 = r1 + 8 * MRS;
+      union {
+        uint32_t u[4];
+        bf16x8 b;
+      } u;
+      const uint32_t* src = (sg < 2) ? h0 : h1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u.u[e] = src[4 * (sg & 1) + e];
+      pf[sg] = u.b;
+    }
+
+    // O^T[256vv + 32dt .. +32][32 heads] += V^T . P^T, V^T fragments by transposing LDS reads:
+    // read #1 of step sg gives rows rb .. rb+3 of column (lane), read #2 rows rb+8 .. rb+11
+    const unsigned char* vp = tb + vbase;
+#pragma unroll
+    for (int sg = 0; sg < 4; ++sg) {
+      const int rb = 32 * (sg >> 1) + 16 * (sg & 1);  // row offset of read #1; read #2 is 8 rows on
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const int col = 256 * vv + 32 * dt + 16 * blk + 4 * (li & 3);
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(r1 + col * 2));
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(r2 + col * 2));
+        const unsigned char* r1 = vp + dt * (4 * COL_BYTES) + rb * 16;
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)r1);
+        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(r1 + 128));
         union {
           i16x4 h[2];
           bf16x8 b;
@@ -259,7 +281,7 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
     __syncthreads();
     constexpr int OST = MDC + 8;  // padded bf16 row stride of the staging buffer
     uint16_t* ost = reinterpret_cast<uint16_t*>(smem);
-    const float inv = 1.f / l_run;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const int hl = 32 * hh + lr;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -268,7 +290,7 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
         const int dim = 256 * vv + 32 * dt + 8 * j + 4 * lg;
         uint16_t* dst = ost + hl * OST + dim;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = f32_to_bf16_bits(acc[dt][4 * j + i] * inv);
+        for (int q = 0; q < 4; ++q) dst[q] = f32_to_bf16_bits(acc[dt][4 * j + q] * inv);
       }
     __syncthreads();
     unsigned char* og = static_cast<unsigned char*>(p.out) + ((tok * p.Hm + hg * MHG) * MDC) * 2;
@@ -277,7 +299,8 @@ void mla_mfma(MlaParams p, int nsplit, int chunk, float* __restrict__ ws_o, floa
       *reinterpret_cast<i32x4*>(og + (h * MDC) * 2 + ch * 16) =
           *reinterpret_cast<const i32x4*>(reinterpret_cast<const unsigned char*>(ost + h * OST) + ch * 16);
     }
-    if (p.lse && vv == 0 && lg == 0) p.lse[tok * p.Hm + myhead] = (m_run + log2f(l_run)) * LN2;
+    if (p.lse && vv == 0 && lg == 0)
+      p.lse[tok * p.Hm + myhead] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -__builtin_inff();
   } else {
     float* o = ws_o + ((tok * nsplit + split) * p.Hm + myhead) * MDC;
 #pragma unroll
@@ -386,23 +409,20 @@ __global__ __launch_bounds__(256) void mla_generic(MlaParams p) {
 }
 
 struct SplitPlan {
-  int nsplit, chunk;
+  int nsplit, tiles_per_split;
 };
 
+// Few queries (decode): split each query's selection over several workgroups so
+// that >= 512 run; every split covers whole 64-row tiles.
 SplitPlan plan_split(int64_t rows, int Hm, int topk) {
   const int64_t wgs = rows * (Hm / MHG);
+  const int tiles = (topk + MT - 1) / MT;
   int nsplit = 1;
-  const int max_split = (topk + MT - 1) / MT;
-  // few queries (decode): split the selection so that >= 512 workgroups run
-  if (wgs < 512) nsplit = (int)std::min<int64_t>(max_split, (512 + wgs - 1) / std::max<int64_t>(wgs, 1));
-  int chunk = (topk + nsplit - 1) / nsplit;
-  chunk = ((chunk + MT - 1) / MT) * MT;
-  while (chunk > MAX_CHUNK) {
-    ++nsplit;
-    chunk = (((topk + nsplit - 1) / nsplit + MT - 1) / MT) * MT;
-  }
-  nsplit = (topk + chunk - 1) / chunk;
-  return {nsplit, chunk};
+  if (wgs < 512) nsplit = (int)std::min<int64_t>(tiles, (512 + wgs - 1) / std::max<int64_t>(wgs, 1));
+  int tps = (tiles + nsplit - 1) / nsplit;
+  tps = std::min(tps, MAX_TILES_PER_ITEM);
+  nsplit = (tiles + tps - 1) / tps;
+  return {nsplit, tps};
 }
 
 }  // namespace
@@ -425,7 +445,7 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t, hip
   if (rows == 0) return hipSuccess;
   if (mla_uses_mfma(p.Hm, p.Dc, p.Dr, p.s_cap, dt)) {
     const SplitPlan sp = plan_split(rows, p.Hm, p.topk);
-    const size_t lds = LDS_TILE + LDS_XBUF + (size_t)sp.chunk * 4;
+    const size_t lds = LDS_MLA;
     static std::atomic<size_t> high{0};
     const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(mla_mfma), lds, high);
     if (attr != hipSuccess) return attr;
@@ -436,7 +456,7 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t, hip
       ws_ml = ws_o + (size_t)rows * sp.nsplit * p.Hm * MDC;
     }
     dim3 grid((unsigned)(rows * sp.nsplit), (unsigned)(p.Hm / MHG));
-    hipLaunchKernelGGL(mla_mfma, grid, dim3(256), lds, st, p, sp.nsplit, sp.chunk, ws_o, ws_ml);
+    hipLaunchKernelGGL(mla_mfma, grid, dim3(256), lds, st, p, sp.nsplit, sp.tiles_per_split, ws_o, ws_ml);
     if (n_launches) ++*n_launches;
     if (sp.nsplit > 1) {
       hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4))), dim3(256), 0, st, p, sp.nsplit,
