@@ -40,6 +40,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int MT = 64;            // selected rows per tile
 constexpr int MROW = 576;         // latent row (Dc + Dr)
@@ -54,6 +56,10 @@ constexpr int LDS_XMAX = 4 * 32 * 4;             // per-wave tile maxima of 32 h
 constexpr int LDS_XP = 4 * 8 * 64 * 4;           // per-wave P^T tile as bf16 pairs
 constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP;
 constexpr int MAX_TILES_PER_ITEM = 64;
+// The running max is raised only when a tile's max exceeds it by more than 2^8 (log2
+// units); until then probabilities are taken against the stale max (values <= 256),
+// which is exact after the final division and saves rescaling the accumulators.
+constexpr float RESCALE_LOG2 = 8.f;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -70,6 +76,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // slot(r, c) = r ^ (4 * (c & 1)).  Adjacent columns then place a 4-row group at
 // different bank offsets, which makes the transposing V reads conflict free.
 __device__ __forceinline__ int slot(int r, int c) { return r ^ ((c & 1) << 2); }
+
+// two floats -> packed bf16 pair (round to nearest even, hardware conversion)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Multiply an accumulator block in place in the AGPRs that hold it.  Written as
+// read / multiply / write per register so the compiler keeps the matrix-core
+// accumulators in AGPRs across the tile loop (a plain `acc *= alpha` on this rare
+// path makes it carry all of them in VGPRs, copying every tile).
+__device__ __forceinline__ void scale_agpr(f32x16& a, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = a[r], t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t)
+                 : "v"(alpha));
+    a[r] = x;
+  }
+}
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -187,33 +214,62 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;
 
-    // S^T for own 32 kv rows x 32 heads
+    // S^T for own 32 kv rows x 32 heads; K fragments read one group of 6 steps ahead
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const unsigned char* kp = tb + kbase;
+    {
+      constexpr int KG = 4;  // fragments per group
+      const unsigned char* kp = tb + kbase;
+      bf16x8 kf[2][KG];
 #pragma unroll
-    for (int st = 0; st < MROW / 16; ++st) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + st * (2 * COL_BYTES));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s, 0, 0, 0);
+      for (int u = 0; u < KG; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(kp + u * (2 * COL_BYTES));
+#pragma unroll
+      for (int g = 0; g < MROW / 16 / KG; ++g) {
+        if (g + 1 < MROW / 16 / KG) {
+#pragma unroll
+          for (int u = 0; u < KG; ++u)
+            kf[(g + 1) & 1][u] = *reinterpret_cast<const bf16x8*>(kp + (KG * (g + 1) + u) * (2 * COL_BYTES));
+        }
+#pragma unroll
+        for (int u = 0; u < KG; ++u)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g & 1][u], qf[KG * g + u], s, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     float mx = -__builtin_inff();
+    if (vmask != ~0ull) {  // partial tile: mask rows without a valid index
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = 32 * vv + 8 * (r >> 2) + 4 * lg + (r & 3);
-      s[r] = ((vmask >> m) & 1ull) ? s[r] * qk_scale : -__builtin_inff();
-      mx = fmaxf(mx, s[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * vv + 8 * (r >> 2) + 4 * lg + (r & 3);
+        s[r] = ((vmask >> m) & 1ull) ? s[r] * qk_scale : -__builtin_inff();
+        mx = fmaxf(mx, s[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] *= qk_scale;
+        mx = fmaxf(mx, s[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lg == 0) xmax[wave * 32 + lr] = mx;
     __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(mx, xmax[(wave ^ 2) * 32 + lr]));
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    // both waves of a head pair see the same maxima, so they take the same decisions
+    const float m_tile = fmaxf(mx, xmax[(wave ^ 2) * 32 + lr]);
+    if (__ballot(m_tile > m_run + RESCALE_LOG2)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) scale_agpr(acc[d], alpha);
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     uint32_t own[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      own[r] = (uint32_t)f32_to_bf16_bits(exp2f(s[2 * r] - m_use)) |
-               ((uint32_t)f32_to_bf16_bits(exp2f(s[2 * r + 1] - m_use)) << 16);
+      own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
       xp[(wave * 8 + r) * 64 + lane] = own[r];
     }
     __syncthreads();
@@ -227,18 +283,12 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     float s0 = 0.f, s1 = 0.f;  // the same sums, in the same order, in both waves of the pair
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      s0 += bf16_bits_to_f32((uint16_t)(h0[r] & 0xffff)) + bf16_bits_to_f32((uint16_t)(h0[r] >> 16));
-      s1 += bf16_bits_to_f32((uint16_t)(h1[r] & 0xffff)) + bf16_bits_to_f32((uint16_t)(h1[r] >> 16));
+      s0 += __uint_as_float(h0[r] << 16) + __uint_as_float(h0[r] & 0xffff0000u);
+      s1 += __uint_as_float(h1[r] << 16) + __uint_as_float(h1[r] & 0xffff0000u);
     }
     s0 += __shfl_xor(s0, 32, 64);
     s1 += __shfl_xor(s1, 32, 64);
-    const float alpha = exp2f(m_run - m_use);
-    l_run = l_run * alpha + (s0 + s1);
-    m_run = m_new;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+    l_run += s0 + s1;
 
     // P^T fragments: step sg covers C-layout values 8*(sg%2) .. +7 of half sg/2
     bf16x8 pf[4];
@@ -255,23 +305,37 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
 
     // O^T[256vv + 32dt .. +32][32 heads] += V^T . P^T, V^T fragments by transposing LDS reads:
-    // read #1 of step sg gives rows rb .. rb+3 of column (lane), read #2 rows rb+8 .. rb+11
-    const unsigned char* vp = tb + vbase;
+    // read #1 of step sg gives rows rb .. rb+3 of column (lane), read #2 rows rb+8 .. rb+11;
+    // the 8 fragments of step sg+1 are read while step sg's MFMAs run
+    {
+      const unsigned char* vp = tb + vbase;
+      bf16x8 vf[2][4];
+      // group q = (step sg, dims half dh): 4 fragments dt = 4dh .. 4dh+3
+      auto load_v = [&](int q, bf16x8* dst) {
+        const int sg = q >> 1, dh = q & 1;
+        const int rb = 32 * (sg >> 1) + 16 * (sg & 1);
 #pragma unroll
-    for (int sg = 0; sg < 4; ++sg) {
-      const int rb = 32 * (sg >> 1) + 16 * (sg & 1);  // row offset of read #1; read #2 is 8 rows on
+        for (int u = 0; u < 4; ++u) {
+          const unsigned char* r1 = vp + (4 * dh + u) * (4 * COL_BYTES) + rb * 16;
+          union {
+            i16x4 h[2];
+            bf16x8 b;
+          } a;
+          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)r1);
+          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(r1 + 128));
+          dst[u] = a.b;
+        }
+      };
+      load_v(0, vf[0]);
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const unsigned char* r1 = vp + dt * (4 * COL_BYTES) + rb * 16;
-        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)r1);
-        const i16x4 v2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(r1 + 128));
-        union {
-          i16x4 h[2];
-          bf16x8 b;
-        } a;
-        a.h[0] = v1;
-        a.h[1] = v2;
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.b, pf[sg], acc[dt], 0, 0, 0);
+      for (int q = 0; q < 8; ++q) {
+        if (q + 1 < 8) load_v(q + 1, vf[(q + 1) & 1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int dt = 4 * (q & 1) + u;
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q & 1][u], pf[q >> 1], acc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -288,9 +352,9 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int dim = 256 * vv + 32 * dt + 8 * j + 4 * lg;
-        uint16_t* dst = ost + hl * OST + dim;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) dst[q] = f32_to_bf16_bits(acc[dt][4 * j + q] * inv);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(ost + hl * OST + dim);
+        dst[0] = pack_bf16x2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv);
+        dst[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
       }
     __syncthreads();
     unsigned char* og = static_cast<unsigned char*>(p.out) + ((tok * p.Hm + hg * MHG) * MDC) * 2;

@@ -331,3 +331,30 @@ def test_group_prefill4k_full_size_sampled_rows():
     rng = np.random.default_rng(0)
     ts = sorted(set([0, 1, 2, 100, 2046, 2047, 2048, 2049, 3000, 4095] + rng.integers(0, 4096, 14).tolist()))
     _check_group(w, inputs, dev, {0: idx}, [(0, t) for t in ts])
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_sparse_mla_running_max_moves(direction):
+    # logits grow (or shrink) by several log2 units per 64-row tile, so the running
+    # max of the online softmax is raised mid-row (rising) or fixed by the first tile
+    rng = np.random.default_rng(21)
+    T, S, Hm, R = 3, 640, 64, 576
+    u = rng.standard_normal(R)
+    u /= np.linalg.norm(u)
+    gain = rng.uniform(1.0, 3.0, (T, Hm))
+    q = 0.3 * rng.standard_normal((1, T, Hm, R)) + gain[None, :, :, None] * u
+    ramp = np.arange(S) / 64.0 if direction == "rising" else (S - 1 - np.arange(S)) / 64.0
+    kv = 0.5 * rng.standard_normal((1, S, R)) + 24.0 * ramp[None, :, None] * u
+    qb = synth.f32_to_bf16_bits(q.astype(np.float32))
+    kvb = synth.f32_to_bf16_bits(kv.astype(np.float32))
+    idx = np.broadcast_to(np.arange(S, dtype=np.int32), (1, T, S)).copy()   # tiles in position order
+    sm = 1.0 / 24.0
+    out = torch.empty((1, T, Hm, 512), device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty((1, T, Hm), device="cuda")
+    shape = b.make_shape(1, T, S, topk=S, Hm=Hm, Dc=512, Dr=64)
+    ws = torch.empty(max(b.workspace_bytes(shape, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+    b.sparse_mla_attention(to_dev(qb, "bf16"), to_dev(kvb, "bf16"), i32_dev(idx), sm, out, lse, Dc=512,
+                           workspace=ws)
+    ref, rl = O.sparse_mla(O.decode(qb, "bf16"), O.decode(kvb, "bf16"), idx, sm, 512)
+    assert max_abs_rel(out.float().cpu().numpy(), ref) <= ATTN_TOL["bf16"]
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) / np.max(np.abs(rl)) <= ATTN_TOL["bf16"]
