@@ -44,7 +44,21 @@ def parse():
     ap.add_argument("--workload", default="prefill4k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (3 times) and exit: the reference "
+                         "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 3}))
 
 
 def upload(w, inputs, torch):
@@ -115,6 +129,9 @@ def cpu_baseline(w, inputs, rows):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
               f"MI355X; sharding is described in DESIGN.md)", file=sys.stderr)

@@ -16,6 +16,8 @@
 //    tiles, followed by the fused ReLU * weight reduction in fp32 registers.
 //  * indexer_generic: any dtype / D, one thread per key, fp32 FMA.  Used for the
 //    fp32 inputs and for shapes the MFMA kernel does not cover.
+#include <type_traits>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -25,6 +27,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
@@ -218,6 +222,239 @@ __global__ __launch_bounds__(256) void indexer_mfma(IndexerParams p) {
   }
 }
 
+// ----------------------------------------------------------------- prefill tile kernel
+// A workgroup owns a 128-query x 128-key tile of one batch item; wave (wm, wn) owns
+// the 64 x 64 block [64wm, +64) x [64wn, +64) (2 x 2 MFMA tiles of 32 x 32).  For
+// each head the Q_h and K_g tiles, the head weights (and fp8 scales) are gathered
+// straight into LDS with global_load_lds into one of two alternating stages, so the
+// loads of head h+1 run under the contraction of head h.  Tiles are chunk-major:
+// 16-byte chunk c of the 128 rows forms one 2 KiB column, so a fragment read of 32
+// consecutive rows is 512 contiguous bytes (no bank conflicts).  The ReLU * weight
+// epilogue of head h-1 runs while the MFMAs of head h are in flight.
+constexpr int PQ = 128;  // queries per tile
+constexpr int PK = 128;  // keys per tile
+
+template <int DT>
+struct TileCfg {
+  static constexpr int ESZ = (DT == BF16) ? 2 : 1;
+  static constexpr int COLS = HD * ESZ / 16;      // 16-byte columns per tile (16 bf16 / 8 fp8)
+  static constexpr int COL_BYTES = 128 * 16;       // one column of the 128 rows
+  static constexpr int TILE = COLS * COL_BYTES;    // 32 KiB bf16, 16 KiB fp8
+  static constexpr int VEC = 128 * 4;              // one fp32 per row
+  static constexpr int W_OFF = 2 * TILE;           // w
+  static constexpr int QS_OFF = W_OFF + VEC;       // q scale (fp8)
+  static constexpr int KS_OFF = QS_OFF + VEC;      // k scale (fp8)
+  static constexpr int STAGE = 2 * TILE + 3 * VEC;
+  static constexpr int DMA_PER_WAVE = 2 * (2 * COLS) / 4;  // tile loads per wave per stage
+};
+
+template <int DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void indexer_tile(IndexerParams p) {
+  using C = TileCfg<DT>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int32_t rks[PQ], rke[PQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * PQ;
+  const int64_t s0 = (int64_t)blockIdx.x * PK;
+  const int H = p.H, Hk = p.Hk, T = p.T;
+  const int64_t s_cap = p.s_cap;
+
+  int live = 0;
+  if (tid < PQ) {
+    const int t = t0 + tid;
+    int64_t ks = 0, ke = 0;
+    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, s_cap, ks, ke);
+    rks[tid] = (int32_t)ks;
+    rke[tid] = (int32_t)ke;
+    live = (t < T) && (ks < s0 + PK) && (ke > s0) && (ks < ke);
+  }
+  if (!__syncthreads_or(live)) return;
+
+  // rows beyond T / s_cap load a valid row (their results are never written)
+  const int qr0 = min(t0 + lane, T - 1), qr1 = min(t0 + 64 + lane, T - 1);
+  const int64_t kr0 = min<int64_t>(s0 + lane, s_cap - 1), kr1 = min<int64_t>(s0 + 64 + lane, s_cap - 1);
+  const unsigned char* qg = static_cast<const unsigned char*>(p.q);
+  const unsigned char* kg = static_cast<const unsigned char*>(p.k);
+  const int64_t qrow = (int64_t)H * HD * C::ESZ, krow = (int64_t)Hk * HD * C::ESZ;
+  const unsigned char* q0 = qg + ((int64_t)b * T + qr0) * qrow;
+  const unsigned char* q1 = qg + ((int64_t)b * T + qr1) * qrow;
+  const unsigned char* k0 = kg + ((int64_t)b * s_cap + kr0) * krow;
+  const unsigned char* k1 = kg + ((int64_t)b * s_cap + kr1) * krow;
+
+  // gather head h (key head g) into stage st: tile loads are spread over the 4 waves,
+  // load j: tile j / (2*COLS) (0 = Q, 1 = K), column (j % (2*COLS)) / 2, row half j % 2
+  auto issue = [&](int h, int st, bool with_k) {
+    unsigned char* base = smem + st * C::STAGE;
+    const int g = (Hk == H) ? h : 0;
+#pragma unroll
+    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+      const int j = wv * C::DMA_PER_WAVE + i;
+      const int tile = j / (2 * C::COLS), col = (j % (2 * C::COLS)) >> 1, half = j & 1;
+      if (tile == 1 && !with_k) continue;
+      const unsigned char* src = tile == 0 ? (half ? q1 : q0) + (int64_t)h * HD * C::ESZ
+                                           : (half ? k1 : k0) + (int64_t)g * HD * C::ESZ;
+      unsigned char* dst = base + tile * C::TILE + col * C::COL_BYTES + half * 1024;
+      __builtin_amdgcn_global_load_lds(src + col * 16, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+    // per-row vectors: wave 0 w, wave 1 q scale, wave 2 k scale (fp8)
+    if (wv == 0 || (DT == FP8 && wv < 3)) {
+      const float* vsrc;
+      int off;
+      if (wv == 0) {
+        vsrc = p.w + (int64_t)b * T * H + h;
+        off = C::W_OFF;
+      } else if (wv == 1) {
+        vsrc = p.q_scale + (int64_t)b * T * H + h;
+        off = C::QS_OFF;
+      } else {
+        vsrc = p.k_scale + (int64_t)b * s_cap * Hk + g;
+        off = C::KS_OFF;
+      }
+      const int64_t stride = (wv == 2) ? Hk : H;
+      const int64_t r0 = (wv == 2) ? kr0 : qr0, r1 = (wv == 2) ? kr1 : qr1;
+      __builtin_amdgcn_global_load_lds(vsrc + r0 * stride, (__attribute__((address_space(3))) void*)(base + off), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc + r1 * stride, (__attribute__((address_space(3))) void*)(base + off + 256), 4, 0, 0);
+    }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 31, lg = lane >> 5;
+  f32x16 acc[2][2][2];  // [parity][row tile][col tile]
+  f32x16 tot[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
+  float wrow[2][2][16];   // [parity][row tile][value]: weight (x q scale) of this lane's result rows
+  float kcol[2][2];       // [parity][col tile]: key scale of this lane's result column
+
+  auto epilogue = [&](auto par_c) {
+    constexpr int par = decltype(par_c)::value;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = acc[par][i][j][r];
+          if constexpr (DT == FP8) v *= kcol[par][j];
+          tot[i][j][r] = fmaf(wrow[par][i][r], fmaxf(v, 0.f), tot[i][j][r]);
+        }
+  };
+
+  // one head: `st` is the stage / register parity, a compile-time constant
+  auto head = [&](int h, auto st_c) {
+    constexpr int st = decltype(st_c)::value;
+    wait_vmem();
+    __syncthreads();  // stage st holds head h; stage st^1 is free
+    const unsigned char* base = smem + st * C::STAGE;
+    const unsigned char* kbase = (Hk == H) ? base : smem;  // a shared key head stays in stage 0
+    // this head's weights (and scales) into registers before the next gather reuses the stage
+    {
+      const float* wl = reinterpret_cast<const float*>(base + C::W_OFF);
+      const float* ql = reinterpret_cast<const float*>(base + C::QS_OFF);
+      const float* kl = reinterpret_cast<const float*>(kbase + C::KS_OFF);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+          float v = wl[row];
+          if constexpr (DT == FP8) v *= ql[row];
+          wrow[st][i][r] = v;
+        }
+      if constexpr (DT == FP8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) kcol[st][j] = kl[64 * wn + 32 * j + lr];
+      }
+    }
+    if (h + 1 < H) issue(h + 1, st ^ 1, Hk == H);
+
+    // contraction of head h: 2 x 2 tiles of 32 x 32 over D = 128
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[st][i][j][r] = 0.f;
+    const unsigned char* qa = base + (64 * wm + lr) * 16;
+    const unsigned char* kb = kbase + C::TILE + (64 * wn + lr) * 16;
+    if constexpr (DT == BF16) {
+#pragma unroll
+      for (int ks = 0; ks < HD / 16; ++ks) {
+        const int col = 2 * ks + lg;  // elements 16ks + 8lg .. +7
+        bf16x8 a[2], bb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(qa + col * C::COL_BYTES + 32 * i * 16);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(kb + col * C::COL_BYTES + 32 * j * 16);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[st][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[st][i][j], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < HD / 64; ++ks) {
+        const int col = 4 * ks + 2 * lg;  // bytes 64ks + 32lg .. +31 = columns col, col+1
+        i32x8 a[2], bb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + col * C::COL_BYTES + 32 * i * 16);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (col + 1) * C::COL_BYTES + 32 * i * 16);
+          a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + col * C::COL_BYTES + 32 * j * 16);
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + (col + 1) * C::COL_BYTES + 32 * j * 16);
+          bb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[st][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[st][i][j], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    if (h > 0) epilogue(std::integral_constant<int, st ^ 1>{});
+  };
+
+  issue(0, 0, true);
+  int h = 0;
+  for (; h + 1 < H; h += 2) {
+    head(h, std::integral_constant<int, 0>{});
+    head(h + 1, std::integral_constant<int, 1>{});
+  }
+  if (h < H) {
+    head(h, std::integral_constant<int, 0>{});
+    epilogue(std::integral_constant<int, 0>{});
+  } else {
+    epilogue(std::integral_constant<int, 1>{});
+  }
+
+  // write the candidate cells: result row m = 8(r/4) + 4lg + r%4 of tile i, column lr of tile j
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t s = s0 + 64 * wn + 32 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const int t = t0 + m;
+        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = tot[i][j][r];
+      }
+    }
+}
+
 template <auto K>
 hipError_t ensure_lds(size_t bytes) {
   static std::atomic<size_t> high{0};
@@ -229,7 +466,18 @@ hipError_t ensure_lds(size_t bytes) {
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches) {
   if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;
   const bool mfma = (dt == BF16 || dt == FP8) && p.D == HD;
-  if (mfma) {
+  if (mfma && p.T >= 32) {
+    const size_t lds = 2 * (size_t)(dt == BF16 ? TileCfg<BF16>::STAGE : TileCfg<FP8>::STAGE);
+    dim3 grid((unsigned)((p.s_cap + PK - 1) / PK), (unsigned)((p.T + PQ - 1) / PQ), (unsigned)p.B);
+    hipError_t e;
+    if (dt == BF16) {
+      if ((e = ensure_lds<indexer_tile<BF16>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(indexer_tile<BF16>, grid, dim3(256), lds, st, p);
+    } else {
+      if ((e = ensure_lds<indexer_tile<FP8>>(lds)) != hipSuccess) return e;
+      hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(256), lds, st, p);
+    }
+  } else if (mfma) {
     const int rs = (dt == BF16) ? MfmaCfg<BF16>::RS : MfmaCfg<FP8>::RS;
     const size_t lds = (size_t)(TM + TN) * rs + (size_t)p.H * TM * 4 + (dt == FP8 ? (size_t)p.Hk * TN * 4 : 0);
     dim3 grid((unsigned)((p.s_cap + TN - 1) / TN), (unsigned)((p.T + TM - 1) / TM), (unsigned)p.B);

@@ -12,9 +12,11 @@
 //   * tiles of 64 selected rows are gathered from HBM straight into LDS with
 //     16-byte global_load_lds (a latent row is 1152 contiguous bytes) into two
 //     alternating tiles; the gather of tile i+1 runs while tile i is consumed.
-//     A tile is stored chunk-major: the 16-byte chunk c of all 64 rows forms one
-//     1 KiB column (one wave load), rows XOR-permuted by the column's parity so
-//     that the matrix-core fragment reads are bank-conflict free;
+//     Each wave load moves 8 rows x 128 bytes (8 whole cache lines).  A tile is
+//     stored as 9 groups of 128-byte row segments; inside a segment the 16-byte
+//     chunks are XOR-permuted by the row so that the matrix-core fragment reads
+//     (16 rows x 16 B, and the transposing reads of 4 rows x 4 chunks per
+//     half-wave) are bank-conflict free;
 //   * wave (hh, vv) computes S^T = K Q^T for kv rows [32vv, +32) x heads
 //     [32hh, +32) on v_mfma_f32_32x32x16_bf16 (Q^T fragments stay in registers
 //     for the whole kernel); the two vv waves of a head half swap their row
@@ -47,11 +49,13 @@ constexpr int MT = 64;            // selected rows per tile
 constexpr int MROW = 576;         // latent row (Dc + Dr)
 constexpr int MDC = 512;          // value dims
 constexpr int MRB = MROW * 2;     // bytes per latent row
-constexpr int MCH = MRB / 16;     // 16-byte chunks per row = LDS columns per tile (72)
+constexpr int MCH = MRB / 16;     // 16-byte chunks per row (72)
 constexpr int MHG = 64;           // heads per workgroup
-constexpr int COL_BYTES = MT * 16;               // one column: chunk c of the 64 rows
-constexpr int TILE_BYTES = MCH * COL_BYTES;      // 73728
-constexpr int COLS_PER_WAVE = MCH / 4;           // columns gathered by each wave (18)
+constexpr int SEG = 128;                         // bytes of a row segment (8 chunks, one cache line)
+constexpr int GROUP_BYTES = MT * SEG;            // one segment of all 64 rows (8 KiB)
+constexpr int NGROUP = MRB / SEG;                // 9 segments per row
+constexpr int TILE_BYTES = NGROUP * GROUP_BYTES; // 73728
+constexpr int LOADS_PER_WAVE = NGROUP * 2;       // each wave gathers 16 rows: 2 row octets x 9 segments
 constexpr int LDS_XMAX = 4 * 32 * 4;             // per-wave tile maxima of 32 heads
 constexpr int LDS_XP = 4 * 8 * 64 * 4;           // per-wave P^T tile as bf16 pairs
 constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP;
@@ -72,10 +76,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// LDS tile layout: row r's 16-byte chunk c sits at byte c * 1024 + 16 * slot(r, c),
-// slot(r, c) = r ^ (4 * (c & 1)).  Adjacent columns then place a 4-row group at
-// different bank offsets, which makes the transposing V reads conflict free.
-__device__ __forceinline__ int slot(int r, int c) { return r ^ ((c & 1) << 2); }
+// LDS tile layout: chunk c (16 B) of row r sits at byte
+//   (c / 8) * 8192 + r * 128 + 16 * ((c % 8) ^ perm(r)),   perm(r) = bit-reverse of ((r >> 1) & 7).
+// Sixteen consecutive rows read at one chunk (K fragments) then cover 16 distinct
+// 16-byte bank groups, and so do the 4 rows x 4 chunks of a half-wave of
+// transposing V reads (rows r and r + 2 differ in bit 2 of perm).
+__device__ __forceinline__ int perm(int r) {
+  const int j = (r >> 1) & 7;
+  return ((j & 1) << 2) | (j & 2) | ((j >> 2) & 1);
+}
 
 // two floats -> packed bf16 pair (round to nearest even, hardware conversion)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -166,19 +175,25 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     load_idx = ok ? v : 0;  // an invalid entry gathers row 0 (in bounds) and is masked
     return ok;
   };
-  // gather a tile into buffer bf: wave w loads columns [18w, 18w + 18); in column c
-  // lane i fills slot i, i.e. row slot(i, c) (row i for even c, row i ^ 4 for odd c)
+  // gather a tile into buffer bf: wave w loads rows [16w, 16w + 16) as 2 row octets x 9
+  // segments; in each load lane i fills row 8q + i/8 at stored chunk i%8, which holds
+  // the row's logical chunk (i%8) ^ perm(row)
   auto issue = [&](int bf, int32_t lidx) {
-    const int32_t lodd = __shfl(lidx, lane ^ 4, 64);
-    const unsigned char* se = kvg + (uint32_t)lidx * (uint32_t)MRB;
-    const unsigned char* so = kvg + (uint32_t)lodd * (uint32_t)MRB;
-    unsigned char* dst = smem + bf * TILE_BYTES + wv * (COLS_PER_WAVE * COL_BYTES);
-    const int c0 = wv * COLS_PER_WAVE;  // even
+    const unsigned char* src[2];
 #pragma unroll
-    for (int j = 0; j < COLS_PER_WAVE; ++j) {
-      const unsigned char* src = ((j & 1) ? so : se) + (c0 + j) * 16;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(dst + j * COL_BYTES), 16, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * wave + 8 * q + (lane >> 3);
+      const int32_t ri = __shfl(lidx, row, 64);
+      src[q] = kvg + (uint32_t)ri * (uint32_t)MRB + 16 * ((lane & 7) ^ perm(row));
     }
+    unsigned char* dst = smem + bf * TILE_BYTES + wv * (16 * SEG);
+#pragma unroll
+    for (int g = 0; g < NGROUP; ++g)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds(src[q] + g * SEG,
+                                         (__attribute__((address_space(3))) void*)(dst + g * GROUP_BYTES + q * 1024),
+                                         16, 0, 0);
   };
 
   int32_t li_cur, li_nxt = 0;
@@ -195,12 +210,24 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
 
-  // K fragment of step st: row 32vv + lr, chunk 2st + lg
-  const int kbase = lg * COL_BYTES + 16 * slot(32 * vv + lr, lg);
-  // V^T reads: row rb + (li >> 2) (+8 for read #2), chunk 32vv + 4dt + 2blk + x, byte 8 * (li & 1);
-  // slot() only flips row bit 2, which is 4*lg here, so it is a per-lane constant
+  // K fragment of step st: row m = 32vv + lr, chunk 2st + lg = segment st/4, chunk-in-segment
+  // 2(st%4) + lg: four per-lane offsets, the segment is an immediate
+  const int mk = 32 * vv + lr;
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = mk * SEG + 16 * ((2 * u + lg) ^ perm(mk));
+  // V^T reads: row rb + vrow (read #2: + 8), chunk c = 32vv + 4dt + 2blk + x, byte 8(li & 1);
+  // segment 4vv + dt/2, chunk-in-segment 4(dt%2) + 2blk + x; rb is a multiple of 16 so
+  // perm(row) = perm(vrow): per-lane offsets for (read, dt parity)
   const int blk = lr >> 4, li = lr & 15, x = (li & 3) >> 1;
-  const int vbase = (32 * vv + 2 * blk + x) * COL_BYTES + 16 * slot(4 * lg + (li >> 2), x) + ((li & 1) << 3);
+  const int vrow = 4 * lg + (li >> 2);
+  int voff[2][2];
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+    for (int dp = 0; dp < 2; ++dp)
+      voff[rd][dp] = 4 * vv * GROUP_BYTES + (vrow + 8 * rd) * SEG +
+                     16 * ((4 * dp + 2 * blk + x) ^ perm(vrow + 8 * rd)) + ((li & 1) << 3);
 
   for (int i = 0; i < ntiles; ++i) {
     const int bf = i & 1;
@@ -220,16 +247,17 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
     {
       constexpr int KG = 4;  // fragments per group
-      const unsigned char* kp = tb + kbase;
+      auto kfrag = [&](int st) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(tb + koff[st & 3] + (st >> 2) * GROUP_BYTES);
+      };
       bf16x8 kf[2][KG];
 #pragma unroll
-      for (int u = 0; u < KG; ++u) kf[0][u] = *reinterpret_cast<const bf16x8*>(kp + u * (2 * COL_BYTES));
+      for (int u = 0; u < KG; ++u) kf[0][u] = kfrag(u);
 #pragma unroll
       for (int g = 0; g < MROW / 16 / KG; ++g) {
         if (g + 1 < MROW / 16 / KG) {
 #pragma unroll
-          for (int u = 0; u < KG; ++u)
-            kf[(g + 1) & 1][u] = *reinterpret_cast<const bf16x8*>(kp + (KG * (g + 1) + u) * (2 * COL_BYTES));
+          for (int u = 0; u < KG; ++u) kf[(g + 1) & 1][u] = kfrag(KG * (g + 1) + u);
         }
 #pragma unroll
         for (int u = 0; u < KG; ++u)
@@ -308,7 +336,6 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     // read #1 of step sg gives rows rb .. rb+3 of column (lane), read #2 rows rb+8 .. rb+11;
     // the 8 fragments of step sg+1 are read while step sg's MFMAs run
     {
-      const unsigned char* vp = tb + vbase;
       bf16x8 vf[2][4];
       // group q = (step sg, dims half dh): 4 fragments dt = 4dh .. 4dh+3
       auto load_v = [&](int q, bf16x8* dst) {
@@ -316,13 +343,16 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
         const int rb = 32 * (sg >> 1) + 16 * (sg & 1);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const unsigned char* r1 = vp + (4 * dh + u) * (4 * COL_BYTES) + rb * 16;
+          const int dt = 4 * dh + u;
+          const int off = (dt >> 1) * GROUP_BYTES + rb * SEG;
           union {
             i16x4 h[2];
             bf16x8 b;
           } a;
-          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)r1);
-          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(r1 + 128));
+          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tb + voff[0][dt & 1] + off));
+          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tb + voff[1][dt & 1] + off));
           dst[u] = a.b;
         }
       };

@@ -116,7 +116,8 @@ def index_scores_row(q_row: np.ndarray, k: np.ndarray, w_row: np.ndarray,
     H = q_row.shape[0]
     kk = k[key_start:key_end]                                   # [n, Hk, D]
     if kk.shape[1] == H:
-        dots = np.einsum("hd,shd->sh", q_row, kk)
+        # per head: keys of that head [n, D] times its query [D]
+        dots = np.matmul(np.ascontiguousarray(kk.transpose(1, 0, 2)), q_row[:, :, None])[:, :, 0].T
     else:
         dots = kk[:, 0, :] @ q_row.T                            # [n, H]
     return np.maximum(dots, 0.0) @ w_row

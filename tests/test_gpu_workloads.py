@@ -1,0 +1,121 @@
+"""The three large workloads at full size through dsa_group_forward, checked against
+the oracle on sampled query rows: 32K-token decode for 64 sequences over an 8-layer
+F,F,F,S,S,S,F,S group; a 4096-query fp8 chunk at positions 126976..131071; 1M-token
+decode with planted keys.  Indices follow the tie-band rule, attention the bf16
+max-abs-relative bar on rows whose indices equal the oracle's.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from dsa_indexer_top_lightning_amd import binding as b
+from dsa_indexer_top_lightning_amd import synth
+from helpers import ATTN_TOL, check_topk_row, f32_dev, i32_dev, max_abs_rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+KEY_BLOCK = 16384
+
+
+def _upload(w, L):
+    d = {"q": to_dev(L["mla_q"], w.mla_dtype), "kv": to_dev(L["kv"], w.mla_dtype),
+         "out": torch.empty((w.B, w.T, w.Hm, w.Dc), device="cuda", dtype=torch.bfloat16),
+         "lse": torch.empty((w.B, w.T, w.Hm), device="cuda")}
+    if "idx_q" in L:
+        d["index"] = {"q": to_dev(L["idx_q"], w.idx_dtype), "k": to_dev(L["idx_k"], w.idx_dtype),
+                      "w": f32_dev(L["w"])}
+        if w.idx_dtype == "fp8":
+            d["index"]["q_scale"] = f32_dev(L["idx_q_scale"])
+            d["index"]["k_scale"] = f32_dev(L["idx_k_scale"])
+    return d
+
+
+def _oracle_scores(w, keep, bb, t, ks, ke):
+    """Oracle index scores of row (bb, t) over [ks, ke), computed key block by key block."""
+    qs = keep["idx_q_scale"][bb][t] if "idx_q_scale" in keep else None
+    q = O.decode(keep["idx_q"][bb][t], w.idx_dtype, qs)
+    wr = keep["w"][bb][t].astype(np.float64)
+    parts = []
+    for s0 in range(ks, ke, KEY_BLOCK):
+        s1 = min(ke, s0 + KEY_BLOCK)
+        ksc = keep["idx_k_scale"][bb][s0:s1] if "idx_k_scale" in keep else None
+        kblk = O.decode(keep["idx_k"][bb][s0:s1], w.idx_dtype, ksc)
+        parts.append(O.index_scores_row(q, kblk, wr, 0, s1 - s0))
+    return np.concatenate(parts)
+
+
+def _run(w, rows):
+    """Build, upload and run the whole group; keep host copies only for the sampled rows."""
+    types = ["full" if c == "F" else "shared" for c in w.layers]
+    bs = sorted({bb for bb, _ in rows})
+    dev, keep = [], []
+    for l in range(w.n_layers):
+        L = synth.build_layer_inputs(w, l, types[l] == "full")
+        dev.append(_upload(w, L))
+        k = {"mla_q": {bb: L["mla_q"][bb].copy() for bb in bs}, "kv": {bb: L["kv"][bb].copy() for bb in bs}}
+        if types[l] == "full":
+            for name in ("idx_q", "idx_k", "w", "idx_q_scale", "idx_k_scale"):
+                if name in L:
+                    k[name] = {bb: L[name][bb].copy() for bb in bs}
+        keep.append(k)
+        del L
+    ke_h = w.key_end()
+    shape = b.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
+                         key_end=i32_dev(ke_h))
+    ws = torch.empty(b.workspace_bytes(shape, b.OP_GROUP), dtype=torch.uint8, device="cuda")
+    donors = O.donor_map(types)
+    # run the group once per distinct donor so every donor's indices can be checked:
+    # the cache ends with the last full layer's indices, so earlier donors are read
+    # back right after a call that stops at them
+    per_donor = {}
+    for d in sorted(set(donors)):
+        cache = b.IndexCache(w.B, w.T, w.topk)
+        last = max(l for l in range(w.n_layers) if donors[l] == d)
+        b.group_forward(shape, b.BF16, types[:last + 1], dev[:last + 1], w.sm_scale, cache, 1, ws)
+        per_donor[d] = cache.indices.cpu().numpy()
+    torch.cuda.synchronize()
+    return types, donors, dev, keep, per_donor, ke_h
+
+
+def _check(w, rows):
+    types, donors, dev, keep, per_donor, ke_h = _run(w, rows)
+    exact = {d: set() for d in per_donor}
+    ref_idx = {}
+    for d in per_donor:
+        for (bb, t) in rows:
+            ke = int(ke_h[bb, t])
+            sc = _oracle_scores(w, keep[d], bb, t, 0, ke)
+            r, tau = O.topk_row(sc, 0, ke, w.topk)
+            ref_idx[(d, bb, t)] = r
+            if check_topk_row(per_donor[d][bb, t], r, sc, 0, tau):
+                exact[d].add((bb, t))
+    for d in exact:
+        assert len(exact[d]) >= 0.75 * len(rows), f"donor {d}: {len(exact[d])} of {len(rows)} rows identical"
+    for l in range(w.n_layers):
+        got = dev[l]["out"].float().cpu().numpy()
+        use = [r for r in rows if r in exact[donors[l]]]
+        g, o = [], []
+        for (bb, t) in use:
+            idx = ref_idx[(donors[l], bb, t)]
+            sel = idx[idx >= 0]
+            kv_rows = O.decode(keep[l]["kv"][bb][sel], w.mla_dtype)
+            q = O.decode(keep[l]["mla_q"][bb][t], w.mla_dtype)
+            o.append(O.sparse_mla_row(q, kv_rows, np.arange(len(sel)), w.sm_scale, w.Dc)[0])
+            g.append(got[bb, t])
+        assert max_abs_rel(np.stack(g), np.stack(o)) <= ATTN_TOL["bf16"], f"layer {l}"
+
+
+def test_decode32k_b64_bf16_sampled():
+    w = synth.WORKLOADS["decode32k_b64_bf16"]
+    _check(w, [(0, 0), (17, 0), (40, 0), (63, 0)])
+
+
+def test_chunk128k_fp8_sampled():
+    w = synth.WORKLOADS["chunk128k_fp8"]
+    _check(w, [(0, t) for t in (0, 1, 1000, 2047, 3071, 4095)])
+
+
+def test_decode1m_b4_fp8_planted_sampled():
+    w = synth.WORKLOADS["decode1m_b4_fp8"]
+    _check(w, [(3, 0)])
