@@ -143,7 +143,9 @@ def _stream(stream) -> int:
 
 
 def make_shape(B, T, s_cap, *, H=0, D=0, Hk=0, topk=0, Hm=0, Dc=0, Dr=0, key_start=None, key_end=None) -> Shape:
-    return Shape(B, T, s_cap, H, D, Hk, topk, Hm, Dc, Dr, _dev_ptr(key_start), _dev_ptr(key_end))
+    shape = Shape(B, T, s_cap, H, D, Hk, topk, Hm, Dc, Dr, _dev_ptr(key_start), _dev_ptr(key_end))
+    shape._keep = (key_start, key_end)  # the struct holds raw pointers: keep their tensors alive
+    return shape
 
 
 def workspace_bytes(shape: Shape, op: int) -> int:

@@ -16,8 +16,6 @@
 //    tiles, followed by the fused ReLU * weight reduction in fp32 registers.
 //  * indexer_generic: any dtype / D, one thread per key, fp32 FMA.  Used for the
 //    fp32 inputs and for shapes the MFMA kernel does not cover.
-#include <type_traits>
-
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -227,78 +225,83 @@ __global__ __launch_bounds__(256) void indexer_mfma(IndexerParams p) {
 // the 64 x 64 block [64wm, +64) x [64wn, +64) (2 x 2 MFMA tiles of 32 x 32).  For
 // each head the Q_h and K_g tiles, the head weights (and fp8 scales) are gathered
 // straight into LDS with global_load_lds into one of two alternating stages, so the
-// loads of head h+1 run under the contraction of head h.  Tiles are chunk-major:
-// 16-byte chunk c of the 128 rows forms one 2 KiB column, so a fragment read of 32
-// consecutive rows is 512 contiguous bytes (no bank conflicts).  The ReLU * weight
-// epilogue of head h-1 runs while the MFMAs of head h are in flight.
+// loads of head h+1 run under the contraction of head h.  Each wave load moves 8
+// rows x 128 bytes (whole cache lines); a tile is stored as 128-byte row segments
+// whose 16-byte chunks are XOR-permuted by the row, which keeps the fragment reads
+// of 16 consecutive rows bank-conflict free.  The ReLU * weight epilogue of head
+// h-1 runs while the MFMAs of head h are in flight; the per-row weights and scales
+// live in a ring of three LDS stages so that epilogue can still read them.
 constexpr int PQ = 128;  // queries per tile
 constexpr int PK = 128;  // keys per tile
 
 template <int DT>
 struct TileCfg {
   static constexpr int ESZ = (DT == BF16) ? 2 : 1;
-  static constexpr int COLS = HD * ESZ / 16;      // 16-byte columns per tile (16 bf16 / 8 fp8)
-  static constexpr int COL_BYTES = 128 * 16;       // one column of the 128 rows
-  static constexpr int TILE = COLS * COL_BYTES;    // 32 KiB bf16, 16 KiB fp8
-  static constexpr int VEC = 128 * 4;              // one fp32 per row
-  static constexpr int W_OFF = 2 * TILE;           // w
-  static constexpr int QS_OFF = W_OFF + VEC;       // q scale (fp8)
-  static constexpr int KS_OFF = QS_OFF + VEC;      // k scale (fp8)
-  static constexpr int STAGE = 2 * TILE + 3 * VEC;
-  static constexpr int DMA_PER_WAVE = 2 * (2 * COLS) / 4;  // tile loads per wave per stage
+  static constexpr int SEGS = HD * ESZ / 128;      // 128-byte segments per row (2 bf16 / 1 fp8)
+  static constexpr int SEG_BYTES = 128 * 128;      // one segment of the 128 rows
+  static constexpr int TILE = SEGS * SEG_BYTES;    // 32 KiB bf16, 16 KiB fp8
+  static constexpr int STAGE = 2 * TILE;            // Q and K tiles of one head
+  static constexpr int VEC = 128 * 4;               // one fp32 per row
+  static constexpr int W_OFF = 0;                   // w          (in a vector stage)
+  static constexpr int QS_OFF = VEC;                // q scale    (fp8)
+  static constexpr int KS_OFF = 2 * VEC;            // k scale    (fp8)
+  static constexpr int VSTAGE = 3 * VEC;
+  static constexpr int VBASE = 2 * STAGE;           // 3 vector stages follow the 2 tile stages
+  static constexpr int LDS = 2 * STAGE + 3 * VSTAGE;
+  static constexpr int LOADS = 2 * SEGS * 16;       // wave loads per stage: 2 tiles x segments x 16 row octets
+  static constexpr int DMA_PER_WAVE = LOADS / 4;
 };
 
+// 16-byte chunk u (0..7) of row r's segment is stored at chunk u ^ tperm(r)
+__device__ __forceinline__ int tperm(int r) {
+  const int j = (r >> 1) & 7;
+  return ((j & 1) << 2) | (j & 2) | ((j >> 2) & 1);
+}
+
+// Per-workgroup state and steps of indexer_tile (all inlined into the kernel).
 template <int DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void indexer_tile(IndexerParams p) {
+struct TileWork {
   using C = TileCfg<DT>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int32_t rks[PQ], rke[PQ];
+  const IndexerParams& p;
+  unsigned char* smem;
+  int lane, wave, wv, b, t0, H, Hk, T;
+  int64_t s0, s_cap;
+  int wm, wn, lr, lg;
+  const unsigned char* qg;
+  const unsigned char* kg;
+  int64_t qrow, krow;
+  int qr0, qr1;
+  int64_t kr0, kr1;
+  f32x16 acc0[2][2], acc1[2][2];  // accumulators of even / odd heads: [row tile][col tile]
+  f32x16 tot[2][2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int b = blockIdx.z;
-  const int t0 = blockIdx.y * PQ;
-  const int64_t s0 = (int64_t)blockIdx.x * PK;
-  const int H = p.H, Hk = p.Hk, T = p.T;
-  const int64_t s_cap = p.s_cap;
-
-  int live = 0;
-  if (tid < PQ) {
-    const int t = t0 + tid;
-    int64_t ks = 0, ke = 0;
-    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, s_cap, ks, ke);
-    rks[tid] = (int32_t)ks;
-    rke[tid] = (int32_t)ke;
-    live = (t < T) && (ks < s0 + PK) && (ke > s0) && (ks < ke);
+  // wave load j of a stage: tile j / (SEGS*16) (0 = Q, 1 = K), segment, row octet; lane i
+  // fills row 8*octet + i/8, stored chunk i%8 <- logical chunk (i%8) ^ tperm(row); rows
+  // beyond T / s_cap load a valid row (their results are never written)
+  __device__ __forceinline__ const unsigned char* load_src(int j, int h, int g) const {
+    const int tile = j / (C::SEGS * 16), seg = (j / 16) % C::SEGS, oct = j % 16;
+    const int row = 8 * oct + (lane >> 3);
+    const int chunk = (lane & 7) ^ tperm(row);
+    if (tile == 0) {
+      const int64_t t = min(t0 + row, T - 1);
+      return qg + ((int64_t)b * T + t) * qrow + (int64_t)h * HD * C::ESZ + seg * 128 + chunk * 16;
+    }
+    const int64_t sk = min<int64_t>(s0 + row, s_cap - 1);
+    return kg + ((int64_t)b * s_cap + sk) * krow + (int64_t)g * HD * C::ESZ + seg * 128 + chunk * 16;
   }
-  if (!__syncthreads_or(live)) return;
 
-  // rows beyond T / s_cap load a valid row (their results are never written)
-  const int qr0 = min(t0 + lane, T - 1), qr1 = min(t0 + 64 + lane, T - 1);
-  const int64_t kr0 = min<int64_t>(s0 + lane, s_cap - 1), kr1 = min<int64_t>(s0 + 64 + lane, s_cap - 1);
-  const unsigned char* qg = static_cast<const unsigned char*>(p.q);
-  const unsigned char* kg = static_cast<const unsigned char*>(p.k);
-  const int64_t qrow = (int64_t)H * HD * C::ESZ, krow = (int64_t)Hk * HD * C::ESZ;
-  const unsigned char* q0 = qg + ((int64_t)b * T + qr0) * qrow;
-  const unsigned char* q1 = qg + ((int64_t)b * T + qr1) * qrow;
-  const unsigned char* k0 = kg + ((int64_t)b * s_cap + kr0) * krow;
-  const unsigned char* k1 = kg + ((int64_t)b * s_cap + kr1) * krow;
-
-  // gather head h (key head g) into stage st: tile loads are spread over the 4 waves,
-  // load j: tile j / (2*COLS) (0 = Q, 1 = K), column (j % (2*COLS)) / 2, row half j % 2
-  auto issue = [&](int h, int st, bool with_k) {
+  // gather head h into tile stage st (K only if with_k) and its vectors into vector stage h % 3
+  __device__ __forceinline__ void issue(int h, int st, bool with_k) const {
     unsigned char* base = smem + st * C::STAGE;
+    unsigned char* vbase = smem + C::VBASE + (h % 3) * C::VSTAGE;
     const int g = (Hk == H) ? h : 0;
 #pragma unroll
     for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
       const int j = wv * C::DMA_PER_WAVE + i;
-      const int tile = j / (2 * C::COLS), col = (j % (2 * C::COLS)) >> 1, half = j & 1;
+      const int tile = j / (C::SEGS * 16), seg = (j / 16) % C::SEGS, oct = j % 16;
       if (tile == 1 && !with_k) continue;
-      const unsigned char* src = tile == 0 ? (half ? q1 : q0) + (int64_t)h * HD * C::ESZ
-                                           : (half ? k1 : k0) + (int64_t)g * HD * C::ESZ;
-      unsigned char* dst = base + tile * C::TILE + col * C::COL_BYTES + half * 1024;
-      __builtin_amdgcn_global_load_lds(src + col * 16, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      unsigned char* dst = base + tile * C::TILE + seg * C::SEG_BYTES + oct * 1024;
+      __builtin_amdgcn_global_load_lds(load_src(j, h, g), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
     }
     // per-row vectors: wave 0 w, wave 1 q scale, wave 2 k scale (fp8)
     if (wv == 0 || (DT == FP8 && wv < 3)) {
@@ -316,150 +319,177 @@ void indexer_tile(IndexerParams p) {
       }
       const int64_t stride = (wv == 2) ? Hk : H;
       const int64_t r0 = (wv == 2) ? kr0 : qr0, r1 = (wv == 2) ? kr1 : qr1;
-      __builtin_amdgcn_global_load_lds(vsrc + r0 * stride, (__attribute__((address_space(3))) void*)(base + off), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc + r1 * stride, (__attribute__((address_space(3))) void*)(base + off + 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc + r0 * stride, (__attribute__((address_space(3))) void*)(vbase + off), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc + r1 * stride, (__attribute__((address_space(3))) void*)(vbase + off + 256), 4, 0, 0);
     }
-  };
+  }
 
-  const int wm = wave & 1, wn = wave >> 1;
-  const int lr = lane & 31, lg = lane >> 5;
-  f32x16 acc[2][2][2];  // [parity][row tile][col tile]
-  f32x16 tot[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
-  float wrow[2][2][16];   // [parity][row tile][value]: weight (x q scale) of this lane's result rows
-  float kcol[2][2];       // [parity][col tile]: key scale of this lane's result column
+  // 16-byte fragment of row r, logical chunk c: segment c / 8, stored chunk (c % 8) ^ tperm(r)
+  __device__ __forceinline__ const unsigned char* frag(const unsigned char* tile, int r, int c) const {
+    return tile + (c >> 3) * C::SEG_BYTES + r * 128 + 16 * ((c & 7) ^ tperm(r));
+  }
 
-  auto epilogue = [&](auto par_c) {
-    constexpr int par = decltype(par_c)::value;
+  // ReLU * weight of head hh from accumulator set `acc`, weights / scales from its vector stage
+  __device__ __forceinline__ void epilogue(const f32x16 (&acc)[2][2], int hh) {
+    const unsigned char* vb = smem + C::VBASE + (hh % 3) * C::VSTAGE;
+    const float* wl = reinterpret_cast<const float*>(vb + C::W_OFF);
+    const float* ql = reinterpret_cast<const float*>(vb + C::QS_OFF);
+    const float* kl = reinterpret_cast<const float*>(vb + C::KS_OFF);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = acc[par][i][j][r];
-          if constexpr (DT == FP8) v *= kcol[par][j];
-          tot[i][j][r] = fmaf(wrow[par][i][r], fmaxf(v, 0.f), tot[i][j][r]);
-        }
-  };
-
-  // one head: `st` is the stage / register parity, a compile-time constant
-  auto head = [&](int h, auto st_c) {
-    constexpr int st = decltype(st_c)::value;
-    wait_vmem();
-    __syncthreads();  // stage st holds head h; stage st^1 is free
-    const unsigned char* base = smem + st * C::STAGE;
-    const unsigned char* kbase = (Hk == H) ? base : smem;  // a shared key head stays in stage 0
-    // this head's weights (and scales) into registers before the next gather reuses the stage
-    {
-      const float* wl = reinterpret_cast<const float*>(base + C::W_OFF);
-      const float* ql = reinterpret_cast<const float*>(base + C::QS_OFF);
-      const float* kl = reinterpret_cast<const float*>(kbase + C::KS_OFF);
+    for (int j = 0; j < 2; ++j) {
+      float kc = 1.f;
+      if constexpr (DT == FP8) kc = kl[64 * wn + 32 * j + lr];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          float v = wl[row];
-          if constexpr (DT == FP8) v *= ql[row];
-          wrow[st][i][r] = v;
+          float wv_ = wl[row];
+          if constexpr (DT == FP8) wv_ *= ql[row];
+          float v = acc[i][j][r];
+          if constexpr (DT == FP8) v *= kc;
+          tot[i][j][r] = fmaf(wv_, fmaxf(v, 0.f), tot[i][j][r]);
         }
-      if constexpr (DT == FP8) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) kcol[st][j] = kl[64 * wn + 32 * j + lr];
-      }
     }
-    if (h + 1 < H) issue(h + 1, st ^ 1, Hk == H);
+  }
 
-    // contraction of head h: 2 x 2 tiles of 32 x 32 over D = 128
+  // contraction of head h from tile stage st into `acc`: 2 x 2 tiles of 32 x 32 over D = 128
+  __device__ __forceinline__ void contract(f32x16 (&acc)[2][2], int st) const {
+    const unsigned char* qt = smem + st * C::STAGE;
+    const unsigned char* kt = ((Hk == H) ? qt : smem) + C::TILE;  // a shared key head stays in stage 0
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[st][i][j][r] = 0.f;
-    const unsigned char* qa = base + (64 * wm + lr) * 16;
-    const unsigned char* kb = kbase + C::TILE + (64 * wn + lr) * 16;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     if constexpr (DT == BF16) {
 #pragma unroll
       for (int ks = 0; ks < HD / 16; ++ks) {
         const int col = 2 * ks + lg;  // elements 16ks + 8lg .. +7
         bf16x8 a[2], bb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(qa + col * C::COL_BYTES + 32 * i * 16);
+        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(frag(qt, 64 * wm + 32 * i + lr, col));
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(kb + col * C::COL_BYTES + 32 * j * 16);
+        for (int j = 0; j < 2; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(frag(kt, 64 * wn + 32 * j + lr, col));
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[st][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[st][i][j], 0, 0, 0);
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < HD / 64; ++ks) {
-        const int col = 4 * ks + 2 * lg;  // bytes 64ks + 32lg .. +31 = columns col, col+1
+        const int col = 4 * ks + 2 * lg;  // bytes 64ks + 32lg .. +31 = chunks col, col+1
         i32x8 a[2], bb[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(qa + col * C::COL_BYTES + 32 * i * 16);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(qa + (col + 1) * C::COL_BYTES + 32 * i * 16);
+          const int r = 64 * wm + 32 * i + lr;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(frag(qt, r, col));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(frag(qt, r, col + 1));
           a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(kb + col * C::COL_BYTES + 32 * j * 16);
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(kb + (col + 1) * C::COL_BYTES + 32 * j * 16);
+          const int r = 64 * wn + 32 * j + lr;
+          const i32x4 lo = *reinterpret_cast<const i32x4*>(frag(kt, r, col));
+          const i32x4 hi = *reinterpret_cast<const i32x4*>(frag(kt, r, col + 1));
           bb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[st][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[st][i][j], 0, 0, 0, 127, 0, 127);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
       }
     }
-    if (h > 0) epilogue(std::integral_constant<int, st ^ 1>{});
-  };
+  }
 
-  issue(0, 0, true);
-  int h = 0;
-  for (; h + 1 < H; h += 2) {
-    head(h, std::integral_constant<int, 0>{});
-    head(h + 1, std::integral_constant<int, 1>{});
+  // head h lives in tile stage h & 1; its MFMAs go into `cur` while the epilogue of head
+  // h-1 (accumulators `prev`) runs
+  __device__ __forceinline__ void head(int h, int st, f32x16 (&cur)[2][2], const f32x16 (&prev)[2][2]) {
+    wait_vmem();
+    __syncthreads();  // stage st holds head h; the other stage is free
+    if (h + 1 < H) issue(h + 1, st ^ 1, Hk == H);
+    contract(cur, st);
+    if (h > 0) epilogue(prev, h - 1);
   }
-  if (h < H) {
-    head(h, std::integral_constant<int, 0>{});
-    epilogue(std::integral_constant<int, 0>{});
-  } else {
-    epilogue(std::integral_constant<int, 1>{});
+
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
+    issue(0, 0, true);
+    int h = 0;
+    for (; h + 1 < H; h += 2) {
+      head(h, 0, acc0, acc1);
+      head(h + 1, 1, acc1, acc0);
+    }
+    if (h < H) {
+      head(h, 0, acc0, acc1);
+      epilogue(acc0, h);
+    } else {
+      epilogue(acc1, H - 1);
+    }
   }
+};
+
+template <int DT>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void indexer_tile(IndexerParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int32_t rks[PQ], rke[PQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * PQ;
+  const int64_t s0 = (int64_t)blockIdx.x * PK;
+  const int T = p.T;
+  const int64_t s_cap = p.s_cap;
+
+  int live = 0;
+  if (tid < PQ) {
+    const int t = t0 + tid;
+    int64_t ks = 0, ke = 0;
+    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, s_cap, ks, ke);
+    rks[tid] = (int32_t)ks;
+    rke[tid] = (int32_t)ke;
+    live = (t < T) && (ks < s0 + PK) && (ke > s0) && (ks < ke);
+  }
+  if (!__syncthreads_or(live)) return;
+
+  TileWork<DT> w{p, smem, lane, wave, __builtin_amdgcn_readfirstlane(wave), b, t0, p.H, p.Hk, T, s0, s_cap,
+                 wave & 1, wave >> 1, lane & 31, lane >> 5,
+                 static_cast<const unsigned char*>(p.q), static_cast<const unsigned char*>(p.k),
+                 (int64_t)p.H * HD * TileCfg<DT>::ESZ, (int64_t)p.Hk * HD * TileCfg<DT>::ESZ,
+                 min(t0 + lane, T - 1), min(t0 + 64 + lane, T - 1),
+                 min<int64_t>(s0 + lane, s_cap - 1), min<int64_t>(s0 + 64 + lane, s_cap - 1)};
+  w.run();
 
   // write the candidate cells: result row m = 8(r/4) + 4lg + r%4 of tile i, column lr of tile j
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int64_t s = s0 + 64 * wn + 32 * j + lr;
+      const int64_t s = s0 + 64 * w.wn + 32 * j + w.lr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+        const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
         const int t = t0 + m;
-        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = tot[i][j][r];
+        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = w.tot[i][j][r];
       }
     }
 }
 
-template <auto K>
-hipError_t ensure_lds(size_t bytes) {
-  static std::atomic<size_t> high{0};
-  return allow_dynamic_lds(reinterpret_cast<const void*>(K), bytes, high);
-}
+// one allowance record per launch site (each site launches one kernel)
+#define DSA_ALLOW_LDS(kernel, bytes)                                                   \
+  [&]() -> hipError_t {                                                                \
+    static std::atomic<size_t> high{0};                                                \
+    return allow_dynamic_lds(reinterpret_cast<const void*>(&(kernel)), (bytes), high); \
+  }()
 
 }  // namespace
 
@@ -467,14 +497,14 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
   if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;
   const bool mfma = (dt == BF16 || dt == FP8) && p.D == HD;
   if (mfma && p.T >= 32) {
-    const size_t lds = 2 * (size_t)(dt == BF16 ? TileCfg<BF16>::STAGE : TileCfg<FP8>::STAGE);
+    const size_t lds = (size_t)(dt == BF16 ? TileCfg<BF16>::LDS : TileCfg<FP8>::LDS);
     dim3 grid((unsigned)((p.s_cap + PK - 1) / PK), (unsigned)((p.T + PQ - 1) / PQ), (unsigned)p.B);
     hipError_t e;
     if (dt == BF16) {
-      if ((e = ensure_lds<indexer_tile<BF16>>(lds)) != hipSuccess) return e;
+      if ((e = DSA_ALLOW_LDS(indexer_tile<BF16>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_tile<BF16>, grid, dim3(256), lds, st, p);
     } else {
-      if ((e = ensure_lds<indexer_tile<FP8>>(lds)) != hipSuccess) return e;
+      if ((e = DSA_ALLOW_LDS(indexer_tile<FP8>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(256), lds, st, p);
     }
   } else if (mfma) {
@@ -483,10 +513,10 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
     dim3 grid((unsigned)((p.s_cap + TN - 1) / TN), (unsigned)((p.T + TM - 1) / TM), (unsigned)p.B);
     hipError_t e;
     if (dt == BF16) {
-      if ((e = ensure_lds<indexer_mfma<BF16>>(lds)) != hipSuccess) return e;
+      if ((e = DSA_ALLOW_LDS(indexer_mfma<BF16>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_mfma<BF16>, grid, dim3(256), lds, st, p);
     } else {
-      if ((e = ensure_lds<indexer_mfma<FP8>>(lds)) != hipSuccess) return e;
+      if ((e = DSA_ALLOW_LDS(indexer_mfma<FP8>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_mfma<FP8>, grid, dim3(256), lds, st, p);
     }
   } else {
@@ -495,15 +525,15 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
     hipError_t e;
     switch (dt) {
       case F32:
-        if ((e = ensure_lds<indexer_generic<F32>>(lds)) != hipSuccess) return e;
+        if ((e = DSA_ALLOW_LDS(indexer_generic<F32>, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(indexer_generic<F32>, grid, dim3(256), lds, st, p);
         break;
       case BF16:
-        if ((e = ensure_lds<indexer_generic<BF16>>(lds)) != hipSuccess) return e;
+        if ((e = DSA_ALLOW_LDS(indexer_generic<BF16>, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(indexer_generic<BF16>, grid, dim3(256), lds, st, p);
         break;
       default:
-        if ((e = ensure_lds<indexer_generic<FP8>>(lds)) != hipSuccess) return e;
+        if ((e = DSA_ALLOW_LDS(indexer_generic<FP8>, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(indexer_generic<FP8>, grid, dim3(256), lds, st, p);
         break;
     }

@@ -4,6 +4,9 @@ F,F,F,S,S,S,F,S group; a 4096-query fp8 chunk at positions 126976..131071; 1M-to
 decode with planted keys.  Indices follow the tie-band rule, attention the bf16
 max-abs-relative bar on rows whose indices equal the oracle's.
 """
+import sys
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +19,10 @@ from helpers import ATTN_TOL, check_topk_row, f32_dev, i32_dev, max_abs_rel, to_
 pytestmark = pytest.mark.gpu
 
 KEY_BLOCK = 16384
+
+
+def _say(msg):
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 def _upload(w, L):
@@ -60,6 +67,7 @@ def _run(w, rows):
                     k[name] = {bb: L[name][bb].copy() for bb in bs}
         keep.append(k)
         del L
+        _say(f"{w.name}: layer {l} generated and uploaded")
     ke_h = w.key_end()
     shape = b.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
                          key_end=i32_dev(ke_h))
@@ -74,6 +82,7 @@ def _run(w, rows):
         last = max(l for l in range(w.n_layers) if donors[l] == d)
         b.group_forward(shape, b.BF16, types[:last + 1], dev[:last + 1], w.sm_scale, cache, 1, ws)
         per_donor[d] = cache.indices.cpu().numpy()
+        _say(f"{w.name}: group through layer {last} done (donor {d})")
     torch.cuda.synchronize()
     return types, donors, dev, keep, per_donor, ke_h
 
@@ -90,6 +99,7 @@ def _check(w, rows):
             ref_idx[(d, bb, t)] = r
             if check_topk_row(per_donor[d][bb, t], r, sc, 0, tau):
                 exact[d].add((bb, t))
+            _say(f"{w.name}: donor {d} row ({bb},{t}) indices checked")
     for d in exact:
         assert len(exact[d]) >= 0.75 * len(rows), f"donor {d}: {len(exact[d])} of {len(rows)} rows identical"
     for l in range(w.n_layers):
