@@ -31,9 +31,11 @@ METRIC = "query tokens/s per 4-layer F/S group (indexer+top-k+sparse MLA); MFMA%
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
-# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of the dominant kernel (KiB per dispatch), measured on the
-# same command and scaled by the copy-kernel calibration; None until taken for the current kernel.
-MEASURED_TRAFFIC_BYTES = None
+# HBM bytes per launch of the roofline kernel from rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE on
+# `bench.py --steps 2 --warmup 1 --no-cpu-baseline`, each scaled by the same counter's reading
+# on a plain copy of known size (`bench.py --copy-calibration`); keyed (workload, kernel) and
+# removed whenever that kernel changes (then reported as null).
+MEASURED_TRAFFIC_BYTES = {}
 
 
 def parse():
@@ -204,16 +206,40 @@ def main():
         "sparse_mla": {"ms": t_attn, "tflops": attn_flops / (t_attn * 1e-3) / 1e12,
                        "gbs": attn_bytes / (t_attn * 1e-3) / 1e9, "peak_tflops": PEAK_BF16_TFLOPS},
     }
+    # roofline of the kernel that takes the largest share of the step; prefill kernels are
+    # dense matrix-core work (bound: MFMA peak of their input type), decode kernels and
+    # top-k stream memory (bound: HBM)
     prefill = w.T > 1
-    if prefill:
+    nf = max(len(full_layers), 1)
+    cands = {
+        "indexer": (t_idx or 0.0) * len(full_layers),
+        "topk": (t_topk or 0.0) * len(full_layers),
+        "sparse_mla": t_attn * n,
+    }
+    dom = max(cands, key=cands.get)
+    if dom == "indexer" and prefill:
+        ach = idx_flops / (t_idx * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": idx_peak, "unit": "TFLOP/s",
+                "kernel": "indexer_tile", "algorithmic_per_launch": idx_flops}
+    elif dom == "indexer":
+        byt = stats.indexer_bytes / nf
+        ach = byt / (t_idx * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "indexer_stream", "algorithmic_per_launch": byt}
+    elif dom == "topk":
+        ach = topk_bytes / (t_topk * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "topk_rows", "algorithmic_per_launch": topk_bytes}
+    elif prefill:
         ach = attn_flops / (t_attn * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": MEASURED_TRAFFIC_BYTES, "kernel": "mla_mfma",
-                "algorithmic_per_launch": attn_flops}
+                "kernel": "mla_mfma", "algorithmic_per_launch": attn_flops}
     else:
         ach = attn_bytes / (t_attn * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                "traffic": MEASURED_TRAFFIC_BYTES, "kernel": "mla_mfma", "algorithmic_per_launch": attn_bytes}
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "mla_mfma", "algorithmic_per_launch": attn_bytes}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get((w.name, roof["kernel"])) if MEASURED_TRAFFIC_BYTES else None
 
     tokens = w.B * w.T
     value = tokens / (elapsed / steps) * n / 4.0

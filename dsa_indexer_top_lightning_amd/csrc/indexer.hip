@@ -25,6 +25,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -484,6 +485,100 @@ void indexer_tile(IndexerParams p) {
     }
 }
 
+// ----------------------------------------------------------------- decode streaming kernel
+// Few queries per batch item (decode): the work is one pass over the item's index
+// keys, so this kernel streams them from HBM with whole-row 16-byte loads and does
+// the products on the vector ALUs (the matrix cores would idle on one query row).
+// A key row holds all Hk heads (Hk*D contiguous values); lane l owns head l / LPH,
+// elements (l % LPH) * D/LPH .. +D/LPH of it (LPH = 64 / H lanes per head), the
+// query slice stays in registers, per-head dots are completed by lane shuffles,
+// then ReLU * weight and a shuffle reduction over the heads give the score.
+// grid: x = block of 64 keys, y = query row.  256 threads: wave w takes keys w, w+4, ...
+template <int DT, int LPH>
+__global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
+  constexpr int H = 64 / LPH;
+  constexpr int EPL = HD / LPH;                 // elements per lane
+  constexpr int ESZ = (DT == BF16) ? 2 : 1;
+  constexpr int BYTES = EPL * ESZ;              // bytes per lane per key
+  constexpr int LOADS = BYTES / 16;
+  static_assert(BYTES % 16 == 0, "lane slice must be whole 16-byte loads");
+  constexpr int KPB = 64;                       // keys per workgroup
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.y;
+  int64_t ks, ke;
+  clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
+  const int64_t sblk = (int64_t)blockIdx.x * KPB;
+  if (sblk >= ke || sblk + KPB <= ks) return;
+  const int64_t b = row / p.T;
+  const int Hk = p.Hk;
+  const int h = lane / LPH, part = lane % LPH;
+
+  // query slice (decoded, times the fp8 query scale) and head weight
+  float q[EPL];
+  {
+    const int64_t qo = (row * H + h) * HD + part * EPL;
+    if constexpr (DT == BF16) {
+      const uint16_t* qb = static_cast<const uint16_t*>(p.q) + qo;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = __uint_as_float((uint32_t)qb[e] << 16);
+    } else {
+      const uint8_t* qb = static_cast<const uint8_t*>(p.q) + qo;
+      const float qs = p.q_scale[row * H + h];
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2) {
+        const f32x2 v = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)qb[e] | ((uint32_t)qb[e + 1] << 8), false);
+        q[e] = v[0] * qs;
+        q[e + 1] = v[1] * qs;
+      }
+    }
+  }
+  const float wh = p.w[row * H + h];
+  const int g = (Hk == H) ? h : 0;
+  const unsigned char* kg = static_cast<const unsigned char*>(p.k);
+  const int64_t krow = (int64_t)Hk * HD * ESZ;
+
+  for (int j = wave; j < KPB; j += 4) {
+    const int64_t s = sblk + j;
+    if (s < ks || s >= ke) continue;  // the whole wave takes the same branch
+    const unsigned char* src = kg + (b * p.s_cap + s) * krow + (int64_t)g * HD * ESZ + part * BYTES;
+    i32x4 raw[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) raw[u] = *reinterpret_cast<const i32x4*>(src + 16 * u);
+    float dot = 0.f;
+    if constexpr (DT == BF16) {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kk = (uint32_t)raw[u][e];
+          dot = fmaf(q[8 * u + 2 * e], __uint_as_float(kk << 16), dot);
+          dot = fmaf(q[8 * u + 2 * e + 1], __uint_as_float(kk & 0xffff0000u), dot);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kk = (uint32_t)raw[u][e];
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(kk, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(kk, true);
+          dot = fmaf(q[16 * u + 4 * e], lo[0], dot);
+          dot = fmaf(q[16 * u + 4 * e + 1], lo[1], dot);
+          dot = fmaf(q[16 * u + 4 * e + 2], hi[0], dot);
+          dot = fmaf(q[16 * u + 4 * e + 3], hi[1], dot);
+        }
+      dot *= p.k_scale[(b * p.s_cap + s) * Hk + g];
+    }
+#pragma unroll
+    for (int off = 1; off < LPH; off <<= 1) dot += __shfl_xor(dot, off, 64);
+    float v = (part == 0) ? wh * fmaxf(dot, 0.f) : 0.f;
+#pragma unroll
+    for (int off = LPH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) p.scores[row * p.ld + s] = v;
+  }
+}
+
 // one allowance record per launch site (each site launches one kernel)
 #define DSA_ALLOW_LDS(kernel, bytes)                                                   \
   [&]() -> hipError_t {                                                                \
@@ -506,6 +601,18 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
     } else {
       if ((e = DSA_ALLOW_LDS(indexer_tile<FP8>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(256), lds, st, p);
+    }
+  } else if (mfma && p.T <= 4 && (int64_t)p.B * p.T <= 65535 && (p.H == 16 || p.H == 32 || p.H == 64)) {
+    // decode: stream the keys once per query row
+    dim3 grid((unsigned)((p.s_cap + 63) / 64), (unsigned)((int64_t)p.B * p.T));
+    if (dt == BF16) {
+      if (p.H == 16) hipLaunchKernelGGL((indexer_stream<BF16, 4>), grid, dim3(256), 0, st, p);
+      else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<BF16, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((indexer_stream<BF16, 1>), grid, dim3(256), 0, st, p);
+    } else {
+      if (p.H == 16) hipLaunchKernelGGL((indexer_stream<FP8, 4>), grid, dim3(256), 0, st, p);
+      else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<FP8, 2>), grid, dim3(256), 0, st, p);
+      else hipLaunchKernelGGL((indexer_stream<FP8, 1>), grid, dim3(256), 0, st, p);
     }
   } else if (mfma) {
     const int rs = (dt == BF16) ? MfmaCfg<BF16>::RS : MfmaCfg<FP8>::RS;
