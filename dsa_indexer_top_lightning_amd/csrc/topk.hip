@@ -17,6 +17,15 @@
 //  3. an ordered pass that keeps every key > tau and the first (in position
 //     order) `rem` keys == tau, writing each kept position to its slot found by
 //     wavefront ballots + popcount prefix sums and a cross-wave prefix in LDS.
+//
+// Few long rows (decode over a long prefix) would leave most compute units idle
+// with one workgroup per row, so there each row is cut into chunks of 8192 keys,
+// one 256-thread workgroup per chunk, and the same radix select runs as a chain
+// of launches on the stream: the three digit histograms are summed per row in a
+// workspace with device-scope atomics, every later launch re-derives the digit
+// prefix by scanning the finished histograms, a counting launch stores each
+// chunk's number of keys > tau and == tau, and the emitting launch writes each
+// chunk's kept positions after those of the chunks before it.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -144,13 +153,270 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
   }
 }
 
+
+// ----------------------------------------------------------------- split rows
+constexpr int SP_THREADS = 256;
+constexpr int SP_PER = 32;                        // keys per thread
+constexpr int SP_CHUNK = SP_THREADS * SP_PER;     // keys per workgroup
+constexpr int SP_BINS = 2048;
+constexpr int64_t SP_MIN_KEYS = 2 * SP_CHUNK;     // shorter rows stay on one workgroup
+constexpr int64_t SP_MAX_ROWS = 512;              // more rows fill the chip by themselves
+
+__host__ __device__ constexpr int sp_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
+__host__ __device__ constexpr uint32_t sp_mask(int pass) { return pass < 2 ? 2047u : 1023u; }
+
+int64_t split_chunks(int64_t rows, int64_t s_cap) {
+  if (rows >= SP_MAX_ROWS || s_cap <= SP_MIN_KEYS) return 0;
+  return (s_cap + SP_CHUNK - 1) / SP_CHUNK;
+}
+
+struct SplitArgs {
+  uint32_t* hist;  // [rows][3][SP_BINS]
+  uint32_t* cnt;   // [rows][nchunk][2]: keys > tau, keys == tau
+  int64_t nchunk;
+};
+
+// Finds, in the summed histogram gh of one digit, the digit value d that holds the
+// rem-th largest candidate and the rank of that candidate among the keys with digit
+// d.  Thread t owns bins 8t..8t+7; suffix sums over threads locate the owner.
+__device__ void sp_scan(const uint32_t* gh, uint32_t& rem, uint32_t& digit, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t h[8], c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = gh[8 * tid + i];
+    c += h[i];
+  }
+  uint32_t x = c;  // suffix sum inside the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += v;
+  }
+  if (lane == 0) sh[wave] = x;
+  __syncthreads();
+  for (int w = wave + 1; w < SP_THREADS / 64; ++w) x += sh[w];
+  // x = candidates with digit >= 8*tid; exactly one thread has x >= rem > x - c
+  if (x >= rem && x - c < rem) {
+    uint32_t above = x - c;
+    int i = 7;
+    for (; i > 0; --i) {
+      if (above + h[i] >= rem) break;
+      above += h[i];
+    }
+    sh[4] = (uint32_t)(8 * tid + i);
+    sh[5] = rem - above;
+  }
+  __syncthreads();
+  digit = sh[4];
+  rem = sh[5];
+  __syncthreads();
+}
+
+// prefix / mask of the digits fixed by the first `passes` finished histograms
+__device__ void sp_prefix(const uint32_t* gh, int passes, uint32_t K, uint32_t& prefix, uint32_t& pmask,
+                          uint32_t& rem, uint32_t* sh) {
+  prefix = 0;
+  pmask = 0;
+  rem = K;
+  for (int q = 0; q < passes; ++q) {
+    uint32_t d;
+    sp_scan(gh + q * SP_BINS, rem, d, sh);
+    prefix |= d << sp_shift(q);
+    pmask |= sp_mask(q) << sp_shift(q);
+  }
+}
+
+struct SpRow {
+  int64_t ks, ke, lo, hi;
+  bool skip;
+};
+
+__device__ __forceinline__ SpRow sp_row(const TopkParams& p) {
+  SpRow r;
+  clamp_range(p.key_start, p.key_end, blockIdx.y, p.s_cap, r.ks, r.ke);
+  r.lo = r.ks + (int64_t)blockIdx.x * SP_CHUNK;
+  r.hi = min(r.ke, r.lo + SP_CHUNK);
+  r.skip = (r.ke - r.ks <= p.topk) || r.lo >= r.ke;
+  return r;
+}
+
+__global__ __launch_bounds__(256) void topk_split_clear(uint32_t* hist, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    hist[i] = 0u;
+}
+
+template <int PASS>
+__global__ __launch_bounds__(SP_THREADS) void topk_split_hist(TopkParams p, SplitArgs a) {
+  __shared__ uint32_t lh[SP_BINS];
+  __shared__ uint32_t sh[8];
+  const SpRow r = sp_row(p);
+  if (r.skip) return;
+  const int64_t row = blockIdx.y;
+  uint32_t* gh = a.hist + row * 3 * SP_BINS;
+  uint32_t prefix, pmask, rem;
+  sp_prefix(gh, PASS, (uint32_t)p.topk, prefix, pmask, rem, sh);
+  for (int i = threadIdx.x; i < SP_BINS; i += SP_THREADS) lh[i] = 0u;
+  __syncthreads();
+  const float* src = p.scores + row * p.ld;
+  constexpr int shift = sp_shift(PASS);
+  constexpr uint32_t dmask = sp_mask(PASS);
+  for (int64_t i = r.lo + threadIdx.x; i < r.hi; i += SP_THREADS) {
+    const uint32_t key = order_key(src[i]);
+    if ((key & pmask) == prefix) atomicAdd(&lh[(key >> shift) & dmask], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < SP_BINS; i += SP_THREADS) {
+    const uint32_t v = lh[i];
+    if (v) atomicAdd(&gh[PASS * SP_BINS + i], v);
+  }
+}
+
+__device__ __forceinline__ void sp_block_sum2(uint32_t& a, uint32_t& b, uint32_t* sh) {
+  // inclusive block sums of (a, b); returns totals in a, b for every thread
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, 64);
+    b += __shfl_xor(b, off, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sh[wave] = a;
+    sh[4 + wave] = b;
+  }
+  __syncthreads();
+  a = sh[0] + sh[1] + sh[2] + sh[3];
+  b = sh[4] + sh[5] + sh[6] + sh[7];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_count(TopkParams p, SplitArgs a) {
+  __shared__ uint32_t sh[8];
+  const SpRow r = sp_row(p);
+  if (r.skip) return;
+  const int64_t row = blockIdx.y;
+  uint32_t tau, pmask, rem;
+  sp_prefix(a.hist + row * 3 * SP_BINS, 3, (uint32_t)p.topk, tau, pmask, rem, sh);
+  const float* src = p.scores + row * p.ld;
+  uint32_t gt = 0, eq = 0;
+  for (int64_t i = r.lo + threadIdx.x; i < r.hi; i += SP_THREADS) {
+    const uint32_t key = order_key(src[i]);
+    gt += key > tau;
+    eq += key == tau;
+  }
+  sp_block_sum2(gt, eq, sh);
+  if (threadIdx.x == 0) {
+    uint32_t* c = a.cnt + (row * a.nchunk + blockIdx.x) * 2;
+    c[0] = gt;
+    c[1] = eq;
+  }
+}
+
+__global__ __launch_bounds__(SP_THREADS) void topk_split_emit(TopkParams p, SplitArgs a) {
+  __shared__ uint32_t keys[SP_CHUNK + SP_CHUNK / SP_PER];  // one pad word per thread segment
+  __shared__ uint32_t sh[8];
+  __shared__ uint32_t scan_g[SP_THREADS / 64], scan_e[SP_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.y;
+  const int K = p.topk;
+  int32_t* out = p.out + row * (int64_t)K;
+  SpRow r = sp_row(p);
+  if (r.ke - r.ks <= K) {
+    if (blockIdx.x == 0)
+      for (int i = tid; i < K; i += SP_THREADS) out[i] = (i < r.ke - r.ks) ? (int32_t)(r.ks + i) : -1;
+    return;
+  }
+  if (r.skip) return;
+  uint32_t tau, pmask, rem;
+  sp_prefix(a.hist + row * 3 * SP_BINS, 3, (uint32_t)K, tau, pmask, rem, sh);
+
+  // keys > tau and == tau in the chunks before this one
+  const uint32_t* c = a.cnt + row * a.nchunk * 2;
+  uint32_t gtb = 0, eqb = 0;
+  for (int64_t j = tid; j < (int64_t)blockIdx.x; j += SP_THREADS) {
+    gtb += c[2 * j];
+    eqb += c[2 * j + 1];
+  }
+  sp_block_sum2(gtb, eqb, sh);
+  const uint32_t my_gt = c[2 * blockIdx.x], my_eq = c[2 * blockIdx.x + 1];
+  if (my_gt == 0 && (my_eq == 0 || eqb >= rem)) return;  // nothing kept here (uniform)
+
+  // stage the chunk's keys; thread t then walks positions lo + 32t .. lo + 32t + 31
+  const float* src = p.scores + row * p.ld;
+  const int len = (int)(r.hi - r.lo);
+  for (int i = tid; i < len; i += SP_THREADS) keys[i + i / SP_PER] = order_key(src[r.lo + i]);
+  __syncthreads();
+  const int i0 = tid * SP_PER, i1 = min(len, i0 + SP_PER);
+  uint32_t g = 0, e = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = keys[i + i / SP_PER];
+    g += key > tau;
+    e += key == tau;
+  }
+  // exclusive prefix over threads
+  uint32_t gi = g, ei = e;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t vg = __shfl_up(gi, off, 64), ve = __shfl_up(ei, off, 64);
+    if (lane >= off) {
+      gi += vg;
+      ei += ve;
+    }
+  }
+  if (lane == 63) {
+    scan_g[wave] = gi;
+    scan_e[wave] = ei;
+  }
+  __syncthreads();
+  uint32_t gpos = gtb + gi - g, epos = eqb + ei - e;
+  for (int w = 0; w < wave; ++w) {
+    gpos += scan_g[w];
+    epos += scan_e[w];
+  }
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = keys[i + i / SP_PER];
+    if (key > tau) {
+      const uint32_t slot = gpos + min(epos, rem);
+      if (slot < (uint32_t)K) out[slot] = (int32_t)(r.lo + i);
+      ++gpos;
+    } else if (key == tau) {
+      if (epos < rem && gpos + epos < (uint32_t)K) out[gpos + epos] = (int32_t)(r.lo + i);
+      ++epos;
+    }
+  }
+}
+
+size_t split_ws_bytes(int64_t rows, int64_t nchunk) {
+  return (size_t)rows * 3 * SP_BINS * 4 + (size_t)rows * nchunk * 2 * 4;
+}
+
 }  // namespace
 
-size_t topk_workspace_bytes(int, int, int, int64_t) { return 0; }
+size_t topk_workspace_bytes(int B, int T, int, int64_t s_cap) {
+  const int64_t rows = (int64_t)B * T;
+  const int64_t nch = split_chunks(rows, s_cap);
+  return nch ? split_ws_bytes(rows, nch) : 0;
+}
 
-hipError_t launch_topk(const TopkParams& p, void*, size_t, hipStream_t st, int* n_launches) {
+hipError_t launch_topk(const TopkParams& p, void* ws, size_t ws_bytes, hipStream_t st, int* n_launches) {
   const int64_t rows = (int64_t)p.B * p.T;
   if (rows == 0) return hipSuccess;
+  const int64_t nch = split_chunks(rows, p.s_cap);
+  if (nch) {
+    if (!ws || ws_bytes < split_ws_bytes(rows, nch)) return hipErrorInvalidValue;
+    SplitArgs a{static_cast<uint32_t*>(ws), static_cast<uint32_t*>(ws) + rows * 3 * SP_BINS, nch};
+    const int64_t words = rows * 3 * SP_BINS;
+    hipLaunchKernelGGL(topk_split_clear, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 1024)), dim3(256), 0, st,
+                       a.hist, words);
+    const dim3 grid((unsigned)nch, (unsigned)rows);
+    hipLaunchKernelGGL(topk_split_hist<0>, grid, dim3(SP_THREADS), 0, st, p, a);
+    hipLaunchKernelGGL(topk_split_hist<1>, grid, dim3(SP_THREADS), 0, st, p, a);
+    hipLaunchKernelGGL(topk_split_hist<2>, grid, dim3(SP_THREADS), 0, st, p, a);
+    hipLaunchKernelGGL(topk_split_count, grid, dim3(SP_THREADS), 0, st, p, a);
+    hipLaunchKernelGGL(topk_split_emit, grid, dim3(SP_THREADS), 0, st, p, a);
+    if (n_launches) *n_launches += 6;
+    return hipGetLastError();
+  }
   if (p.s_cap <= TK_CACHE_KEYS) {
     const size_t lds = (size_t)(p.s_cap > 0 ? p.s_cap : 1) * 4;
     static std::atomic<size_t> high{0};

@@ -134,6 +134,18 @@ def test_group_argument_errors(L):
     assert cache.valid == 0 and cache.donor_layer == -1
 
 
+def test_topk_workspace_only_for_few_long_rows(L):
+    # few rows over a long prefix are chunked over workgroups and need histogram space
+    long_rows = _shape(B=4, T=1, s_cap=1 << 20, topk=2048)
+    need = L.dsa_workspace_bytes(C.byref(long_rows), b.OP_TOPK)
+    assert need >= 4 * 3 * 2048 * 4
+    assert L.dsa_topk_select(C.byref(long_rows), FAKE, 1 << 20, FAKE, None, 0, None) == 5
+    assert L.dsa_topk_select(C.byref(long_rows), FAKE, 1 << 20, FAKE, FAKE, need - 1, None) == 5
+    # many rows, or short rows, take one workgroup per row and no workspace
+    assert L.dsa_workspace_bytes(C.byref(_shape(B=1, T=4096, s_cap=4096, topk=2048)), b.OP_TOPK) == 0
+    assert L.dsa_workspace_bytes(C.byref(_shape(B=1, T=512, s_cap=1 << 17, topk=2048)), b.OP_TOPK) == 0
+
+
 def test_workspace_sizes(L):
     s = _shape(B=1, T=4096, s_cap=4096, topk=2048, Hm=64, Dc=512, Dr=64)
     assert L.dsa_workspace_bytes(C.byref(s), b.OP_GROUP) >= 4096 * 4096 * 4

@@ -78,8 +78,13 @@ TOPK_CASES = [
     ((1, 64), 5000, 2048, "ties"),
     ((2, 16), 3000, 100, "zeros"),
     ((1, 48), 4096, 2048, "mixed"),
-    ((1, 6), 40000, 2048, "mixed"),      # rows longer than the LDS key cache
+    ((1, 6), 40000, 2048, "mixed"),      # few long rows: chunked over workgroups
     ((3, 1), 33000, 2048, "normal"),
+    ((2, 5), 100000, 2048, "ties"),
+    ((1, 3), 70001, 2048, "zeros"),
+    ((1, 7), 20000, 512, "mixed"),
+    ((4, 1), 1 << 20, 2048, "normal"),   # 1M-key rows
+    ((1, 512), 40000, 2048, "normal"),   # many rows longer than the LDS key cache
 ]
 
 
@@ -96,7 +101,10 @@ def test_topk_is_bit_exact(rows, s_cap, k, kind):
     ks = np.minimum(rng.integers(0, 50, (B, T)), ke).astype(np.int32)
     ks[0, 0] = 0
     out = torch.full((B, T, k), -7, dtype=torch.int32, device="cuda")
-    b.topk_select(f32_dev(sc), out, s_cap, key_start=i32_dev(ks), key_end=i32_dev(ke))
+    nws = b.workspace_bytes(b.make_shape(B, T, s_cap, topk=k), b.OP_TOPK)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)                        # the split path must not rely on a cleared workspace
+    b.topk_select(f32_dev(sc), out, s_cap, key_start=i32_dev(ks), key_end=i32_dev(ke), workspace=ws)
     got = out.cpu().numpy()
     ref, _ = O.topk(sc.astype(np.float64), ks, ke, k)
     assert np.array_equal(got, ref)
