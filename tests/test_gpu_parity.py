@@ -38,6 +38,13 @@ INDEXER_CASES = {
     "bf16_decode": dict(B=3, T=1, S=300, pos0=299),
     "fp8_decode_planted": dict(B=2, T=1, S=700, pos0=699, idx_dtype="fp8", plant_frac=0.05),
     "bf16_generic_d64": dict(B=1, T=40, S=90, pos0=50, D=64, H=8, Hk=8),
+    # decode streaming kernel: shared key head, 16 / 64 heads, several queries per item
+    "bf16_decode_shared_key": dict(B=2, T=1, S=300, pos0=299, Hk=1),
+    "fp8_decode_shared_key_h64": dict(B=2, T=1, S=257, pos0=256, H=64, Hk=1, idx_dtype="fp8"),
+    "bf16_decode_h16_t3": dict(B=2, T=3, S=130, pos0=127, H=16, Hk=16),
+    "fp8_decode_h64_t4": dict(B=1, T=4, S=1000, pos0=996, H=64, Hk=64, idx_dtype="fp8"),
+    # between decode and prefill tiles
+    "bf16_t8": dict(B=2, T=8, S=100, pos0=92),
 }
 
 
