@@ -36,7 +36,6 @@ PEAK_HBM_GBS = 8000.0
 # on a plain copy of known size (`bench.py --copy-calibration`); keyed (workload, kernel) and
 # removed whenever that kernel changes (then reported as null).
 MEASURED_TRAFFIC_BYTES = {
-    ("prefill4k_bf16", "mla_mfma"): 319451.6 * 1024 * 2.0 + 263168.0 * 1024 * 1.0,
     ("decode32k_b64_bf16", "indexer_stream"): 8426542.5 * 1024 * 2.0 + 18968.1 * 1024 * 1.0,
 }
 

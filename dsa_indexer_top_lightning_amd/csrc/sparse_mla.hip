@@ -58,7 +58,8 @@ constexpr int TILE_BYTES = NGROUP * GROUP_BYTES; // 73728
 constexpr int LOADS_PER_WAVE = NGROUP * 2;       // each wave gathers 16 rows: 2 row octets x 9 segments
 constexpr int LDS_XMAX = 4 * 32 * 4;             // per-wave tile maxima of 32 heads
 constexpr int LDS_XP = 4 * 8 * 64 * 4;           // per-wave P^T tile as bf16 pairs
-constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP;
+constexpr int LDS_RING = 4 * 4 * 64 * 4;         // per-wave ring of 4 tiles' entries
+constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP + LDS_RING;
 constexpr int MAX_TILES_PER_ITEM = 64;
 // The running max is raised only when a tile's max exceeds it by more than 2^8 (log2
 // units); until then probabilities are taken against the stale max (values <= 256),
@@ -107,7 +108,36 @@ __device__ __forceinline__ void scale_agpr(f32x16& a, float alpha) {
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }           // vmcnt(0)
+// Transposing LDS read (ds_read_b64_tr_b16) issued as inline asm.  The compiler treats
+// the intrinsic as possibly reading what an in-flight global-to-LDS gather writes and
+// waits for every outstanding global load before it; these reads only touch the tile
+// being consumed, never the one being gathered.  The compiler does not count these
+// reads, so their results are waited for explicitly with lds_wait_frags.
+__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+// Wait until at most N LDS operations are outstanding; tied to the fragments it
+// guards so that their consumers cannot be scheduled above it.
+template <int N>
+__device__ __forceinline__ void lds_wait_frags(bf16x8 (&f)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "i"(N));
+}
+
+// Workgroup barriers that order LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load of the wave (vmcnt(0)), which would stall on the next tile's
+// gather that is meant to fly across the barrier.  The memory clobber keeps the
+// compiler from moving memory operations across either barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// ... and the tile barrier: this wave's gather of the current tile has landed (all but
+// the newest global load, the entry load issued after it) before the barrier.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // grid.x = (query, split) work item, heaviest queries first; grid.y = head group.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
@@ -134,10 +164,16 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   const int t0 = split * tiles_per_split;
   const int e_lo = t0 * MT, e_hi = min(topk, (t0 + tiles_per_split) * MT);
   int emax = -1;
-#pragma unroll 8
-  for (int e = e_lo + lane; e < e_hi; e += 64) {
-    const int32_t v = gidx[e];
-    if (v >= 0 && (int64_t)v < s_cap) emax = e;
+  for (int e0 = e_lo; e0 < e_hi; e0 += 16 * 64) {  // 16 independent loads in flight per lane
+    int32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + 64 * u + lane;
+      v[u] = e < e_hi ? gidx[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (v[u] >= 0 && (int64_t)v[u] < s_cap) emax = e0 + 64 * u + lane;
   }
   for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
   const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
@@ -167,18 +203,22 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   }
 
   const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
-  // this lane's entry of tile t: returns validity; `load_idx` is the row to gather
-  auto entry = [&](int t, int32_t& load_idx) -> bool {
-    const int e = t * MT + lane;
-    const int32_t v = e < topk ? gidx[e] : -1;
-    const bool ok = v >= 0 && (int64_t)v < s_cap;
-    load_idx = ok ? v : 0;  // an invalid entry gathers row 0 (in bounds) and is masked
-    return ok;
+  // The entries of tile t are copied by each wave into its own LDS ring slot t % 4 with
+  // one 4-byte global-to-LDS load (lane i writes word i), so that no register carries a
+  // pending load across tiles.  Past the end the loads re-read the last entry (never used).
+  const int32_t* ering = reinterpret_cast<const int32_t*>(smem + 2 * TILE_BYTES + LDS_XMAX + LDS_XP) + wv * 4 * MT;
+  auto fetch_entries = [&](int t) {
+    __builtin_amdgcn_global_load_lds(gidx + min((t0 + t) * MT + lane, topk - 1),
+                                     (__attribute__((address_space(3))) void*)(ering + (t & 3) * MT), 4, 0, 0);
   };
+  auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
+  auto valid = [&](int32_t v) -> bool { return v >= 0 && (int64_t)v < s_cap; };
   // gather a tile into buffer bf: wave w loads rows [16w, 16w + 16) as 2 row octets x 9
   // segments; in each load lane i fills row 8q + i/8 at stored chunk i%8, which holds
-  // the row's logical chunk (i%8) ^ perm(row)
-  auto issue = [&](int bf, int32_t lidx) {
+  // the row's logical chunk (i%8) ^ perm(row).  An invalid entry gathers row 0 (in
+  // bounds) and is masked out of the softmax.
+  auto issue = [&](int bf, int32_t ent) {
+    const int32_t lidx = valid(ent) ? ent : 0;
     const unsigned char* src[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -196,11 +236,20 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
                                          16, 0, 0);
   };
 
-  int32_t li_cur, li_nxt = 0;
-  bool ok_cur = entry(t0, li_cur), ok_nxt = false;
+  // Entries are fetched two tiles ahead of their gather and every gather is followed by
+  // exactly one entry fetch, so at the top of tile i `vmcnt(1)` leaves only the newest
+  // entry fetch in flight: the gather of tile i has landed and so have the entries of
+  // tile i + 1, without waiting for anything issued later.
+  fetch_entries(0);
+  fetch_entries(1);
   wait_vmem();
-  issue(0, li_cur);
-  if (ntiles > 1) ok_nxt = entry(t0 + 1, li_nxt);
+  uint64_t vmask_nxt;
+  {
+    const int32_t e0 = read_entry(0);
+    vmask_nxt = __ballot(valid(e0));
+    issue(0, e0);
+  }
+  fetch_entries(2);
 
   const float qk_scale = p.sm_scale * LOG2E;
   float m_run = -__builtin_inff(), l_run = 0.f;
@@ -231,15 +280,16 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 
   for (int i = 0; i < ntiles; ++i) {
     const int bf = i & 1;
-    wait_vmem();
-    __syncthreads();  // tile i is in LDS for every wave; buffer bf^1 is free
-    const uint64_t vmask = __ballot(ok_cur);
+    tile_barrier();  // tile i is in LDS for every wave; buffer bf^1 is free
+    const uint64_t vmask = vmask_nxt;
     if (i + 1 < ntiles) {
-      issue(bf ^ 1, li_nxt);
-      ok_cur = ok_nxt;
-      if (i + 2 < ntiles) ok_nxt = entry(t0 + i + 2, li_nxt);
+      const int32_t e_next = read_entry(i + 1);
+      vmask_nxt = __ballot(valid(e_next));
+      issue(bf ^ 1, e_next);
+      fetch_entries(i + 3);
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;
+    const uint32_t tb_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)tb;
 
     // S^T for own 32 kv rows x 32 heads; K fragments read one group of 6 steps ahead
     f32x16 s;
@@ -282,7 +332,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lg == 0) xmax[wave * 32 + lr] = mx;
-    __syncthreads();
+    lds_barrier();
     // both waves of a head pair see the same maxima, so they take the same decisions
     const float m_tile = fmaxf(mx, xmax[(wave ^ 2) * 32 + lr]);
     if (__ballot(m_tile > m_run + RESCALE_LOG2)) {
@@ -300,7 +350,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
       xp[(wave * 8 + r) * 64 + lane] = own[r];
     }
-    __syncthreads();
+    lds_barrier();
     uint32_t h0[8], h1[8];  // P^T of kv rows [0, 32) and [32, 64), C-layout order
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
@@ -349,17 +399,20 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
             i16x4 h[2];
             bf16x8 b;
           } a;
-          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tb + voff[0][dt & 1] + off));
-          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tb + voff[1][dt & 1] + off));
+          a.h[0] = lds_read_tr(tb_lds + voff[0][dt & 1] + off);
+          a.h[1] = lds_read_tr(tb_lds + voff[1][dt & 1] + off);
           dst[u] = a.b;
         }
       };
       load_v(0, vf[0]);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        if (q + 1 < 8) load_v(q + 1, vf[(q + 1) & 1]);
+        if (q + 1 < 8) {
+          load_v(q + 1, vf[(q + 1) & 1]);
+          lds_wait_frags<8>(vf[q & 1]);  // this step's 8 reads, not the 8 just issued
+        } else {
+          lds_wait_frags<0>(vf[q & 1]);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int dt = 4 * (q & 1) + u;
