@@ -116,14 +116,39 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // reads, so their results are waited for explicitly with lds_wait_frags.
 __device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
   i16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=a"(r) : "v"(addr));
   return r;
 }
-// Wait until at most N LDS operations are outstanding; tied to the fragments it
-// guards so that their consumers cannot be scheduled above it.
+// 16-byte LDS read into accumulation registers (a matrix-core operand), inline asm for
+// the same reason; waited for with lds_wait_frags_p.
+__device__ __forceinline__ bf16x8 lds_read_b128_a(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1" : "=a"(r) : "v"(addr));
+  return r;
+}
+// 16-byte LDS store issued as inline asm, for the same reason: as a plain store the
+// compiler waits for the in-flight gather before it.  Completed by the lgkmcnt(0) of
+// the next barrier.
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, i32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+// Wait until at most N LDS operations are outstanding.  Tied (read and written) to the
+// registers the guarded reads fill, so that neither their consumers nor any copy of
+// them can be scheduled above it.
 template <int N>
-__device__ __forceinline__ void lds_wait_frags(bf16x8 (&f)[4]) {
-  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]) : "i"(N));
+__device__ __forceinline__ void lds_wait_halves(i16x4 (&h)[4][2]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+a"(h[0][0]), "+a"(h[0][1]), "+a"(h[1][0]), "+a"(h[1][1]), "+a"(h[2][0]), "+a"(h[2][1]),
+                 "+a"(h[3][0]), "+a"(h[3][1])
+               : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lds_wait_halves_p(i16x4 (&h)[4][2], bf16x8 (&pf)[4][2]) {
+  asm volatile("s_waitcnt lgkmcnt(%16)"
+               : "+a"(h[0][0]), "+a"(h[0][1]), "+a"(h[1][0]), "+a"(h[1][1]), "+a"(h[2][0]), "+a"(h[2][1]),
+                 "+a"(h[3][0]), "+a"(h[3][1]), "+a"(pf[0][0]), "+a"(pf[0][1]), "+a"(pf[1][0]), "+a"(pf[1][1]),
+                 "+a"(pf[2][0]), "+a"(pf[2][1]), "+a"(pf[3][0]), "+a"(pf[3][1])
+               : "i"(N));
 }
 
 // Workgroup barriers that order LDS traffic only.  __syncthreads() also waits for every
@@ -252,12 +277,18 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   fetch_entries(2);
 
   const float qk_scale = p.sm_scale * LOG2E;
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  f32x16 acc[8];
+  // Running maxima (log2 units) of the two heads this lane meets in the O^T accumulators:
+  // head lr of half 0 (m0) and of half 1 (m1); every wave holds the same values and
+  // takes the same rescale decisions.  l_part sums the bf16 probabilities of this
+  // wave's own S^T block (head 32hh + lr, rows of lane group lg).
+  float m0 = -__builtin_inff(), m1 = -__builtin_inff(), l_part = 0.f;
+  f32x16 acc[4][2];  // O^T: dims 128*wave + 32*db .. +32  x  heads 32*hb .. +32
 #pragma unroll
-  for (int d = 0; d < 8; ++d)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[d][r] = 0.f;
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][hb][r] = 0.f;
 
   // K fragment of step st: row m = 32vv + lr, chunk 2st + lg = segment st/4, chunk-in-segment
   // 2(st%4) + lg: four per-lane offsets, the segment is an immediate
@@ -265,9 +296,10 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   int koff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) koff[u] = mk * SEG + 16 * ((2 * u + lg) ^ perm(mk));
-  // V^T reads: row rb + vrow (read #2: + 8), chunk c = 32vv + 4dt + 2blk + x, byte 8(li & 1);
-  // segment 4vv + dt/2, chunk-in-segment 4(dt%2) + 2blk + x; rb is a multiple of 16 so
-  // perm(row) = perm(vrow): per-lane offsets for (read, dt parity)
+  // V^T fragment (k-step ks, dim block db) = dims 128*wave + 32db .. +32 x the 16 rows of ks:
+  // read #1 gives rows rb + vrow, read #2 rows rb + 8 + vrow, chunk 16wave + 4db + 2blk + x =
+  // segment 2wave + db/2, chunk-in-segment 4(db%2) + 2blk + x, byte 8(li & 1); rb is a
+  // multiple of 16 so perm(row) = perm(vrow): per-lane offsets for (read, db parity)
   const int blk = lr >> 4, li = lr & 15, x = (li & 3) >> 1;
   const int vrow = 4 * lg + (li >> 2);
   int voff[2][2];
@@ -275,8 +307,10 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp)
-      voff[rd][dp] = 4 * vv * GROUP_BYTES + (vrow + 8 * rd) * SEG +
+      voff[rd][dp] = 2 * wave * GROUP_BYTES + (vrow + 8 * rd) * SEG +
                      16 * ((4 * dp + 2 * blk + x) ^ perm(vrow + 8 * rd)) + ((li & 1) << 3);
+  // P exchange: block of wave w, half j (k-step 2vv(w) + j) at xp[(2w + j) * 64 + lane] as 4 dwords
+  const uint32_t xp_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)xp;
 
   for (int i = 0; i < ntiles; ++i) {
     const int bf = i & 1;
@@ -291,12 +325,12 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     const unsigned char* tb = smem + bf * TILE_BYTES;
     const uint32_t tb_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)tb;
 
-    // S^T for own 32 kv rows x 32 heads; K fragments read one group of 6 steps ahead
+    // ---- S^T for own 32 kv rows x 32 heads; K fragments read one group of 4 steps ahead
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
     {
-      constexpr int KG = 4;  // fragments per group
+      constexpr int KG = 4;
       auto kfrag = [&](int st) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(tb + koff[st & 3] + (st >> 2) * GROUP_BYTES);
       };
@@ -333,112 +367,112 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     if (lg == 0) xmax[wave * 32 + lr] = mx;
     lds_barrier();
-    // both waves of a head pair see the same maxima, so they take the same decisions
-    const float m_tile = fmaxf(mx, xmax[(wave ^ 2) * 32 + lr]);
-    if (__ballot(m_tile > m_run + RESCALE_LOG2)) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-      m_run = m_new;
+    // tile maxima of head lr of each half (waves 0, 2 hold half 0; waves 1, 3 half 1)
+    const float mt0 = fmaxf(xmax[lr], xmax[64 + lr]);
+    const float mt1 = fmaxf(xmax[32 + lr], xmax[96 + lr]);
+    if (__ballot(mt0 > m0 + RESCALE_LOG2 || mt1 > m1 + RESCALE_LOG2)) {
+      const float n0 = fmaxf(m0, mt0), n1 = fmaxf(m1, mt1);
+      const float a0 = n0 == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m0 - n0);
+      const float a1 = n1 == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m1 - n1);
+      l_part *= hh ? a1 : a0;
+      m0 = n0;
+      m1 = n1;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) scale_agpr(acc[d], alpha);
+      for (int db = 0; db < 4; ++db) {
+        scale_agpr(acc[db][0], a0);
+        scale_agpr(acc[db][1], a1);
+      }
     }
-    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
+    const float m_own = hh ? m1 : m0;
+    const float m_use = m_own == -__builtin_inff() ? 0.f : m_own;
     uint32_t own[8];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
+    for (int r = 0; r < 8; ++r)
       own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
-      xp[(wave * 8 + r) * 64 + lane] = own[r];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      lds_write_b128(xp_lds + ((2 * wave + j) * 64 + lane) * 16,
+                     i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]});
+    {
+      float ls = 0.f;  // the probabilities actually used, as rounded to bf16
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ls += __uint_as_float(own[r] << 16) + __uint_as_float(own[r] & 0xffff0000u);
+      l_part += ls;
     }
     lds_barrier();
-    uint32_t h0[8], h1[8];  // P^T of kv rows [0, 32) and [32, 64), C-layout order
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const uint32_t o = xp[((wave ^ 2) * 8 + r) * 64 + lane];
-      h0[r] = vv == 0 ? own[r] : o;
-      h1[r] = vv == 0 ? o : own[r];
-    }
-    float s0 = 0.f, s1 = 0.f;  // the same sums, in the same order, in both waves of the pair
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      s0 += __uint_as_float(h0[r] << 16) + __uint_as_float(h0[r] & 0xffff0000u);
-      s1 += __uint_as_float(h1[r] << 16) + __uint_as_float(h1[r] & 0xffff0000u);
-    }
-    s0 += __shfl_xor(s0, 32, 64);
-    s1 += __shfl_xor(s1, 32, 64);
-    l_run += s0 + s1;
 
-    // P^T fragments: step sg covers C-layout values 8*(sg%2) .. +7 of half sg/2
-    bf16x8 pf[4];
-#pragma unroll
-    for (int sg = 0; sg < 4; ++sg) {
-      union {
-        uint32_t u[4];
-        bf16x8 b;
-      } u;
-      const uint32_t* src = (sg < 2) ? h0 : h1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u.u[e] = src[4 * (sg & 1) + e];
-      pf[sg] = u.b;
-    }
-
-    // O^T[256vv + 32dt .. +32][32 heads] += V^T . P^T, V^T fragments by transposing LDS reads:
-    // read #1 of step sg gives rows rb .. rb+3 of column (lane), read #2 rows rb+8 .. rb+11;
-    // the 8 fragments of step sg+1 are read while step sg's MFMAs run
+    // ---- O^T[dims 128wave + 32db][heads 32hb] += V^T . P^T over the tile's 4 k-steps of
+    // 16 rows; k-step ks uses C-layout values 8(ks%2) .. +7 of the S^T block of rows
+    // 32(ks/2) .. +32.  The 8 V^T reads of step ks+1 are issued while step ks's MFMAs run.
     {
-      bf16x8 vf[2][4];
-      // group q = (step sg, dims half dh): 4 fragments dt = 4dh .. 4dh+3
-      auto load_v = [&](int q, bf16x8* dst) {
-        const int sg = q >> 1, dh = q & 1;
-        const int rb = 32 * (sg >> 1) + 16 * (sg & 1);
+      // P^T fragments of all 4 k-steps x 2 head halves (every wave's block, own included)
+      bf16x8 pf[4][2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dt = 4 * dh + u;
-          const int off = (dt >> 1) * GROUP_BYTES + rb * SEG;
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          pf[ks][hb] = lds_read_b128_a(xp_lds + ((2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane) * 16);
+      // V^T halves as read (i16x4 each): the 128-bit fragments are assembled only after
+      // the wait, so no copy of a register still being filled by LDS is ever made
+      i16x4 vh[2][4][2];
+      auto load_v = [&](int ks, i16x4 (&dst)[4][2]) {
+        const int rb = 32 * (ks >> 1) + 16 * (ks & 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int off = (db >> 1) * GROUP_BYTES + rb * SEG;
+          dst[db][0] = lds_read_tr(tb_lds + voff[0][db & 1] + off);
+          dst[db][1] = lds_read_tr(tb_lds + voff[1][db & 1] + off);
+        }
+      };
+      load_v(0, vh[0]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) {
+          load_v(ks + 1, vh[(ks + 1) & 1]);
+          // this step's V^T reads (and, at step 0, the P^T reads) but not the 8 just issued
+          if (ks == 0) lds_wait_halves_p<8>(vh[0], pf);
+          else lds_wait_halves<8>(vh[ks & 1]);
+        } else {
+          lds_wait_halves<0>(vh[ks & 1]);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
           union {
             i16x4 h[2];
             bf16x8 b;
-          } a;
-          a.h[0] = lds_read_tr(tb_lds + voff[0][dt & 1] + off);
-          a.h[1] = lds_read_tr(tb_lds + voff[1][dt & 1] + off);
-          dst[u] = a.b;
-        }
-      };
-      load_v(0, vf[0]);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q + 1 < 8) {
-          load_v(q + 1, vf[(q + 1) & 1]);
-          lds_wait_frags<8>(vf[q & 1]);  // this step's 8 reads, not the 8 just issued
-        } else {
-          lds_wait_frags<0>(vf[q & 1]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dt = 4 * (q & 1) + u;
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[q & 1][u], pf[q >> 1], acc[dt], 0, 0, 0);
+          } v;
+          v.h[0] = vh[ks & 1][db][0];
+          v.h[1] = vh[ks & 1][db][1];
+          acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.b, pf[ks][0], acc[db][0], 0, 0, 0);
+          acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.b, pf[ks][1], acc[db][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
+  // ---- row sums per head: own block (both lane groups), then both row halves
+  l_part += __shfl_xor(l_part, 32, 64);
+  if (lg == 0) xmax[wave * 32 + lr] = l_part;  // every wave is past its last read of xmax
+  __syncthreads();
+  const float L0 = xmax[lr] + xmax[64 + lr], L1 = xmax[32 + lr] + xmax[96 + lr];
+
   if (nsplit == 1) {
     // normalise, transpose through LDS, write out[tok][hg*64 .. +64][512] with 16-byte stores
-    __syncthreads();
     constexpr int OST = MDC + 8;  // padded bf16 row stride of the staging buffer
     uint16_t* ost = reinterpret_cast<uint16_t*>(smem);
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    const int hl = 32 * hh + lr;
+    const float inv[2] = {L0 > 0.f ? 1.f / L0 : 0.f, L1 > 0.f ? 1.f / L1 : 0.f};
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dim = 256 * vv + 32 * dt + 8 * j + 4 * lg;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(ost + hl * OST + dim);
-        dst[0] = pack_bf16x2(acc[dt][4 * j] * inv, acc[dt][4 * j + 1] * inv);
-        dst[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
-      }
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dim = 128 * wave + 32 * db + 8 * j + 4 * lg;
+          uint32_t* dst = reinterpret_cast<uint32_t*>(ost + (32 * hb + lr) * OST + dim);
+          dst[0] = pack_bf16x2(acc[db][hb][4 * j] * inv[hb], acc[db][hb][4 * j + 1] * inv[hb]);
+          dst[1] = pack_bf16x2(acc[db][hb][4 * j + 2] * inv[hb], acc[db][hb][4 * j + 3] * inv[hb]);
+        }
     __syncthreads();
     unsigned char* og = static_cast<unsigned char*>(p.out) + ((tok * p.Hm + hg * MHG) * MDC) * 2;
     for (int c = tid; c < MHG * (MDC * 2 / 16); c += 256) {
@@ -446,22 +480,30 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       *reinterpret_cast<i32x4*>(og + (h * MDC) * 2 + ch * 16) =
           *reinterpret_cast<const i32x4*>(reinterpret_cast<const unsigned char*>(ost + h * OST) + ch * 16);
     }
-    if (p.lse && vv == 0 && lg == 0)
-      p.lse[tok * p.Hm + myhead] = l_run > 0.f ? (m_run + log2f(l_run)) * LN2 : -__builtin_inff();
+    if (p.lse && wave == 0 && lg == 0) {
+      p.lse[tok * p.Hm + hg * MHG + lr] = L0 > 0.f ? (m0 + log2f(L0)) * LN2 : -__builtin_inff();
+      p.lse[tok * p.Hm + hg * MHG + 32 + lr] = L1 > 0.f ? (m1 + log2f(L1)) * LN2 : -__builtin_inff();
+    }
   } else {
-    float* o = ws_o + ((tok * nsplit + split) * p.Hm + myhead) * MDC;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int hb = 0; hb < 2; ++hb) {
+      float* o = ws_o + ((tok * nsplit + split) * p.Hm + hg * MHG + 32 * hb + lr) * MDC;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int dim = 256 * vv + 32 * dt + 8 * j + 4 * lg;
-        float4 v = make_float4(acc[dt][4 * j], acc[dt][4 * j + 1], acc[dt][4 * j + 2], acc[dt][4 * j + 3]);
-        *reinterpret_cast<float4*>(o + dim) = v;
-      }
-    if (vv == 0 && lg == 0) {
-      float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + myhead) * 2;
-      ml[0] = m_run;
-      ml[1] = l_run;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int dim = 128 * wave + 32 * db + 8 * j + 4 * lg;
+          *reinterpret_cast<float4*>(o + dim) =
+              make_float4(acc[db][hb][4 * j], acc[db][hb][4 * j + 1], acc[db][hb][4 * j + 2], acc[db][hb][4 * j + 3]);
+        }
+    }
+    if (wave == 0 && lg == 0) {
+      float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + hg * MHG + lr) * 2;
+      ml[0] = m0;
+      ml[1] = L0;
+      ml += 32 * 2;
+      ml[0] = m1;
+      ml[1] = L1;
     }
   }
 }
