@@ -108,48 +108,31 @@ __device__ __forceinline__ void scale_agpr(f32x16& a, float alpha) {
   }
 }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }           // vmcnt(0)
-// Transposing LDS read (ds_read_b64_tr_b16) issued as inline asm.  The compiler treats
-// the intrinsic as possibly reading what an in-flight global-to-LDS gather writes and
-// waits for every outstanding global load before it; these reads only touch the tile
-// being consumed, never the one being gathered.  The compiler does not count these
-// reads, so their results are waited for explicitly with lds_wait_frags.
-__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
-  i16x4 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=a"(r) : "v"(addr));
-  return r;
+// every global load of this wave has landed, the asm global-to-LDS copies included
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Global-to-LDS copies issued as inline asm.  Written with the compiler's builtin, the
+// copies are LDS stores it cannot tell apart from the tile being read, so it makes
+// every later LDS access wait for all of them (vmcnt(0)) and the next tile's gather
+// could no longer overlap the current tile's math.  Issued here, they are ordered by
+// the memory clobber and waited for explicitly at the tile barrier (vmcnt).  Each copy
+// sets M0 one wait state before the load reads it; the lane's data lands at
+// M0 + instruction offset + size * lane (the immediate offset moves the LDS address
+// as well as the global one, so M0 takes the LDS offset minus the global one).  The compiler issues no other global-to-LDS copy in this
+// kernel and nothing else here uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int GOFF, int LOFF>
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  static_assert(LOFF >= GOFF && GOFF >= 0 && GOFF < 4096, "offset outside the immediate field");
+  asm volatile("s_add_i32 m0, %1, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               ::"v"(src), "s"(lds_base), "i"(GOFF), "i"(LOFF - GOFF)
+               : "memory", "m0");
 }
-// 16-byte LDS read into accumulation registers (a matrix-core operand), inline asm for
-// the same reason; waited for with lds_wait_frags_p.
-__device__ __forceinline__ bf16x8 lds_read_b128_a(uint32_t addr) {
-  bf16x8 r;
-  asm volatile("ds_read_b128 %0, %1" : "=a"(r) : "v"(addr));
-  return r;
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds_base)
+               : "memory", "m0");
 }
-// 16-byte LDS store issued as inline asm, for the same reason: as a plain store the
-// compiler waits for the in-flight gather before it.  Completed by the lgkmcnt(0) of
-// the next barrier.
-__device__ __forceinline__ void lds_write_b128(uint32_t addr, i32x4 v) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
-}
-// Wait until at most N LDS operations are outstanding.  Tied (read and written) to the
-// registers the guarded reads fill, so that neither their consumers nor any copy of
-// them can be scheduled above it.
-template <int N>
-__device__ __forceinline__ void lds_wait_halves(i16x4 (&h)[4][2]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+a"(h[0][0]), "+a"(h[0][1]), "+a"(h[1][0]), "+a"(h[1][1]), "+a"(h[2][0]), "+a"(h[2][1]),
-                 "+a"(h[3][0]), "+a"(h[3][1])
-               : "i"(N));
-}
-template <int N>
-__device__ __forceinline__ void lds_wait_halves_p(i16x4 (&h)[4][2], bf16x8 (&pf)[4][2]) {
-  asm volatile("s_waitcnt lgkmcnt(%16)"
-               : "+a"(h[0][0]), "+a"(h[0][1]), "+a"(h[1][0]), "+a"(h[1][1]), "+a"(h[2][0]), "+a"(h[2][1]),
-                 "+a"(h[3][0]), "+a"(h[3][1]), "+a"(pf[0][0]), "+a"(pf[0][1]), "+a"(pf[1][0]), "+a"(pf[1][1]),
-                 "+a"(pf[2][0]), "+a"(pf[2][1]), "+a"(pf[3][0]), "+a"(pf[3][1])
-               : "i"(N));
-}
+#pragma clang diagnostic pop
 
 // Workgroup barriers that order LDS traffic only.  __syncthreads() also waits for every
 // outstanding global load of the wave (vmcnt(0)), which would stall on the next tile's
@@ -225,6 +208,10 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     const unsigned char* qg = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + myhead) * MRB;
 #pragma unroll
     for (int st = 0; st < MROW / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qg + (16 * st + 8 * lg) * 2);
+    // opaque to the compiler from here on: under register pressure it would otherwise
+    // re-load the query from global memory on every tile instead of keeping it
+#pragma unroll
+    for (int st = 0; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
   }
 
   const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
@@ -232,16 +219,15 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   // one 4-byte global-to-LDS load (lane i writes word i), so that no register carries a
   // pending load across tiles.  Past the end the loads re-read the last entry (never used).
   const int32_t* ering = reinterpret_cast<const int32_t*>(smem + 2 * TILE_BYTES + LDS_XMAX + LDS_XP) + wv * 4 * MT;
-  auto fetch_entries = [&](int t) {
-    __builtin_amdgcn_global_load_lds(gidx + min((t0 + t) * MT + lane, topk - 1),
-                                     (__attribute__((address_space(3))) void*)(ering + (t & 3) * MT), 4, 0, 0);
-  };
+  const uint32_t ering_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int32_t*)ering;
+  auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
   auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
   auto valid = [&](int32_t v) -> bool { return v >= 0 && (int64_t)v < s_cap; };
   // gather a tile into buffer bf: wave w loads rows [16w, 16w + 16) as 2 row octets x 9
   // segments; in each load lane i fills row 8q + i/8 at stored chunk i%8, which holds
   // the row's logical chunk (i%8) ^ perm(row).  An invalid entry gathers row 0 (in
   // bounds) and is masked out of the softmax.
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
   auto issue = [&](int bf, int32_t ent) {
     const int32_t lidx = valid(ent) ? ent : 0;
     const unsigned char* src[2];
@@ -251,14 +237,26 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       const int32_t ri = __shfl(lidx, row, 64);
       src[q] = kvg + (uint32_t)ri * (uint32_t)MRB + 16 * ((lane & 7) ^ perm(row));
     }
-    unsigned char* dst = smem + bf * TILE_BYTES + wv * (16 * SEG);
-#pragma unroll
-    for (int g = 0; g < NGROUP; ++g)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_global_load_lds(src[q] + g * SEG,
-                                         (__attribute__((address_space(3))) void*)(dst + g * GROUP_BYTES + q * 1024),
-                                         16, 0, 0);
+    const uint32_t dst = smem_lds + bf * TILE_BYTES + wv * (16 * SEG);
+    // segment g of the 2 row octets: global byte g * 128 of each row, LDS group g
+    dma16<0 * SEG, 0 * GROUP_BYTES>(src[0], dst);
+    dma16<0 * SEG, 0 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<1 * SEG, 1 * GROUP_BYTES>(src[0], dst);
+    dma16<1 * SEG, 1 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<2 * SEG, 2 * GROUP_BYTES>(src[0], dst);
+    dma16<2 * SEG, 2 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<3 * SEG, 3 * GROUP_BYTES>(src[0], dst);
+    dma16<3 * SEG, 3 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<4 * SEG, 4 * GROUP_BYTES>(src[0], dst);
+    dma16<4 * SEG, 4 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<5 * SEG, 5 * GROUP_BYTES>(src[0], dst);
+    dma16<5 * SEG, 5 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<6 * SEG, 6 * GROUP_BYTES>(src[0], dst);
+    dma16<6 * SEG, 6 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<7 * SEG, 7 * GROUP_BYTES>(src[0], dst);
+    dma16<7 * SEG, 7 * GROUP_BYTES + 1024>(src[1], dst);
+    dma16<8 * SEG, 8 * GROUP_BYTES>(src[0], dst);
+    dma16<8 * SEG, 8 * GROUP_BYTES + 1024>(src[1], dst);
   };
 
   // Entries are fetched two tiles ahead of their gather and every gather is followed by
@@ -310,7 +308,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       voff[rd][dp] = 2 * wave * GROUP_BYTES + (vrow + 8 * rd) * SEG +
                      16 * ((4 * dp + 2 * blk + x) ^ perm(vrow + 8 * rd)) + ((li & 1) << 3);
   // P exchange: block of wave w, half j (k-step 2vv(w) + j) at xp[(2w + j) * 64 + lane] as 4 dwords
-  const uint32_t xp_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t*)xp;
+  i32x4* xpv = reinterpret_cast<i32x4*>(xp);
 
   for (int i = 0; i < ntiles; ++i) {
     const int bf = i & 1;
@@ -323,7 +321,6 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       fetch_entries(i + 3);
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;
-    const uint32_t tb_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const unsigned char*)tb;
 
     // ---- S^T for own 32 kv rows x 32 heads; K fragments read one group of 4 steps ahead
     f32x16 s;
@@ -391,8 +388,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      lds_write_b128(xp_lds + ((2 * wave + j) * 64 + lane) * 16,
-                     i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]});
+      xpv[(2 * wave + j) * 64 + lane] = i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]};
     {
       float ls = 0.f;  // the probabilities actually used, as rounded to bf16
 #pragma unroll
@@ -406,45 +402,35 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     // 32(ks/2) .. +32.  The 8 V^T reads of step ks+1 are issued while step ks's MFMAs run.
     {
       // P^T fragments of all 4 k-steps x 2 head halves (every wave's block, own included)
-      bf16x8 pf[4][2];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          pf[ks][hb] = lds_read_b128_a(xp_lds + ((2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane) * 16);
-      // V^T halves as read (i16x4 each): the 128-bit fragments are assembled only after
-      // the wait, so no copy of a register still being filled by LDS is ever made
-      i16x4 vh[2][4][2];
-      auto load_v = [&](int ks, i16x4 (&dst)[4][2]) {
+      auto p_frag = [&](int ks, int hb) -> bf16x8 {
+        return __builtin_bit_cast(bf16x8, xpv[(2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane]);
+      };
+      bf16x8 vf[2][4];
+      auto load_v = [&](int ks, bf16x8* dst) {
         const int rb = 32 * (ks >> 1) + 16 * (ks & 1);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int off = (db >> 1) * GROUP_BYTES + rb * SEG;
-          dst[db][0] = lds_read_tr(tb_lds + voff[0][db & 1] + off);
-          dst[db][1] = lds_read_tr(tb_lds + voff[1][db & 1] + off);
-        }
-      };
-      load_v(0, vh[0]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
-          load_v(ks + 1, vh[(ks + 1) & 1]);
-          // this step's V^T reads (and, at step 0, the P^T reads) but not the 8 just issued
-          if (ks == 0) lds_wait_halves_p<8>(vh[0], pf);
-          else lds_wait_halves<8>(vh[ks & 1]);
-        } else {
-          lds_wait_halves<0>(vh[ks & 1]);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
           union {
             i16x4 h[2];
             bf16x8 b;
-          } v;
-          v.h[0] = vh[ks & 1][db][0];
-          v.h[1] = vh[ks & 1][db][1];
-          acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.b, pf[ks][0], acc[db][0], 0, 0, 0);
-          acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v.b, pf[ks][1], acc[db][1], 0, 0, 0);
+          } a;
+          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tb + voff[0][db & 1] + off));
+          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4*)(tb + voff[1][db & 1] + off));
+          dst[db] = a.b;
+        }
+      };
+      load_v(0, vf[0]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 p0 = p_frag(ks, 0), p1 = p_frag(ks, 1);
+        if (ks + 1 < 4) load_v(ks + 1, vf[(ks + 1) & 1]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks & 1][db], p0, acc[db][0], 0, 0, 0);
+          acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks & 1][db], p1, acc[db][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
