@@ -56,7 +56,7 @@ constexpr int GROUP_BYTES = MT * SEG;            // one segment of all 64 rows (
 constexpr int NGROUP = MRB / SEG;                // 9 segments per row
 constexpr int TILE_BYTES = NGROUP * GROUP_BYTES; // 73728
 constexpr int LOADS_PER_WAVE = NGROUP * 2;       // each wave gathers 16 rows: 2 row octets x 9 segments
-constexpr int LDS_XMAX = 4 * 32 * 4;             // per-wave tile maxima of 32 heads
+constexpr int LDS_XMAX = 4 * 32 * 4 + 64;        // per-wave tile maxima of 32 heads + rescale flags
 constexpr int LDS_XP = 4 * 8 * 64 * 4;           // per-wave P^T tile as bf16 pairs
 constexpr int LDS_RING = 4 * 4 * 64 * 4;         // per-wave ring of 4 tiles' entries
 constexpr int LDS_MLA = 2 * TILE_BYTES + LDS_XMAX + LDS_XP + LDS_RING;
@@ -208,10 +208,14 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     const unsigned char* qg = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + myhead) * MRB;
 #pragma unroll
     for (int st = 0; st < MROW / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qg + (16 * st + 8 * lg) * 2);
-    // opaque to the compiler from here on: under register pressure it would otherwise
-    // re-load the query from global memory on every tile instead of keeping it
+    // opaque to the compiler from here on (under register pressure it would otherwise
+    // re-load the query from global memory on every tile); the 512 latent dims live in
+    // accumulation registers, which the matrix cores read directly, leaving the vector
+    // registers for deeper LDS prefetch
 #pragma unroll
-    for (int st = 0; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
+    for (int st = 0; st < MDC / 16; ++st) asm volatile("" : "+a"(qf[st]));
+#pragma unroll
+    for (int st = MDC / 16; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
   }
 
   const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
@@ -223,40 +227,46 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
   auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
   auto valid = [&](int32_t v) -> bool { return v >= 0 && (int64_t)v < s_cap; };
-  // gather a tile into buffer bf: wave w loads rows [16w, 16w + 16) as 2 row octets x 9
-  // segments; in each load lane i fills row 8q + i/8 at stored chunk i%8, which holds
-  // the row's logical chunk (i%8) ^ perm(row).  An invalid entry gathers row 0 (in
-  // bounds) and is masked out of the softmax.
-  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  auto issue = [&](int bf, int32_t ent) {
+  struct GatherSrc {
+    const unsigned char* a[2];
+  };
+  // per-lane sources of a tile's gather: wave w loads rows [16w, 16w + 16) as 2 row octets
+  // x 9 segments; in each load lane i fills row 8q + i/8 at stored chunk i%8, which holds
+  // the row's logical chunk (i%8) ^ perm(row).  An invalid entry gathers row 0 (in bounds)
+  // and is masked out of the softmax.
+  auto gather_src = [&](int32_t ent) -> GatherSrc {
     const int32_t lidx = valid(ent) ? ent : 0;
-    const unsigned char* src[2];
+    GatherSrc g;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int row = 16 * wave + 8 * q + (lane >> 3);
       const int32_t ri = __shfl(lidx, row, 64);
-      src[q] = kvg + (uint32_t)ri * (uint32_t)MRB + 16 * ((lane & 7) ^ perm(row));
+      g.a[q] = kvg + (uint32_t)ri * (uint32_t)MRB + 16 * ((lane & 7) ^ perm(row));
     }
+    return g;
+  };
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  auto gather = [&](int bf, const GatherSrc& g) {
     const uint32_t dst = smem_lds + bf * TILE_BYTES + wv * (16 * SEG);
-    // segment g of the 2 row octets: global byte g * 128 of each row, LDS group g
-    dma16<0 * SEG, 0 * GROUP_BYTES>(src[0], dst);
-    dma16<0 * SEG, 0 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<1 * SEG, 1 * GROUP_BYTES>(src[0], dst);
-    dma16<1 * SEG, 1 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<2 * SEG, 2 * GROUP_BYTES>(src[0], dst);
-    dma16<2 * SEG, 2 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<3 * SEG, 3 * GROUP_BYTES>(src[0], dst);
-    dma16<3 * SEG, 3 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<4 * SEG, 4 * GROUP_BYTES>(src[0], dst);
-    dma16<4 * SEG, 4 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<5 * SEG, 5 * GROUP_BYTES>(src[0], dst);
-    dma16<5 * SEG, 5 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<6 * SEG, 6 * GROUP_BYTES>(src[0], dst);
-    dma16<6 * SEG, 6 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<7 * SEG, 7 * GROUP_BYTES>(src[0], dst);
-    dma16<7 * SEG, 7 * GROUP_BYTES + 1024>(src[1], dst);
-    dma16<8 * SEG, 8 * GROUP_BYTES>(src[0], dst);
-    dma16<8 * SEG, 8 * GROUP_BYTES + 1024>(src[1], dst);
+    // segment k of the 2 row octets: global byte k * 128 of each row, LDS group k
+    dma16<0 * SEG, 0 * GROUP_BYTES>(g.a[0], dst);
+    dma16<0 * SEG, 0 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<1 * SEG, 1 * GROUP_BYTES>(g.a[0], dst);
+    dma16<1 * SEG, 1 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<2 * SEG, 2 * GROUP_BYTES>(g.a[0], dst);
+    dma16<2 * SEG, 2 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<3 * SEG, 3 * GROUP_BYTES>(g.a[0], dst);
+    dma16<3 * SEG, 3 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<4 * SEG, 4 * GROUP_BYTES>(g.a[0], dst);
+    dma16<4 * SEG, 4 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<5 * SEG, 5 * GROUP_BYTES>(g.a[0], dst);
+    dma16<5 * SEG, 5 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<6 * SEG, 6 * GROUP_BYTES>(g.a[0], dst);
+    dma16<6 * SEG, 6 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<7 * SEG, 7 * GROUP_BYTES>(g.a[0], dst);
+    dma16<7 * SEG, 7 * GROUP_BYTES + 1024>(g.a[1], dst);
+    dma16<8 * SEG, 8 * GROUP_BYTES>(g.a[0], dst);
+    dma16<8 * SEG, 8 * GROUP_BYTES + 1024>(g.a[1], dst);
   };
 
   // Entries are fetched two tiles ahead of their gather and every gather is followed by
@@ -270,7 +280,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   {
     const int32_t e0 = read_entry(0);
     vmask_nxt = __ballot(valid(e0));
-    issue(0, e0);
+    gather(0, gather_src(e0));
   }
   fetch_entries(2);
 
@@ -310,19 +320,40 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   // P exchange: block of wave w, half j (k-step 2vv(w) + j) at xp[(2w + j) * 64 + lane] as 4 dwords
   i32x4* xpv = reinterpret_cast<i32x4*>(xp);
 
+  // V^T fragment reads of k-step ks from tile tb (see the PV step below)
+  auto load_v = [&](const unsigned char* tb, int ks, bf16x8* dst) {
+    const int rb = 32 * (ks >> 1) + 16 * (ks & 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int off = (db >> 1) * GROUP_BYTES + rb * SEG;
+      union {
+        i16x4 h[2];
+        bf16x8 b;
+      } a;
+      a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(tb + voff[0][db & 1] + off));
+      a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(tb + voff[1][db & 1] + off));
+      dst[db] = a.b;
+    }
+  };
+  int* xflag = reinterpret_cast<int*>(xmax + 4 * 32);
+
   for (int i = 0; i < ntiles; ++i) {
     const int bf = i & 1;
     tile_barrier();  // tile i is in LDS for every wave; buffer bf^1 is free
     const uint64_t vmask = vmask_nxt;
-    if (i + 1 < ntiles) {
+    const bool more = i + 1 < ntiles;
+    GatherSrc gnext;
+    if (more) {
       const int32_t e_next = read_entry(i + 1);
       vmask_nxt = __ballot(valid(e_next));
-      issue(bf ^ 1, e_next);
-      fetch_entries(i + 3);
+      gnext = gather_src(e_next);
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;
 
-    // ---- S^T for own 32 kv rows x 32 heads; K fragments read one group of 4 steps ahead
+    // ---- S^T for own 32 kv rows x 32 heads; the next tile's gather is issued after the
+    // first group of matrix-core steps, so that these start as soon as possible
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -331,21 +362,33 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       auto kfrag = [&](int st) -> bf16x8 {
         return *reinterpret_cast<const bf16x8*>(tb + koff[st & 3] + (st >> 2) * GROUP_BYTES);
       };
-      bf16x8 kf[2][KG];
+      constexpr int NG = MROW / 16 / KG;  // 9 groups of 4 steps, read two groups ahead
+      bf16x8 kf[3][KG];
 #pragma unroll
-      for (int u = 0; u < KG; ++u) kf[0][u] = kfrag(u);
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int g = 0; g < MROW / 16 / KG; ++g) {
-        if (g + 1 < MROW / 16 / KG) {
+        for (int u = 0; u < KG; ++u) kf[g][u] = kfrag(KG * g + u);
 #pragma unroll
-          for (int u = 0; u < KG; ++u) kf[(g + 1) & 1][u] = kfrag(KG * (g + 1) + u);
+      for (int g = 0; g < NG; ++g) {
+        if (g + 2 < NG) {
+#pragma unroll
+          for (int u = 0; u < KG; ++u) kf[(g + 2) % 3][u] = kfrag(KG * (g + 2) + u);
         }
 #pragma unroll
         for (int u = 0; u < KG; ++u)
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g & 1][u], qf[KG * g + u], s, 0, 0, 0);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g % 3][u], qf[KG * g + u], s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        if (g == 0 && more) {
+          gather(bf ^ 1, gnext);
+          fetch_entries(i + 3);
+        }
       }
     }
+    // the first two k-steps of V^T are read while the softmax runs
+    bf16x8 vf[3][4];
+    load_v(tb, 0, vf[0]);
+    load_v(tb, 1, vf[1]);
+
     float mx = -__builtin_inff();
     if (vmask != ~0ull) {  // partial tile: mask rows without a valid index
 #pragma unroll
@@ -362,12 +405,32 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (lg == 0) xmax[wave * 32 + lr] = mx;
+
+    // P of the own block against the running max.  A wave whose tile maximum exceeds the
+    // running max of one of its heads by more than 2^8 raises a flag; the flags travel
+    // with the P blocks, and only when one is raised (the first tile, or a jump of the
+    // maximum) do all waves exchange tile maxima, rescale and recompute P.
+    uint32_t own[8];
+    auto make_p = [&]() {
+      const float m_own = hh ? m1 : m0;
+      const float m_use = m_own == -__builtin_inff() ? 0.f : m_own;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        xpv[(2 * wave + j) * 64 + lane] = i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]};
+    };
+    make_p();
+    const uint64_t need = __ballot(mx > (hh ? m1 : m0) + RESCALE_LOG2);
+    if (lane == 0) xflag[wave] = need != 0ull;
     lds_barrier();
-    // tile maxima of head lr of each half (waves 0, 2 hold half 0; waves 1, 3 half 1)
-    const float mt0 = fmaxf(xmax[lr], xmax[64 + lr]);
-    const float mt1 = fmaxf(xmax[32 + lr], xmax[96 + lr]);
-    if (__ballot(mt0 > m0 + RESCALE_LOG2 || mt1 > m1 + RESCALE_LOG2)) {
+    if (xflag[0] | xflag[1] | xflag[2] | xflag[3]) {  // the same in every wave
+      if (lg == 0) xmax[wave * 32 + lr] = mx;
+      lds_barrier();
+      // tile maxima of head lr of each half (waves 0, 2 hold half 0; waves 1, 3 half 1)
+      const float mt0 = fmaxf(xmax[lr], xmax[64 + lr]);
+      const float mt1 = fmaxf(xmax[32 + lr], xmax[96 + lr]);
       const float n0 = fmaxf(m0, mt0), n1 = fmaxf(m1, mt1);
       const float a0 = n0 == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m0 - n0);
       const float a1 = n1 == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m1 - n1);
@@ -379,58 +442,32 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
         scale_agpr(acc[db][0], a0);
         scale_agpr(acc[db][1], a1);
       }
+      make_p();
+      lds_barrier();
     }
-    const float m_own = hh ? m1 : m0;
-    const float m_use = m_own == -__builtin_inff() ? 0.f : m_own;
-    uint32_t own[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      xpv[(2 * wave + j) * 64 + lane] = i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]};
     {
       float ls = 0.f;  // the probabilities actually used, as rounded to bf16
 #pragma unroll
       for (int r = 0; r < 8; ++r) ls += __uint_as_float(own[r] << 16) + __uint_as_float(own[r] & 0xffff0000u);
       l_part += ls;
     }
-    lds_barrier();
 
     // ---- O^T[dims 128wave + 32db][heads 32hb] += V^T . P^T over the tile's 4 k-steps of
     // 16 rows; k-step ks uses C-layout values 8(ks%2) .. +7 of the S^T block of rows
-    // 32(ks/2) .. +32.  The 8 V^T reads of step ks+1 are issued while step ks's MFMAs run.
+    // 32(ks/2) .. +32 (the P^T fragments of every wave's block, own included).  The V^T
+    // reads of step ks+2 are issued while step ks's matrix-core steps run.
     {
-      // P^T fragments of all 4 k-steps x 2 head halves (every wave's block, own included)
       auto p_frag = [&](int ks, int hb) -> bf16x8 {
         return __builtin_bit_cast(bf16x8, xpv[(2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane]);
       };
-      bf16x8 vf[2][4];
-      auto load_v = [&](int ks, bf16x8* dst) {
-        const int rb = 32 * (ks >> 1) + 16 * (ks & 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int off = (db >> 1) * GROUP_BYTES + rb * SEG;
-          union {
-            i16x4 h[2];
-            bf16x8 b;
-          } a;
-          a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tb + voff[0][db & 1] + off));
-          a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(tb + voff[1][db & 1] + off));
-          dst[db] = a.b;
-        }
-      };
-      load_v(0, vf[0]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 p0 = p_frag(ks, 0), p1 = p_frag(ks, 1);
-        if (ks + 1 < 4) load_v(ks + 1, vf[(ks + 1) & 1]);
+        if (ks + 2 < 4) load_v(tb, ks + 2, vf[(ks + 2) % 3]);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks & 1][db], p0, acc[db][0], 0, 0, 0);
-          acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks & 1][db], p1, acc[db][1], 0, 0, 0);
+          acc[db][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks % 3][db], p0, acc[db][0], 0, 0, 0);
+          acc[db][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks % 3][db], p1, acc[db][1], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
