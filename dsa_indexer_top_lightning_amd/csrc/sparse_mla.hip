@@ -246,27 +246,46 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     return g;
   };
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
-  auto gather = [&](int bf, const GatherSrc& g) {
+  // part k (0..5) of a tile's gather: three of its 18 copies (segment m of row octet q is
+  // copy 2m + q: global byte m * 128 of each row, LDS group m)
+  auto gather_part = [&](int k, int bf, const GatherSrc& g) {
     const uint32_t dst = smem_lds + bf * TILE_BYTES + wv * (16 * SEG);
-    // segment k of the 2 row octets: global byte k * 128 of each row, LDS group k
-    dma16<0 * SEG, 0 * GROUP_BYTES>(g.a[0], dst);
-    dma16<0 * SEG, 0 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<1 * SEG, 1 * GROUP_BYTES>(g.a[0], dst);
-    dma16<1 * SEG, 1 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<2 * SEG, 2 * GROUP_BYTES>(g.a[0], dst);
-    dma16<2 * SEG, 2 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<3 * SEG, 3 * GROUP_BYTES>(g.a[0], dst);
-    dma16<3 * SEG, 3 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<4 * SEG, 4 * GROUP_BYTES>(g.a[0], dst);
-    dma16<4 * SEG, 4 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<5 * SEG, 5 * GROUP_BYTES>(g.a[0], dst);
-    dma16<5 * SEG, 5 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<6 * SEG, 6 * GROUP_BYTES>(g.a[0], dst);
-    dma16<6 * SEG, 6 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<7 * SEG, 7 * GROUP_BYTES>(g.a[0], dst);
-    dma16<7 * SEG, 7 * GROUP_BYTES + 1024>(g.a[1], dst);
-    dma16<8 * SEG, 8 * GROUP_BYTES>(g.a[0], dst);
-    dma16<8 * SEG, 8 * GROUP_BYTES + 1024>(g.a[1], dst);
+    switch (k) {
+      case 0:
+        dma16<0 * SEG, 0 * GROUP_BYTES>(g.a[0], dst);
+        dma16<0 * SEG, 0 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<1 * SEG, 1 * GROUP_BYTES>(g.a[0], dst);
+        break;
+      case 1:
+        dma16<1 * SEG, 1 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<2 * SEG, 2 * GROUP_BYTES>(g.a[0], dst);
+        dma16<2 * SEG, 2 * GROUP_BYTES + 1024>(g.a[1], dst);
+        break;
+      case 2:
+        dma16<3 * SEG, 3 * GROUP_BYTES>(g.a[0], dst);
+        dma16<3 * SEG, 3 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<4 * SEG, 4 * GROUP_BYTES>(g.a[0], dst);
+        break;
+      case 3:
+        dma16<4 * SEG, 4 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<5 * SEG, 5 * GROUP_BYTES>(g.a[0], dst);
+        dma16<5 * SEG, 5 * GROUP_BYTES + 1024>(g.a[1], dst);
+        break;
+      case 4:
+        dma16<6 * SEG, 6 * GROUP_BYTES>(g.a[0], dst);
+        dma16<6 * SEG, 6 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<7 * SEG, 7 * GROUP_BYTES>(g.a[0], dst);
+        break;
+      default:
+        dma16<7 * SEG, 7 * GROUP_BYTES + 1024>(g.a[1], dst);
+        dma16<8 * SEG, 8 * GROUP_BYTES>(g.a[0], dst);
+        dma16<8 * SEG, 8 * GROUP_BYTES + 1024>(g.a[1], dst);
+        break;
+    }
+  };
+  auto gather = [&](int bf, const GatherSrc& g) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) gather_part(k, bf, g);
   };
 
   // Entries are fetched two tiles ahead of their gather and every gather is followed by
@@ -352,8 +371,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;
 
-    // ---- S^T for own 32 kv rows x 32 heads; the next tile's gather is issued after the
-    // first group of matrix-core steps, so that these start as soon as possible
+    // ---- S^T for own 32 kv rows x 32 heads
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -378,9 +396,13 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
         for (int u = 0; u < KG; ++u)
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[g % 3][u], qf[KG * g + u], s, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if (g == 0 && more) {
-          gather(bf ^ 1, gnext);
-          fetch_entries(i + 3);
+        // the next tile's gather, three copies after each of the first six groups (issued
+        // in one burst the copies fill the global-to-LDS path and stall the issuing
+        // waves), then the entry copy, which must stay the newest global load for the
+        // vmcnt(1) of the next tile barrier
+        if (g < 6 && more) {
+          gather_part(g, bf ^ 1, gnext);
+          if (g == 5) fetch_entries(i + 3);
         }
       }
     }
@@ -437,10 +459,12 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       l_part *= hh ? a1 : a0;
       m0 = n0;
       m1 = n1;
+      if (i > 0) {  // before the first tile's P the accumulators are still zero
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        scale_agpr(acc[db][0], a0);
-        scale_agpr(acc[db][1], a1);
+        for (int db = 0; db < 4; ++db) {
+          scale_agpr(acc[db][0], a0);
+          scale_agpr(acc[db][1], a1);
+        }
       }
       make_p();
       lds_barrier();
