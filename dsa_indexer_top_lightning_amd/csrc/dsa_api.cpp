@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -101,6 +102,12 @@ dsa_status check_mla_ptrs(const dsa_shape* s, const void* q, const void* kv, con
   return DSA_OK;
 }
 
+dsa_status check_sm_scale(float sm_scale) {
+  if (!(sm_scale > 0.f) || !std::isfinite(sm_scale))
+    return fail(DSA_ERR_INVALID_ARG, "sm_scale must be a positive finite number (got %g)", (double)sm_scale);
+  return DSA_OK;
+}
+
 size_t topk_ws(const dsa_shape* s) { return dsa::topk_workspace_bytes(s->B, s->T, s->topk, s->s_cap); }
 size_t mla_ws(const dsa_shape* s, dsa_dtype dt) {
   return dsa::mla_workspace_bytes(s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, (dsa::Dtype)dt);
@@ -181,6 +188,7 @@ dsa_status dsa_sparse_mla_attention(const dsa_shape* s, dsa_dtype dt, const void
                                     size_t ws_bytes, void* stream) {
   dsa_status st = check_mla_shape(s, dt);
   if (st == DSA_OK) st = check_mla_ptrs(s, q, kv, out);
+  if (st == DSA_OK) st = check_sm_scale(sm_scale);
   if (st != DSA_OK) return st;
   if (rows_of(s) > 0 && !idx) return fail(DSA_ERR_INVALID_ARG, "topk_indices must be non-NULL");
   const size_t need = mla_ws(s, dt);
@@ -197,6 +205,7 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
                              dsa_group_stats* stats, void* stream) {
   // ---- every check first: a failing call enqueues nothing
   dsa_status st = check_common(s);
+  if (st == DSA_OK) st = check_sm_scale(sm_scale);
   if (st != DSA_OK) return st;
   if (n_layers < 0) return fail(DSA_ERR_INVALID_ARG, "n_layers=%d", n_layers);
   if (n_layers > 0 && (!types || !layers)) return fail(DSA_ERR_INVALID_ARG, "indexer_types and layers must be non-NULL");

@@ -109,7 +109,8 @@ dsa_status dsa_topk_select(const dsa_shape* shape, const float* scores, int64_t 
  *     out[b,t,h,:] = sum_j p_j kv[b,idx_j,:Dc],     lse[b,t,h] = log sum_j exp(z_j)
  * over the entries idx_j of topk_indices[b,t,:] that lie in [0, s_cap); other
  * entries (-1 padding) are skipped.  A row with no valid entry gives out = 0 and
- * lse = -inf.  Each listed entry counts once per occurrence.
+ * lse = -inf.  Each listed entry counts once per occurrence.  sm_scale must be a
+ * positive finite number (DSA_ERR_INVALID_ARG otherwise).
  *   q    [B,T,Hm,Dc+Dr] mla_dtype     kv  [B,s_cap,Dc+Dr] mla_dtype
  *   out  [B,T,Hm,Dc]    mla_dtype     lse [B,T,Hm] fp32 or NULL
  * Arithmetic: fp32 softmax and accumulation; bf16 MFMA for bf16 with Dc == 512,

@@ -134,6 +134,14 @@ def test_group_argument_errors(L):
     assert cache.valid == 0 and cache.donor_layer == -1
 
 
+def test_sparse_mla_rejects_bad_softmax_scale(L):
+    d = _shape(B=1, T=1, s_cap=64, topk=64, Hm=64, Dc=512, Dr=64)
+    f = L.dsa_sparse_mla_attention
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        assert f(C.byref(d), b.BF16, FAKE, FAKE, FAKE, bad, FAKE, None, None, 0, None) == 1
+        assert "sm_scale" in b.last_error()
+
+
 def test_topk_workspace_only_for_few_long_rows(L):
     # few rows over a long prefix are chunked over workgroups and need histogram space
     long_rows = _shape(B=4, T=1, s_cap=1 << 20, topk=2048)
