@@ -189,7 +189,10 @@ def test_sparse_mla_full_selection_equals_dense_causal():
     for t in range(48):
         idx[0, t, :t + 1] = np.arange(t + 1)
     out = torch.empty((1, 48, 64, 512), device="cuda", dtype=torch.bfloat16)
-    b.sparse_mla_attention(to_dev(q, "bf16"), to_dev(kv, "bf16"), i32_dev(idx), w.sm_scale, out, Dc=512)
+    shape = b.make_shape(1, 48, 48, topk=64, Hm=64, Dc=512, Dr=64)
+    ws = torch.empty(max(b.workspace_bytes(shape, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+    b.sparse_mla_attention(to_dev(q, "bf16"), to_dev(kv, "bf16"), i32_dev(idx), w.sm_scale, out, Dc=512,
+                           workspace=ws)
     q64, kv64 = O.decode(q, "bf16"), O.decode(kv, "bf16")
     qq = torch.from_numpy(q64[0]).permute(1, 0, 2)[None]
     kk = torch.from_numpy(kv64[0])[None, None].expand(1, 64, 48, 576)
