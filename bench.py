@@ -153,10 +153,12 @@ def main():
     dev = upload(w, inputs, torch)
     ke_host, ks_host = w.key_end(), w.key_start()
     ke = torch.from_numpy(ke_host).cuda()
+    ks = torch.from_numpy(ks_host).cuda() if ks_host.any() else None
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
     types = ["full" if c == "F" else "shared" for c in w.layers]
-    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr, key_end=ke)
+    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
+                         key_start=ks, key_end=ke)
     ws = torch.empty(max(B.workspace_bytes(shape, B.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
     cache = B.IndexCache(w.B, w.T, w.topk)
     mdt = B.F32 if w.mla_dtype == "f32" else B.BF16

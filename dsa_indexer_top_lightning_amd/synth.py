@@ -19,6 +19,10 @@ Input recipe (the workloads of the pages, restated as shapes):
     fp8 as OCP e4m3fn codes with one float32 scale per (token, head) vector of
     D values, ``scale = float32(amax / 448)``, codes by round-to-nearest-even
     with saturation at +-448.
+  * Packed variable-length batch (``seqlens``): B = 1 and the sequences lie end to
+    end on the token axis; a query sees the keys of its own sequence up to itself
+    ([first token of its sequence, its position]) and RoPE positions restart at 0 in
+    every sequence.
   * Planted keys (1M-context decode workload): a Bernoulli(p) subset of key
     positions gets ``k += gamma * sqrt(D) * u_h`` with gamma ~ U(0.5, 1.5) and
     u_h the unit index query of head h (Hk == H) or of sum_h w_h q_h (Hk == 1),
@@ -67,6 +71,13 @@ class Workload:
     seed: int
     rope: bool = False
     plant_frac: float = 0.0
+    seqlens: tuple = ()    # packed variable-length batch: sequence lengths laid end to end (B == 1)
+
+    def __post_init__(self):
+        if self.seqlens:
+            n = int(sum(self.seqlens))
+            if self.B != 1 or self.pos0 != 0 or self.T != n or self.S != n or min(self.seqlens) < 1:
+                raise ValueError("a packed batch has B = 1, pos0 = 0 and T = S = sum(seqlens), every length >= 1")
 
     @property
     def n_layers(self) -> int:
@@ -86,14 +97,32 @@ class Workload:
         ke = np.minimum(self.pos0 + t + 1, self.S)
         return np.broadcast_to(ke, (self.B, self.T)).astype(np.int32).copy()
 
+    def seq_offsets(self) -> np.ndarray:
+        """Packed batch: first packed position of each token's sequence, int64 [T]."""
+        cu = np.concatenate([[0], np.cumsum(self.seqlens)]).astype(np.int64)
+        return np.repeat(cu[:-1], self.seqlens)
+
     def key_start(self) -> np.ndarray:
+        """Start of every query's candidate range, int32 [B, T]: 0, or in a packed batch the
+        first token of the query's own sequence (causal attention stays inside it)."""
+        if self.seqlens:
+            return self.seq_offsets().astype(np.int32)[None].copy()
         return np.zeros((self.B, self.T), np.int32)
+
+    def positions(self, r0: int, r1: int, queries: bool) -> np.ndarray:
+        """Positions of tokens [r0, r1) used by RoPE: absolute (queries start at pos0), or in a
+        packed batch the position inside the token's own sequence."""
+        if self.seqlens:
+            return np.arange(r0, r1) - self.seq_offsets()[r0:r1]
+        return (self.pos0 if queries else 0) + np.arange(r0, r1)
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
 
 
-# The five workloads (shapes from the pages' settings: 4096-token synthetic
+PACKED_SEQLENS = (3000, 2049, 2048, 1500, 1000, 700, 511, 300, 256, 255, 129, 100, 65, 64, 33, 17, 9, 1)
+
+# The workloads (shapes from the pages' settings: 4096-token synthetic
 # pre-training sequences, index_topk 2048, 1M context, MLA latent 512 + 64).
 WORKLOADS = {
     "tiny_prefill256_fp32": Workload(
@@ -108,6 +137,12 @@ WORKLOADS = {
     "chunk128k_fp8": Workload(
         "chunk128k_fp8", B=1, T=4096, S=131072, pos0=126976, layers="FSSS", H=32, D=128,
         Hk=32, topk=2048, Hm=64, Dc=512, Dr=64, idx_dtype="fp8", mla_dtype="bf16", seed=3),
+    # packed variable-length batch (the pages' RL-rollout / thd layout): 18 sequences end to
+    # end, from a single token to longer than index_topk, so that many rows pad with -1
+    "packed_varlen_bf16": Workload(
+        "packed_varlen_bf16", B=1, T=sum(PACKED_SEQLENS), S=sum(PACKED_SEQLENS), pos0=0, layers="FSS", H=32,
+        D=128, Hk=32, topk=2048, Hm=64, Dc=512, Dr=64, idx_dtype="bf16", mla_dtype="bf16", seed=5, rope=True,
+        seqlens=PACKED_SEQLENS),
     "decode1m_b4_fp8": Workload(
         "decode1m_b4_fp8", B=4, T=1, S=1048576, pos0=1048575, layers="FSSS", H=32, D=128,
         Hk=32, topk=2048, Hm=64, Dc=512, Dr=64, idx_dtype="fp8", mla_dtype="bf16", seed=4,
@@ -212,7 +247,7 @@ def index_q_rows(w: Workload, layer: int, b: int, t0: int, t1: int):
     """Index queries of rows [t0, t1): float64 values [rows, H, D] before storage rounding."""
     x = draw_rows(w.seed, TID_IDX_Q, layer, b, t0, t1, w.H * w.D).reshape(-1, w.H, w.D).astype(np.float64)
     if w.rope:
-        x = rope_last_half(x, w.pos0 + np.arange(t0, t1))
+        x = rope_last_half(x, w.positions(t0, t1, True))
     return x
 
 
@@ -237,7 +272,7 @@ def index_k_rows(w: Workload, layer: int, b: int, s0: int, s1: int):
     """Index keys of positions [s0, s1): float64 [rows, Hk, D] before storage rounding."""
     x = draw_rows(w.seed, TID_IDX_K, layer, b, s0, s1, w.Hk * w.D).reshape(-1, w.Hk, w.D).astype(np.float64)
     if w.rope:
-        x = rope_last_half(x, np.arange(s0, s1))
+        x = rope_last_half(x, w.positions(s0, s1, False))
     if w.plant_frac > 0:
         u = draw_rows(w.seed, TID_PLANT_POS, layer, b, s0, s1, 1, kind="uniform")[:, 0]
         g = draw_rows(w.seed, TID_PLANT_GAMMA, layer, b, s0, s1, 1, kind="uniform")[:, 0]

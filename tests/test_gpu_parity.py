@@ -340,6 +340,64 @@ def test_group_is_deterministic_and_shared_layers_match_standalone():
         assert torch.equal(o, outs[l])
 
 
+def test_group_packed_varlen_sampled_rows():
+    # packed variable-length batch: per-query [start of own sequence, position] ranges,
+    # sequences from 1 token to longer than index_topk (many rows padded with -1)
+    w = synth.WORKLOADS["packed_varlen_bf16"]
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    cache, stats = _run_group(w, dev, i32_dev(w.key_end()), ks_dev=i32_dev(w.key_start()))
+    assert (stats.n_full, stats.n_shared) == (1, 2)
+    idx = cache.indices.cpu().numpy()
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)])
+    ts = set()
+    for i, n in enumerate(w.seqlens):
+        ts |= {int(cu[i]), int(cu[i] + n - 1), int(cu[i] + n // 2)}
+    ts |= set(np.random.default_rng(1).integers(0, w.T, 12).tolist())
+    rows = [(0, t) for t in sorted(ts)]
+    _check_group(w, inputs, dev, {0: idx}, rows)
+    ks, ke = w.key_start()[0], w.key_end()[0]
+    for _, t in rows:   # every kept index inside the row's own sequence, -1 padding after
+        n = min(int(ke[t] - ks[t]), w.topk)
+        r = idx[0, t]
+        assert ((r[:n] >= ks[t]) & (r[:n] < ke[t])).all() and (r[n:] == -1).all()
+
+
+def test_group_decode_graph_capture_replays_match_eager():
+    # a decode step captured once as a HIP graph and replayed: chunked top-k over 20,000-key
+    # rows and split sparse MLA with its combine pass; every replay (with eager work and a
+    # synchronisation between replays) must reproduce the eager results bit for bit
+    w = _wl(B=4, T=1, S=20000, pos0=19999, layers="FSSF", topk=2048)
+    inputs = synth.build_inputs(w)
+    dev = _upload_group(w, inputs)
+    types = ["full" if c == "F" else "shared" for c in w.layers]
+    ke = i32_dev(w.key_end())
+    shape = b.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
+                         key_end=ke)
+    ws = torch.empty(max(b.workspace_bytes(shape, b.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
+    cache = b.IndexCache(w.B, w.T, w.topk)
+    b.group_forward(shape, b.BF16, types, dev, w.sm_scale, cache, 1, ws)
+    torch.cuda.synchronize()
+    eager = [d["out"].clone() for d in dev]
+    eager_idx = cache.indices.clone()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            b.group_forward(shape, b.BF16, types, dev, w.sm_scale, cache, 1, ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for d in dev:
+            d["out"].fill_(float(rep + 1))
+        cache.indices.fill_(-5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(cache.indices, eager_idx), f"replay {rep}: indices"
+        for l, d in enumerate(dev):
+            assert torch.equal(d["out"], eager[l]), f"replay {rep}: layer {l}"
+
+
 def test_group_prefill4k_full_size_sampled_rows():
     w = synth.WORKLOADS["prefill4k_bf16"]
     inputs = synth.build_inputs(w)

@@ -1,5 +1,6 @@
 """The seeded input generator: storage codecs against torch's, block regeneration."""
 import numpy as np
+import pytest
 import torch
 
 from dsa_indexer_top_lightning_amd import synth
@@ -76,3 +77,22 @@ def test_workload_key_ranges():
     assert ke.shape == (1, 4096) and ke[0, 0] == 126977 and ke[0, -1] == 131072
     d = synth.WORKLOADS["decode32k_b64_bf16"].key_end()
     assert d.shape == (64, 1) and (d == 32768).all()
+
+
+def test_packed_batch_key_ranges_and_positions():
+    w = synth.WORKLOADS["packed_varlen_bf16"]
+    ks, ke = w.key_start()[0].astype(np.int64), w.key_end()[0].astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(w.seqlens)])
+    for i, n in enumerate(w.seqlens):
+        o = cu[i]
+        assert (ks[o:o + n] == o).all()                          # range starts at its sequence
+        assert np.array_equal(ke[o:o + n], np.arange(o + 1, o + n + 1))   # causal inside it
+        assert np.array_equal(w.positions(o, o + n, True), np.arange(n))  # RoPE restarts
+    assert (ke - ks >= 1).all() and ke[-1] == w.S
+    assert ((ke - ks) < w.topk).sum() > w.T // 3                  # many rows pad with -1
+    assert {1, w.topk, w.topk + 1} <= set(int(x) for x in w.seqlens)
+
+
+def test_packed_batch_shape_is_checked():
+    with pytest.raises(ValueError):
+        synth.WORKLOADS["packed_varlen_bf16"].with_(B=2)
