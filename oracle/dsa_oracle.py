@@ -342,3 +342,96 @@ def group_stats(types, key_start, key_end, *, H, D, Hk, idx_bytes, idx_scaled, t
                                           + rows * Hm * Dc * mla_bytes)),
         "batch": B,
     }
+
+
+# ------------------------------------------------------------------ decode-step preparation
+# The steps a decode step applies to new index vectors before they are scored:
+# Megatron-Bridge GLM-5 DSA pull request, commit on the indexer RoPE half swap (the
+# rotated dims are the LAST qk_pos_emb_head_dim = D/2 of each index head), its config
+# fix (rope_theta = 8e6), and fp8 e4m3 storage with one fp32 scale per vector.
+# Reading: rotate-half pairs (i, i + D/4) inside the rope part turn by
+# pos * theta^(-2i / (D/2)); the rotated vector is a float32 tensor (the value a
+# projection in float32 would hold); fp8 storage takes scale = float32(amax / 448)
+# (1 when amax is 0) and codes = nearest e4m3fn value of float32(y / scale), ties to
+# the even code, magnitudes above 448 saturated; bf16 storage rounds to nearest even.
+
+
+def rope_last_half(x: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE of the last D/2 dims of every vector of x [N, heads, D], float64."""
+    x = np.asarray(x, dtype=np.float64)
+    D = x.shape[-1]
+    r = D // 2
+    half = r // 2
+    inv = float(theta) ** (-(2.0 * np.arange(half)) / r)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv[None, :]      # [N, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a = x[..., D - r:D - r + half]
+    b = x[..., D - r + half:]
+    y = x.copy()
+    y[..., D - r:D - r + half] = a * c - b * s
+    y[..., D - r + half:] = b * c + a * s
+    return y
+
+
+def encode_e4m3(v32: np.ndarray) -> np.ndarray:
+    """float32 values -> e4m3fn codes: the nearest finite e4m3fn value (ties to the even
+    code, i.e. even mantissa), magnitudes above 448 saturated to 448."""
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    grid = E4M3FN[:127]                       # codes 0..126: the non-negative finite values, ascending
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(grid, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = grid[hi] - a
+    d_lo = a - grid[lo]
+    take_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(take_lo, lo, hi).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 7)
+
+
+def encode_bf16(v32: np.ndarray) -> np.ndarray:
+    """float32 values (finite) -> bf16 bit patterns: keep the top 16 bits of the float32,
+    rounding the dropped 16 bits to nearest, ties to an even kept part."""
+    u = np.asarray(v32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    top = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((top & 1) == 1))
+    return (top + up).astype(np.uint16)
+
+
+def quantize_e4m3_f32(y32: np.ndarray):
+    """float32 vectors [..., D] -> (e4m3fn codes, float32 scale per vector)."""
+    y = np.asarray(y32, dtype=np.float32)
+    amax = np.max(np.abs(y), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return encode_e4m3((y / scale[..., None]).astype(np.float32)), scale
+
+
+def prep_index_vectors(x32: np.ndarray, pos: np.ndarray, theta: float, dtype: str):
+    """New index vectors [N, heads, D] float32 -> stored values after RoPE:
+    bf16 bit patterns (scale None) or (e4m3fn codes, scales [N, heads])."""
+    y = rope_last_half(x32, pos, theta).astype(np.float32)
+    if dtype == "bf16":
+        return encode_bf16(y), None
+    if dtype == "fp8":
+        return quantize_e4m3_f32(y)
+    raise ValueError(dtype)
+
+
+def cache_append(k_cache, k_scale, kv_cache, k_new, pos, rows, theta, dtype, kv_new=None):
+    """Decode-step append: returns new (k_cache, k_scale, kv_cache) with token n's prepared
+    index key at row rows[n] and its latent row copied there; rows outside the cache are
+    skipped.  Caches are flat over rows: k [rows, Hk, D], scales [rows, Hk], kv [rows, R]."""
+    k_cache = np.array(k_cache, copy=True)
+    k_scale = None if k_scale is None else np.array(k_scale, copy=True)
+    kv_cache = None if kv_cache is None else np.array(kv_cache, copy=True)
+    vals, sc = prep_index_vectors(k_new, pos, theta, dtype)
+    for n, r in enumerate(np.asarray(rows, dtype=np.int64)):
+        if not 0 <= r < k_cache.shape[0]:
+            continue
+        k_cache[r] = vals[n]
+        if sc is not None:
+            k_scale[r] = sc[n]
+        if kv_cache is not None and kv_new is not None:
+            kv_cache[r] = kv_new[n]
+    return k_cache, k_scale, kv_cache

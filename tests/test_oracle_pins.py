@@ -355,3 +355,110 @@ def test_group_stats_closed_forms_causal_prefill():
     assert st["attn_flops"] == 4 * 2 * 2 * (2 * 8 + 4) * sum_j
     assert st["topk_bytes"] == 4 * sum_n + 4 * T * k
     assert (st["n_full"], st["n_shared"]) == (1, 3)
+
+
+# ------------------------------------------------------------------ decode-step preparation
+
+def test_e4m3_encoder_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if not np.isnan(O.E4M3FN[c])], np.uint8)
+    vals = O.E4M3FN[codes].astype(np.float32)
+    got = O.encode_e4m3(vals)
+    zero = vals == 0                          # -0.0 and +0.0 keep their sign bit
+    assert np.array_equal(got[~zero], codes[~zero])
+    assert np.array_equal(got[zero], codes[zero])
+
+
+def test_e4m3_encoder_matches_torch_cast_in_range():
+    # library routine: torch's float32 -> float8_e4m3fn cast (round to nearest even) on
+    # random values, exact midpoints between neighbouring codes and subnormals, |x| <= 464
+    rng = np.random.default_rng(4)
+    vals = np.concatenate([
+        rng.standard_normal(20000) * 40.0,
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 5000),
+        (O.E4M3FN[0:126] + O.E4M3FN[1:127]) / 2.0,          # midpoints
+        -(O.E4M3FN[0:126] + O.E4M3FN[1:127]) / 2.0,
+        np.array([464.0, -464.0, 448.0]),
+    ]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 464.0]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3(vals), ref)
+
+
+def test_e4m3_encoder_saturates_and_flushes():
+    v = np.array([449.0, 500.0, 1e30, -1e30, 2.0 ** -10, -(2.0 ** -10), 1.5 * 2.0 ** -10], np.float32)
+    assert O.encode_e4m3(v).tolist() == [126, 126, 126, 254, 0, 128, 1]
+
+
+def test_bf16_encoder_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.standard_normal(50000).astype(np.float32) * 3,
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, 65504.0], np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.encode_bf16(v), ref)
+
+
+def test_rope_rotates_the_last_half_by_position():
+    # unit vector on the first rope dim (index D - D/2) at position p: it turns into the
+    # pair (D - D/2, D - D/4) by angle p (the pair's frequency is theta^0 = 1); the first
+    # half of the vector is untouched
+    D, p = 8, 3
+    x = np.zeros((1, 1, D))
+    x[0, 0, 4] = 1.0
+    x[0, 0, 0] = 7.0
+    y = O.rope_last_half(x, np.array([p]), 1.0e4)[0, 0]
+    assert y[0] == 7.0 and np.allclose(y[1:4], 0)
+    assert np.isclose(y[4], math.cos(p)) and np.isclose(y[6], math.sin(p))
+    assert np.allclose(y[[5, 7]], 0)
+    # second pair turns with frequency theta^(-2/(D/2)) = theta^-0.5
+    x2 = np.zeros((1, 1, D))
+    x2[0, 0, 7] = 1.0
+    y2 = O.rope_last_half(x2, np.array([p]), 1.0e4)[0, 0]
+    a = p * 1.0e4 ** -0.5
+    assert np.isclose(y2[7], math.cos(a)) and np.isclose(y2[5], -math.sin(a))
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((5, 3, 16))
+    k = rng.standard_normal((5, 3, 16))
+    pos = np.array([0, 1, 17, 1000, 1048575])
+    assert np.allclose(O.rope_last_half(q, np.zeros(5), 8e6), q)                   # position 0
+    rq = O.rope_last_half(q, pos, 8e6)
+    assert np.allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(q, axis=-1))   # rotations
+    # relative positions: q at m + d and k at n + d score like q at m and k at n
+    d = 12345
+    s0 = (O.rope_last_half(q, pos, 8e6) * O.rope_last_half(k, pos[::-1], 8e6)).sum(-1)
+    s1 = (O.rope_last_half(q, pos + d, 8e6) * O.rope_last_half(k, pos[::-1] + d, 8e6)).sum(-1)
+    assert np.allclose(s0, s1)
+
+
+def test_fp32_quantisation_maps_the_largest_entry_to_448():
+    rng = np.random.default_rng(7)
+    y = (rng.standard_normal((10, 4, 128)) * rng.uniform(0.01, 100, (10, 4, 1))).astype(np.float32)
+    y[3, 2] = 0.0
+    codes, scale = O.quantize_e4m3_f32(y)
+    amax_pos = np.argmax(np.abs(y), axis=-1)
+    top = np.take_along_axis(codes, amax_pos[..., None], axis=-1)[..., 0] & 0x7F   # [10, 4]
+    nonzero = np.ones((10, 4), bool)
+    nonzero[3, 2] = False
+    assert (top[nonzero] == 126).all()                            # |y| = amax encodes as 448
+    assert scale[3, 2] == 1.0 and not codes[3, 2].any()
+    err = np.abs(O.E4M3FN[codes] * scale[..., None] - y)
+    step = np.maximum(np.abs(y), 2.0 ** -6 * scale[..., None]) * 2.0 ** -4 + 1e-30
+    assert (err <= step * (1 + 1e-6)).all()                       # half an e4m3 step, 3-bit mantissa
+
+
+def test_cache_append_writes_rows_and_skips_outside():
+    rng = np.random.default_rng(8)
+    N, Hk, D, R, rows_total = 3, 2, 16, 8, 6
+    kc = np.zeros((rows_total, Hk, D), np.uint8)
+    sc = np.ones((rows_total, Hk), np.float32)
+    kv = np.zeros((rows_total, R), np.uint16)
+    k_new = rng.standard_normal((N, Hk, D)).astype(np.float32)
+    kv_new = rng.integers(0, 65535, (N, R)).astype(np.uint16)
+    rows = np.array([4, -1, 6])                                    # -1 and 6 are outside
+    k2, s2, kv2 = O.cache_append(kc, sc, kv, k_new, np.array([5, 6, 7]), rows, 8e6, "fp8", kv_new)
+    codes, scales = O.prep_index_vectors(k_new, np.array([5, 6, 7]), 8e6, "fp8")
+    assert np.array_equal(k2[4], codes[0]) and np.array_equal(s2[4], scales[0]) and np.array_equal(kv2[4], kv_new[0])
+    untouched = [0, 1, 2, 3, 5]
+    assert not k2[untouched].any() and (s2[untouched] == 1).all() and not kv2[untouched].any()
