@@ -72,6 +72,10 @@ _SIGS = {
                                     C.c_void_p, C.POINTER(GroupStats), C.c_void_p]),
     "dsa_group_stats_compute": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int, C.c_int32, C.c_void_p, C.c_void_p,
                                           C.c_void_p, C.POINTER(GroupStats)]),
+    "dsa_index_prep": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dsa_latent_append": (C.c_int, [C.c_int32, C.c_int32, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
+                                    C.c_void_p]),
     "dsa_workspace_bytes": (C.c_size_t, [C.POINTER(Shape), C.c_int]),
     "dsa_status_string": (C.c_char_p, [C.c_int]),
     "dsa_last_error": (C.c_char_p, []),
@@ -185,6 +189,29 @@ def sparse_mla_attention(q, kv, topk_indices, sm_scale, out, lse=None, *, Dc, wo
                                           _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
                                           _dev_ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def index_prep(x, pos, out, out_scale=None, *, rows=None, rope_theta=8.0e6, stream=None):
+    """dsa_index_prep.  x [n, heads, D] fp32, pos [n] int32, out [n_rows, heads, D] (bf16 bits as
+    uint16/bfloat16, or e4m3fn codes as uint8/float8_e4m3fn), out_scale [n_rows, heads] fp32 (fp8)."""
+    n, heads, D = x.shape
+    if out.dtype in (torch.uint8, torch.float8_e4m3fn):
+        dt = FP8_E4M3
+    elif out.dtype in (torch.uint16, torch.int16, torch.bfloat16):
+        dt = BF16
+    else:
+        raise ValueError(f"unsupported out dtype {out.dtype}")
+    _check(lib().dsa_index_prep(n, heads, D, float(rope_theta), dt, _dev_ptr(x), _dev_ptr(pos), _dev_ptr(rows),
+                                out.shape[0], _dev_ptr(out), _dev_ptr(out_scale), _stream(stream)))
+    return out
+
+
+def latent_append(latent_new, rows, latent_cache, *, stream=None):
+    """dsa_latent_append.  latent_new [n, R] and latent_cache [n_rows, R], float32 or bf16."""
+    n, R = latent_new.shape
+    _check(lib().dsa_latent_append(n, R, dtype_code(latent_new), _dev_ptr(latent_new), _dev_ptr(rows),
+                                   latent_cache.shape[0], _dev_ptr(latent_cache), _stream(stream)))
+    return latent_cache
 
 
 class IndexCache:

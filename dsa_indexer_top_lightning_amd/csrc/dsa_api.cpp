@@ -332,4 +332,41 @@ dsa_status dsa_group_stats_compute(const dsa_shape* s, dsa_dtype idx_dtype, dsa_
   return DSA_OK;
 }
 
+dsa_status dsa_index_prep(int32_t n, int32_t heads, int32_t D, float rope_theta, dsa_dtype out_dtype,
+                          const float* x, const int32_t* pos, const int64_t* rows, int64_t n_rows, void* out,
+                          float* out_scale, void* stream) {
+  if (n < 0 || heads < 1 || n_rows < 0)
+    return fail(DSA_ERR_INVALID_ARG, "n=%d heads=%d n_rows=%lld: need n >= 0, heads >= 1, n_rows >= 0", n, heads,
+                (long long)n_rows);
+  if (D < 4 || D > 1024 || D % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "D=%d: need D %% 4 == 0, 4 <= D <= 1024", D);
+  if (!(rope_theta > 0.f) || !std::isfinite(rope_theta))
+    return fail(DSA_ERR_INVALID_ARG, "rope_theta must be a positive finite number (got %g)", (double)rope_theta);
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_INVALID_ARG, "out_dtype must be DSA_BF16 or DSA_FP8_E4M3 (got %d)", (int)out_dtype);
+  if (!rows && n_rows < n) return fail(DSA_ERR_INVALID_ARG, "without rows, n_rows=%lld must be >= n=%d",
+                                       (long long)n_rows, n);
+  if (n > 0 && (!x || !pos || !out)) return fail(DSA_ERR_INVALID_ARG, "x, pos and out must be non-NULL");
+  if (n > 0 && out_dtype == DSA_FP8_E4M3 && !out_scale)
+    return fail(DSA_ERR_INVALID_ARG, "fp8 storage needs out_scale");
+  const dsa::PrepParams p{n, heads, D, rope_theta, (int)out_dtype, x, pos, rows, n_rows, out, out_scale};
+  const hipError_t e = dsa::launch_index_prep(p, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "index prep launch");
+}
+
+dsa_status dsa_latent_append(int32_t n, int32_t R, dsa_dtype dtype, const void* latent_new, const int64_t* rows,
+                             int64_t n_rows, void* latent_cache, void* stream) {
+  if (n < 0 || R < 1 || n_rows < 0)
+    return fail(DSA_ERR_INVALID_ARG, "n=%d R=%d n_rows=%lld: need n >= 0, R >= 1, n_rows >= 0", n, R,
+                (long long)n_rows);
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "latent dtype must be DSA_F32 or DSA_BF16 (got %d)", (int)dtype);
+  const int row_bytes = R * (dtype == DSA_F32 ? 4 : 2);
+  if (row_bytes % 16 != 0) return fail(DSA_ERR_UNSUPPORTED, "a latent row of %d bytes is not a multiple of 16", row_bytes);
+  if (n > 0 && (!latent_new || !rows || !latent_cache))
+    return fail(DSA_ERR_INVALID_ARG, "latent_new, rows and latent_cache must be non-NULL");
+  const dsa::LatentAppendParams p{n, row_bytes, latent_new, rows, n_rows, latent_cache};
+  const hipError_t e = dsa::launch_latent_append(p, (hipStream_t)stream);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "latent append launch");
+}
+
 }  // extern "C"

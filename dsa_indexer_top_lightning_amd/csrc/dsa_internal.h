@@ -46,6 +46,29 @@ struct MlaParams {
   float* lse;
 };
 
+// New index vectors x [n, heads, D] fp32 -> RoPE -> out rows (bf16 or fp8 codes + scales).
+struct PrepParams {
+  int n, heads, D;
+  float theta;
+  int out_dtype;            // BF16 or FP8
+  const float* x;
+  const int32_t* pos;       // [n]
+  const int64_t* rows;      // [n] destination rows, or NULL (row = n)
+  int64_t n_rows;           // rows of out; destinations outside [0, n_rows) are skipped
+  void* out;                // [n_rows, heads, D]
+  float* out_scale;         // [n_rows, heads] (fp8)
+};
+
+// New latent rows src [n, row_bytes] -> dst rows.
+struct LatentAppendParams {
+  int64_t n;
+  int row_bytes;            // multiple of 16
+  const void* src;
+  const int64_t* rows;
+  int64_t n_rows;
+  void* dst;
+};
+
 // Each launcher assumes its arguments were validated by the host layer.
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches);
 size_t topk_workspace_bytes(int B, int T, int topk, int64_t s_cap);
@@ -54,6 +77,8 @@ bool mla_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);
 size_t mla_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt);
 hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
                              int* n_launches);
+hipError_t launch_index_prep(const PrepParams& p, hipStream_t st);
+hipError_t launch_latent_append(const LatentAppendParams& p, hipStream_t st);
 
 // Dynamic LDS above 64 KiB must be allowed per kernel.  `high` remembers the
 // largest size already allowed for that kernel; a failure is returned and the

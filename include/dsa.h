@@ -211,6 +211,41 @@ dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
                                    const int32_t* key_start_host, const int32_t* key_end_host,
                                    dsa_group_stats* out);
 
+/*
+ * Decode-step preparation of new index vectors (the Megatron-Bridge pull request's
+ * commit on the indexer RoPE half swap: the LAST D/2 dims of every index head are
+ * rotated; rope_theta = 8e6 in its config fix).  For each vector x[i, h, :] (fp32,
+ * before RoPE), rotate-half pairs (j, j + D/4) of the last D/2 dims turn by
+ * pos[i] * rope_theta^(-2j/(D/2)) (angle in double precision), the result is rounded
+ * to fp32 and stored at row rows[i] (row i when rows is NULL) as
+ *   DSA_BF16       round to nearest even, or
+ *   DSA_FP8_E4M3   scale = amax/448 (1 if amax is 0), codes e4m3fn(y/scale) rounded to
+ *                  nearest even and saturated at 448; the scale goes to out_scale.
+ * Serves both the queries of a step (rows NULL) and the append of new keys to the
+ * index-key cache (rows = cache rows, e.g. b * s_cap + slot).
+ *   x         [n, heads, D] fp32          pos [n] int32 (position in the sequence)
+ *   rows      [n] int64 or NULL; rows outside [0, n_rows) are skipped; two entries that
+ *             name one row race (the row ends up holding either vector)
+ *   out       [n_rows, heads, D] bf16 or e4m3fn codes
+ *   out_scale [n_rows, heads] fp32 (fp8 only)
+ * Requires D % 4 == 0, 4 <= D <= 1024, rope_theta > 0 finite; NaN inputs give
+ * unspecified codes.  DSA_ERR_INVALID_ARG on bad sizes, types or NULL pointers.
+ */
+dsa_status dsa_index_prep(int32_t n, int32_t heads, int32_t D, float rope_theta, dsa_dtype out_dtype,
+                          const float* x, const int32_t* pos, const int64_t* rows, int64_t n_rows,
+                          void* out, float* out_scale, void* stream);
+
+/*
+ * Append new latent rows (kv_lora_rank + rope = Dc + Dr values, the latent row of the
+ * sparse MLA call) of a decode step to the latent cache: latent_new[i, :] is copied to
+ * latent_cache[rows[i], :]; rows outside [0, n_rows) are skipped, and two entries
+ * that name one row race.
+ *   latent_new [n, R], latent_cache [n_rows, R], dtype DSA_F32 or DSA_BF16; a row must
+ *   be a multiple of 16 bytes (DSA_ERR_UNSUPPORTED otherwise).
+ */
+dsa_status dsa_latent_append(int32_t n, int32_t R, dsa_dtype dtype, const void* latent_new,
+                             const int64_t* rows, int64_t n_rows, void* latent_cache, void* stream);
+
 /* Device scratch a call needs (bytes, 0 if none).  Pure host function; returns 0
  * for an invalid shape. */
 size_t dsa_workspace_bytes(const dsa_shape* shape, dsa_op op);

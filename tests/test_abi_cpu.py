@@ -179,3 +179,29 @@ def test_group_stats_match_oracle_counts(types, idx_dt, mla_dt):
     assert (st.n_full, st.n_shared) == (ref["n_full"], ref["n_shared"])
     for key in ("indexer_flops", "indexer_bytes", "topk_bytes", "attn_flops", "attn_bytes"):
         assert getattr(st, key) == pytest.approx(ref[key], rel=1e-12), key
+
+
+def test_index_prep_and_latent_append_validation(L):
+    f = L.dsa_index_prep
+    ok = dict(n=2, heads=4, D=128, theta=8e6, dt=b.FP8_E4M3, x=FAKE, pos=FAKE, rows=None, n_rows=2, out=FAKE,
+              scale=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["n"], a["heads"], a["D"], a["theta"], a["dt"], a["x"], a["pos"], a["rows"], a["n_rows"],
+                 a["out"], a["scale"], None)
+
+    assert call(D=130) == 1 and call(D=0) == 1 and call(D=2048) == 1
+    assert call(theta=0.0) == 1 and call(theta=float("nan")) == 1
+    assert call(dt=b.F32) == 1
+    assert call(scale=None) == 1                        # fp8 needs scales
+    assert call(x=None) == 1 and call(pos=None) == 1 and call(out=None) == 1
+    assert call(n_rows=1) == 1                          # rows NULL: n_rows >= n
+    assert call(heads=0) == 1 and call(n=-1) == 1
+    assert call(n=0, x=None, pos=None, out=None, scale=None) == 0     # nothing to do
+    g = L.dsa_latent_append
+    assert g(2, 0, b.BF16, FAKE, FAKE, 10, FAKE, None) == 1
+    assert g(2, 4, b.BF16, FAKE, FAKE, 10, FAKE, None) == 2          # 8-byte rows
+    assert g(2, 576, b.FP8_E4M3, FAKE, FAKE, 10, FAKE, None) == 1
+    assert g(2, 576, b.BF16, None, FAKE, 10, FAKE, None) == 1
+    assert g(0, 576, b.BF16, None, None, 0, None, None) == 0
