@@ -18,6 +18,11 @@
 //     order) `rem` keys == tau, writing each kept position to its slot found by
 //     wavefront ballots + popcount prefix sums and a cross-wave prefix in LDS.
 //
+// Many rows longer than that cache (a long-context prefill chunk) read each row twice:
+// a histogram of the top digit, then a pass that marks every position above the k-th
+// key's digit in an LDS bitmap and keeps the keys sharing that digit in LDS, where the
+// select finishes; the output is written in order from the bitmaps.
+//
 // Few long rows (decode over a long prefix) would leave most compute units idle
 // with one workgroup per row, so there each row is cut into chunks of 8192 keys,
 // one 256-thread workgroup per chunk, and the same radix select runs as a chain
@@ -45,75 +50,65 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask, int lane) {
   return (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
 }
 
-template <bool CACHE>
-__global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
-  extern __shared__ uint32_t kcache[];
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wcnt[2][TK_WAVES];
-  __shared__ uint32_t sh_digit, sh_rem;
+// Wave 0: in the 2048-bin histogram `hist` (digits of the candidates that match the
+// prefix so far), find the digit holding the rem-th largest candidate and that
+// candidate's rank among the keys with this digit (written to *digit, *rank).  The total
+// count must be >= rem.  Callers synchronise before and after.
+__device__ __forceinline__ void hist_find(const uint32_t* hist, uint32_t rem, uint32_t* digit, uint32_t* rank) {
+  const int lane = threadIdx.x & 63;
+  // lane L owns digits [32L, 32L+32); suffix sums over lanes
+  uint32_t c = 0;
+  for (int d = 0; d < 32; ++d) c += hist[32 * lane + d];
+  uint32_t x = c;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t v = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += v;
+  }
+  // x = number of candidates with digit >= 32*lane; non-increasing in lane
+  const uint64_t ge = __ballot(x >= rem);
+  const int L = __popcll(ge) - 1;  // last lane whose suffix reaches rem (>= 0: total >= rem)
+  if (lane == L) {
+    uint32_t above = x - c;
+    int d = 32 * lane + 31;
+    for (; d > 32 * lane; --d) {
+      const uint32_t h = hist[d];
+      if (above + h >= rem) break;
+      above += h;
+    }
+    *digit = (uint32_t)d;
+    *rank = rem - above;
+  }
+}
 
+struct SelectLds {
+  uint32_t* hist;                  // [2048]
+  uint32_t (*wcnt)[TK_WAVES];      // [2][TK_WAVES]
+  uint32_t* sh;                    // [2]: digit, rank
+};
+
+// Radix passes `first`..2 over key_at(i), i in [0, n) (prefix / pmask / rem carry the
+// digits fixed by earlier passes), then the ordered pass that writes every key > tau and
+// the first `rem` keys == tau, in position order, to out[0..K).
+template <class KeyAt>
+__device__ void finish_select(KeyAt key_at, int64_t n, int64_t ks, int K, int32_t* out, int first, uint32_t prefix,
+                              uint32_t pmask, uint32_t rem, const SelectLds& L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row = blockIdx.x;
-  int64_t ks, ke;
-  clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
-  const int64_t n = ke - ks;
-  const int K = p.topk;
-  int32_t* out = p.out + row * (int64_t)K;
-
-  if (n <= K) {
-    for (int i = tid; i < K; i += TK_THREADS) out[i] = (i < n) ? (int32_t)(ks + i) : -1;
-    return;
-  }
-  const float* src = p.scores + row * p.ld + ks;
-  if constexpr (CACHE) {
-    for (int64_t i = tid; i < n; i += TK_THREADS) kcache[i] = order_key(src[i]);
-    __syncthreads();
-  }
-  auto key_at = [&](int64_t i) -> uint32_t {
-    if constexpr (CACHE) return kcache[i];
-    else return order_key(src[i]);
-  };
-
-  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)K;
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = first; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass < 2 ? 2047u : 1023u;
-    for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+    for (int i = tid; i < 2048; i += TK_THREADS) L.hist[i] = 0;
     __syncthreads();
     for (int64_t i = tid; i < n; i += TK_THREADS) {
       const uint32_t key = key_at(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&L.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    if (wave == 0) {
-      // lane L owns digits [32L, 32L+32); suffix sums over lanes
-      uint32_t c = 0;
-      for (int d = 0; d < 32; ++d) c += hist[32 * lane + d];
-      uint32_t x = c;
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t v = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += v;
-      }
-      // x = number of candidates with digit >= 32*lane; non-increasing in lane
-      const uint64_t ge = __ballot(x >= rem);
-      const int L = __popcll(ge) - 1;  // last lane whose suffix reaches rem (>= 0: total >= rem)
-      if (lane == L) {
-        uint32_t above = x - c;
-        int d = 32 * lane + 31;
-        for (; d > 32 * lane; --d) {
-          const uint32_t h = hist[d];
-          if (above + h >= rem) break;
-          above += h;
-        }
-        sh_digit = (uint32_t)d;
-        sh_rem = rem - above;
-      }
-    }
+    if (wave == 0) hist_find(L.hist, rem, &L.sh[0], &L.sh[1]);
     __syncthreads();
-    prefix |= sh_digit << shift;
+    prefix |= L.sh[0] << shift;
     pmask |= dmask << shift;
-    rem = sh_rem;
+    rem = L.sh[1];
     __syncthreads();
   }
   const uint32_t tau = prefix;  // the k-th largest key; `rem` keys equal to it are kept
@@ -126,22 +121,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
     const bool gt = in && key > tau;
     const bool eq = in && key == tau;
     const uint64_t meq = __ballot(eq);
-    if (lane == 0) wcnt[0][wave] = (uint32_t)__popcll(meq);
+    if (lane == 0) L.wcnt[0][wave] = (uint32_t)__popcll(meq);
     __syncthreads();
     uint32_t eq_before = base_eq, eq_total = 0;
     for (int w = 0; w < TK_WAVES; ++w) {
-      const uint32_t v = wcnt[0][w];
+      const uint32_t v = L.wcnt[0][w];
       eq_total += v;
       if (w < wave) eq_before += v;
     }
     eq_before += lane_prefix(meq, lane);
     const bool sel = gt || (eq && eq_before < rem);
     const uint64_t msel = __ballot(sel);
-    if (lane == 0) wcnt[1][wave] = (uint32_t)__popcll(msel);
+    if (lane == 0) L.wcnt[1][wave] = (uint32_t)__popcll(msel);
     __syncthreads();
     uint32_t sel_before = base_sel, sel_total = 0;
     for (int w = 0; w < TK_WAVES; ++w) {
-      const uint32_t v = wcnt[1][w];
+      const uint32_t v = L.wcnt[1][w];
       sel_total += v;
       if (w < wave) sel_before += v;
     }
@@ -153,6 +148,274 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
   }
 }
 
+template <bool CACHE>
+__global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
+  extern __shared__ uint32_t kcache[];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wcnt[2][TK_WAVES];
+  __shared__ uint32_t sh[2];
+
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  int64_t ks, ke;
+  clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
+  const int64_t n = ke - ks;
+  const int K = p.topk;
+  int32_t* out = p.out + row * (int64_t)K;
+
+  if (n <= K) {
+    for (int i = tid; i < K; i += TK_THREADS) out[i] = (i < n) ? (int32_t)(ks + i) : -1;
+    return;
+  }
+  const float* src = p.scores + row * p.ld + ks;
+  const SelectLds L{hist, wcnt, sh};
+  if constexpr (CACHE) {
+    for (int64_t i = tid; i < n; i += TK_THREADS) kcache[i] = order_key(src[i]);
+    __syncthreads();
+    finish_select([&](int64_t i) { return kcache[i]; }, n, ks, K, out, 0, 0u, 0u, (uint32_t)K, L);
+  } else {
+    finish_select([&](int64_t i) { return order_key(src[i]); }, n, ks, K, out, 0, 0u, 0u, (uint32_t)K, L);
+  }
+}
+
+// ----------------------------------------------------------------- long rows, many of them
+// Rows longer than the LDS key cache (and enough of them to fill the chip).  A 512-thread
+// workgroup per row, two per compute unit, so that one row's scans overlap the other's
+// reads.  Histogram passes over the row fix its top digits (11 bits, then 11, then 10)
+// until the digit holding the k-th key has at most LG_CAP keys (one pass on smooth
+// score distributions).  One more pass then marks in an LDS bitmap every position whose
+// fixed digits lie above that bin and copies the keys inside the bin, with their
+// positions, into LDS, where the remaining digits are resolved.  Keys > tau are marked,
+// keys == tau go to a second bitmap, and the kept positions are written in ascending
+// order by a block scan over the bitmap words (the first `rem` of the == tau keys).
+constexpr int LG_THREADS = 512;
+constexpr int LG_WAVES = LG_THREADS / 64;
+constexpr int64_t LG_MAX_KEYS = 262144;  // bitmap capacity: 2 x 32 KiB
+constexpr int LG_CAP = 4096;             // keys of the k-th key's bin held in LDS
+constexpr int LG_REP = 4;                // copies of a histogram (2048 * LG_REP <= 2 * LG_CAP)
+
+size_t long_lds_bytes(int64_t s_cap) {
+  const int64_t words = (s_cap + 31) / 32;
+  return (size_t)(2 * words + 2 * LG_CAP) * 4;
+}
+
+__host__ __device__ constexpr int lg_shift(int level) { return level == 0 ? 21 : (level == 1 ? 10 : 0); }
+__host__ __device__ constexpr uint32_t lg_mask(int level) { return level < 2 ? 2047u : 1023u; }
+
+// f(i, key) for every i in [0, n), key = order_key(src[i]); the aligned body of the row
+// is read with 16-byte loads, U per thread in flight.  REVERSE walks the body from its
+// end, so that a pass that follows another starts on the part of the row read last
+// (the part most likely still in L2).
+template <bool REVERSE, class F>
+__device__ __forceinline__ void for_each_key(const float* src, int64_t n, F&& f) {
+  const int tid = threadIdx.x;
+  const int64_t head = min<int64_t>(n, (int64_t)(((16u - ((uint32_t)(uintptr_t)src & 15u)) & 15u) >> 2));
+  if (tid < head) f((int64_t)tid, order_key(src[tid]));
+  const float4* body = reinterpret_cast<const float4*>(src + head);
+  const int64_t nv = (n - head) >> 2;
+  constexpr int U = 8;
+  constexpr int64_t STEP = (int64_t)U * LG_THREADS;
+  const int64_t full = nv / STEP;  // whole steps of U loads per thread
+  for (int64_t c = 0; c < full; ++c) {
+    const int64_t v = (REVERSE ? (full - 1 - c) : c) * STEP + tid;
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = body[v + u * LG_THREADS];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = head + 4 * (v + u * LG_THREADS);
+      f(i, order_key(x[u].x));
+      f(i + 1, order_key(x[u].y));
+      f(i + 2, order_key(x[u].z));
+      f(i + 3, order_key(x[u].w));
+    }
+  }
+  for (int64_t v = full * STEP + tid; v < nv; v += LG_THREADS) {
+    const float4 x = body[v];
+    const int64_t i = head + 4 * v;
+    f(i, order_key(x.x));
+    f(i + 1, order_key(x.y));
+    f(i + 2, order_key(x.z));
+    f(i + 3, order_key(x.w));
+  }
+  const int64_t t = head + 4 * nv + tid;  // at most 3 tail keys
+  if (t < n) f(t, order_key(src[t]));
+}
+
+// exclusive prefix sum of v over the workgroup (wsum: LG_WAVES words of LDS)
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t before = x - v;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  __syncthreads();
+  return before;
+}
+
+// the == tau positions of bitmap word x that are kept, given e_before of them earlier in the row
+__device__ __forceinline__ uint32_t take_equal(uint32_t x, uint32_t e_before, uint32_t rem) {
+  if (e_before >= rem) return 0u;
+  uint32_t need = rem - e_before;
+  if ((uint32_t)__popc(x) <= need) return x;
+  uint32_t t = 0u;
+  for (; need > 0; --need) {
+    const uint32_t low = x & (0u - x);
+    t |= low;
+    x ^= low;
+  }
+  return t;
+}
+
+__global__ __launch_bounds__(LG_THREADS) void topk_long(TopkParams p, int map_words) {
+  extern __shared__ uint32_t lds[];
+  uint32_t* selmap = lds;
+  uint32_t* eqmap = lds + map_words;
+  uint32_t* ckey = lds + 2 * map_words;
+  uint32_t* cpos = ckey + LG_CAP;
+  uint32_t* rhist = ckey;  // the candidate area holds the replicated histograms until the marking pass
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wsum[2][LG_WAVES];
+  __shared__ uint32_t sh[3];
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  int64_t ks, ke;
+  clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
+  const int64_t n = ke - ks;
+  const int K = p.topk;
+  int32_t* out = p.out + row * (int64_t)K;
+  if (n <= K) {
+    for (int i = tid; i < K; i += LG_THREADS) out[i] = (i < n) ? (int32_t)(ks + i) : -1;
+    return;
+  }
+  const float* src = p.scores + row * p.ld + ks;
+
+  // histogram passes over the row until the k-th key's bin is small enough; lanes add to
+  // copy tid % LG_REP so that lanes with one digit mostly hit different LDS banks
+  uint32_t prefix = 0, pmask = 0, rem = (uint32_t)K, binc = 0;
+  int level = 0;
+  const uint32_t rep = (uint32_t)(tid % LG_REP);
+#pragma unroll 1
+  do {
+    const int shift = lg_shift(level);
+    const uint32_t dmask = lg_mask(level);
+    for (int i = tid; i < 2048 * LG_REP; i += LG_THREADS) rhist[i] = 0;
+    __syncthreads();
+    auto add = [&](int64_t, uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&rhist[((key >> shift) & dmask) * LG_REP + rep], 1u);
+    };
+    if (level & 1) for_each_key<true>(src, n, add);
+    else for_each_key<false>(src, n, add);
+    __syncthreads();
+    for (int i = tid; i < 2048; i += LG_THREADS) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int r = 0; r < LG_REP; ++r) c += rhist[i * LG_REP + r];
+      hist[i] = c;
+    }
+    __syncthreads();
+    if (wave == 0) hist_find(hist, rem, &sh[0], &sh[1]);
+    __syncthreads();
+    prefix |= sh[0] << shift;
+    pmask |= dmask << shift;
+    rem = sh[1];
+    binc = hist[sh[0]];
+    ++level;
+    __syncthreads();
+  } while (binc > (uint32_t)LG_CAP && level < 3);
+
+  // marking pass: keys above the bin into the bitmap, keys inside it into LDS (or, with
+  // every digit fixed, straight into the == tau bitmap)
+  const int W = (int)((n + 31) >> 5);
+  for (int w = tid; w < W; w += LG_THREADS) {
+    selmap[w] = 0u;
+    eqmap[w] = 0u;
+  }
+  if (tid == 0) sh[2] = 0u;
+  __syncthreads();
+  const bool collect = level < 3;
+  auto mark = [&](int64_t i, uint32_t key) {
+    const uint32_t kp = key & pmask;
+    if (kp > prefix) {
+      atomicOr(&selmap[i >> 5], 1u << (i & 31));
+    } else if (kp == prefix) {
+      if (collect) {
+        const uint32_t j = atomicAdd(&sh[2], 1u);
+        if (j < (uint32_t)LG_CAP) {
+          ckey[j] = key;
+          cpos[j] = (uint32_t)i;
+        }
+      } else {
+        atomicOr(&eqmap[i >> 5], 1u << (i & 31));
+      }
+    }
+  };
+  if (level & 1) for_each_key<true>(src, n, mark);
+  else for_each_key<false>(src, n, mark);
+  __syncthreads();
+
+  if (collect) {
+    // the remaining digits among the binc collected keys
+#pragma unroll 1
+    for (int lv = level; lv < 3; ++lv) {
+      const int shift = lg_shift(lv);
+      const uint32_t dmask = lg_mask(lv);
+      for (int i = tid; i < 2048; i += LG_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (uint32_t j = tid; j < binc; j += LG_THREADS) {
+        const uint32_t key = ckey[j];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) hist_find(hist, rem, &sh[0], &sh[1]);
+      __syncthreads();
+      prefix |= sh[0] << shift;
+      pmask |= dmask << shift;
+      rem = sh[1];
+      __syncthreads();
+    }
+    const uint32_t tau = prefix;
+    for (uint32_t j = tid; j < binc; j += LG_THREADS) {
+      const uint32_t key = ckey[j], i = cpos[j];
+      if (key > tau) atomicOr(&selmap[i >> 5], 1u << (i & 31));
+      else if (key == tau) atomicOr(&eqmap[i >> 5], 1u << (i & 31));
+    }
+    __syncthreads();
+  }
+
+  // emit: thread t owns bitmap words [t*wpt, (t+1)*wpt)
+  const int wpt = (W + LG_THREADS - 1) / LG_THREADS;
+  const int w0 = min(W, tid * wpt), w1 = min(W, w0 + wpt);
+  uint32_t e = 0;
+  for (int w = w0; w < w1; ++w) e += (uint32_t)__popc(eqmap[w]);
+  const uint32_t e_first = block_excl_scan(e, wsum[0]);
+  uint32_t cnt = 0, er = e_first;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = eqmap[w];
+    cnt += (uint32_t)__popc(selmap[w] | take_equal(x, er, rem));
+    er += (uint32_t)__popc(x);
+  }
+  uint32_t slot = block_excl_scan(cnt, wsum[1]);
+  er = e_first;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t x = eqmap[w];
+    uint32_t m = selmap[w] | take_equal(x, er, rem);
+    er += (uint32_t)__popc(x);
+    while (m) {
+      const int bit = __ffs(m) - 1;
+      if (slot < (uint32_t)K) out[slot] = (int32_t)(ks + 32 * (int64_t)w + bit);
+      ++slot;
+      m &= m - 1u;
+    }
+  }
+}
 
 // ----------------------------------------------------------------- split rows
 constexpr int SP_THREADS = 256;
@@ -423,6 +686,12 @@ hipError_t launch_topk(const TopkParams& p, void* ws, size_t ws_bytes, hipStream
     const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(topk_rows<true>), lds, high);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(topk_rows<true>, dim3((unsigned)rows), dim3(TK_THREADS), lds, st, p);
+  } else if (p.s_cap <= LG_MAX_KEYS) {
+    const size_t lds = long_lds_bytes(p.s_cap);
+    static std::atomic<size_t> high{0};
+    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void*>(topk_long), lds, high);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(topk_long, dim3((unsigned)rows), dim3(LG_THREADS), lds, st, p, (int)((p.s_cap + 31) / 32));
   } else {
     hipLaunchKernelGGL(topk_rows<false>, dim3((unsigned)rows), dim3(TK_THREADS), 0, st, p);
   }

@@ -91,7 +91,10 @@ TOPK_CASES = [
     ((1, 3), 70001, 2048, "zeros"),
     ((1, 7), 20000, 512, "mixed"),
     ((4, 1), 1 << 20, 2048, "normal"),   # 1M-key rows
-    ((1, 512), 40000, 2048, "normal"),   # many rows longer than the LDS key cache
+    ((1, 512), 40000, 2048, "normal"),   # many rows longer than the LDS key cache: two reads per row
+    ((1, 520), 70001, 1000, "mixed"),    # odd row length (unaligned rows), ties at the k-th key
+    ((2, 300), 50001, 2048, "ties"),     # the k-th key's digit holds too many keys: HBM passes
+    ((1, 512), 36000, 2048, "zeros"),
 ]
 
 
