@@ -222,8 +222,9 @@ __global__ __launch_bounds__(256) void indexer_mfma(IndexerParams p) {
 }
 
 // ----------------------------------------------------------------- prefill tile kernel
-// A workgroup owns a 128-query x 128-key tile of one batch item; wave (wm, wn) owns
-// the 64 x 64 block [64wm, +64) x [64wn, +64) (2 x 2 MFMA tiles of 32 x 32).  For
+// A workgroup of 8 waves (two per SIMD, so one wave's LDS reads and epilogue run
+// under the other's MFMAs) owns a 128-query x 128-key tile of one batch item; wave
+// (wm, wn) owns the 64 x 32 block [64wm, +64) x [32wn, +32) (2 MFMA tiles of 32 x 32).  For
 // each head the Q_h and K_g tiles, the head weights (and fp8 scales) are gathered
 // straight into LDS with global_load_lds into one of two alternating stages, so the
 // loads of head h+1 run under the contraction of head h.  Each wave load moves 8
@@ -234,6 +235,8 @@ __global__ __launch_bounds__(256) void indexer_mfma(IndexerParams p) {
 // live in a ring of three LDS stages so that epilogue can still read them.
 constexpr int PQ = 128;  // queries per tile
 constexpr int PK = 128;  // keys per tile
+constexpr int TILE_WAVES = 8;
+constexpr int TILE_THREADS = 64 * TILE_WAVES;
 
 template <int DT>
 struct TileCfg {
@@ -242,15 +245,18 @@ struct TileCfg {
   static constexpr int SEG_BYTES = 128 * 128;      // one segment of the 128 rows
   static constexpr int TILE = SEGS * SEG_BYTES;    // 32 KiB bf16, 16 KiB fp8
   static constexpr int STAGE = 2 * TILE;            // Q and K tiles of one head
+  // tile stages in flight: copies run NSTAGE - 1 heads ahead of the contraction
+  static constexpr int NSTAGE = (DT == BF16) ? 2 : 4;
+  static constexpr int NVSTAGE = NSTAGE + 1;        // vector stages (the epilogue lags one head)
   static constexpr int VEC = 128 * 4;               // one fp32 per row
   static constexpr int W_OFF = 0;                   // w          (in a vector stage)
   static constexpr int QS_OFF = VEC;                // q scale    (fp8)
   static constexpr int KS_OFF = 2 * VEC;            // k scale    (fp8)
   static constexpr int VSTAGE = 3 * VEC;
-  static constexpr int VBASE = 2 * STAGE;           // 3 vector stages follow the 2 tile stages
-  static constexpr int LDS = 2 * STAGE + 3 * VSTAGE;
+  static constexpr int VBASE = NSTAGE * STAGE;      // the vector stages follow the tile stages
+  static constexpr int LDS = NSTAGE * STAGE + NVSTAGE * VSTAGE;
   static constexpr int LOADS = 2 * SEGS * 16;       // wave loads per stage: 2 tiles x segments x 16 row octets
-  static constexpr int DMA_PER_WAVE = LOADS / 4;
+  static constexpr int DMA_PER_WAVE = LOADS / TILE_WAVES;
 };
 
 // 16-byte chunk u (0..7) of row r's segment is stored at chunk u ^ tperm(r)
@@ -259,70 +265,110 @@ __device__ __forceinline__ int tperm(int r) {
   return ((j & 1) << 2) | (j & 2) | ((j >> 2) & 1);
 }
 
+// Global-to-LDS copies of the tile kernel, issued as inline asm: written with the
+// compiler's builtin they are LDS stores that the compiler cannot tell apart from the
+// stage being read, so every later LDS read would wait for all of them (vmcnt(0)) and the
+// next head's copies could not run under this head's MFMAs.  They are ordered by the
+// memory clobber and waited for explicitly at the head barrier.  M0 (set one wait state
+// before the load reads it) holds the LDS address; lane i's data lands at M0 + size * i.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void tile_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void tile_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Per-workgroup state and steps of indexer_tile (all inlined into the kernel).
 template <int DT>
 struct TileWork {
   using C = TileCfg<DT>;
+  static constexpr int KS = (DT == BF16) ? HD / 16 : HD / 64;  // MFMA k-steps per head
+  static constexpr int DPW = C::DMA_PER_WAVE;
   const IndexerParams& p;
   unsigned char* smem;
   int lane, wave, wv, b, t0, H, Hk, T;
   int64_t s0, s_cap;
   int wm, wn, lr, lg;
-  const unsigned char* qg;
-  const unsigned char* kg;
-  int64_t qrow, krow;
-  int qr0, qr1;
-  int64_t kr0, kr1;
-  f32x16 acc0[2][2], acc1[2][2];  // accumulators of even / odd heads: [row tile][col tile]
-  f32x16 tot[2][2];
+  uint32_t smem_lds;      // LDS address of smem
+  uint32_t dma_off;       // this wave's first tile copy inside a stage (its copies follow 1 KiB apart)
+  bool dma_k;             // this wave copies key rows (else query rows)
+  const unsigned char* dbase;      // first row of the tile this wave copies from (head 0)
+  uint32_t doff[DPW];              // per-lane byte offsets of this wave's copies from dbase
+  uint32_t abase, bbase;  // fragment addresses (k-step 0) of this lane's query and key rows in a stage
+  const float* vsrc;      // per-row vector (w, q scale or k scale) of head 0 for waves 0..2
+  int64_t vstride;        // its step per head
+  int vr0, vr1;           // its two rows
+  f32x16 acc0[2], acc1[2];  // accumulators of even / odd heads, one per 32-row tile
+  f32x16 tot[2];
 
-  // wave load j of a stage: tile j / (SEGS*16) (0 = Q, 1 = K), segment, row octet; lane i
+  // wave copy j of a stage: tile j / (SEGS*16) (0 = Q, 1 = K), segment, row octet; lane i
   // fills row 8*octet + i/8, stored chunk i%8 <- logical chunk (i%8) ^ tperm(row); rows
   // beyond T / s_cap load a valid row (their results are never written)
-  __device__ __forceinline__ const unsigned char* load_src(int j, int h, int g) const {
-    const int tile = j / (C::SEGS * 16), seg = (j / 16) % C::SEGS, oct = j % 16;
-    const int row = 8 * oct + (lane >> 3);
-    const int chunk = (lane & 7) ^ tperm(row);
-    if (tile == 0) {
-      const int64_t t = min(t0 + row, T - 1);
-      return qg + ((int64_t)b * T + t) * qrow + (int64_t)h * HD * C::ESZ + seg * 128 + chunk * 16;
+  __device__ __forceinline__ void setup(const unsigned char* qg, const unsigned char* kg, int64_t qrow, int64_t krow) {
+    smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    const int j0 = wv * DPW;
+    const int tile = j0 / (C::SEGS * 16);
+    dma_k = tile == 1;
+    dbase = dma_k ? kg + ((int64_t)b * s_cap + s0) * krow : qg + ((int64_t)b * T + t0) * qrow;
+    dma_off = tile * C::TILE + ((j0 / 16) % C::SEGS) * C::SEG_BYTES + (j0 % 16) * 1024;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i) {
+      const int j = j0 + i, seg = (j / 16) % C::SEGS, oct = j % 16;
+      const int row = 8 * oct + (lane >> 3);
+      const int chunk = (lane & 7) ^ tperm(row);
+      // (tile rows are < 128 and a row holds at most 64 heads of 256 bytes: fits 32 bits)
+      const int rr = dma_k ? (int)(min<int64_t>(s0 + row, s_cap - 1) - s0) : min(t0 + row, T - 1) - t0;
+      doff[i] = (uint32_t)(rr * (dma_k ? krow : qrow) + seg * 128 + chunk * 16);
     }
-    const int64_t sk = min<int64_t>(s0 + row, s_cap - 1);
-    return kg + ((int64_t)b * s_cap + sk) * krow + (int64_t)g * HD * C::ESZ + seg * 128 + chunk * 16;
+    // Fragment addresses.  Rows r and r + 32 share tperm(r), and a query row 64wm + 32i + lr
+    // and a key row 32wn + lr both have tperm(lr).  With the chunks of a k-step at bits
+    // above the lane's own chunk bits, the swizzled byte offset of k-step ks inside a
+    // 128-byte segment is the lane's base XOR (32 (bf16) or 64 (fp8)) * ks, plus 16 for the
+    // second fp8 chunk.
+    const uint32_t sw = DT == BF16 ? 16u * (uint32_t)(lg ^ tperm(lr)) : 16u * (uint32_t)((2 * lg) ^ tperm(lr));
+    abase = (uint32_t)(64 * wm + lr) * 128u + sw;
+    bbase = (uint32_t)C::TILE + (uint32_t)(32 * wn + lr) * 128u + sw;
+    // per-row vectors: wave 0 w, wave 1 q scale, wave 2 k scale (fp8)
+    vsrc = nullptr;
+    vstride = 0;
+    vr0 = vr1 = 0;
+    if (wv == 0) {
+      vsrc = p.w + (int64_t)b * T * H;
+      vstride = 1;
+      vr0 = min(t0 + lane, T - 1);
+      vr1 = min(t0 + 64 + lane, T - 1);
+    } else if (DT == FP8 && wv == 1) {
+      vsrc = p.q_scale + (int64_t)b * T * H;
+      vstride = 1;
+      vr0 = min(t0 + lane, T - 1);
+      vr1 = min(t0 + 64 + lane, T - 1);
+    } else if (DT == FP8 && wv == 2) {
+      vsrc = p.k_scale + (int64_t)b * s_cap * Hk;
+      vstride = (Hk == H) ? 1 : 0;
+      vr0 = (int)min<int64_t>(s0 + lane, s_cap - 1);
+      vr1 = (int)min<int64_t>(s0 + 64 + lane, s_cap - 1);
+    }
   }
 
-  // gather head h into tile stage st (K only if with_k) and its vectors into vector stage h % 3
-  __device__ __forceinline__ void issue(int h, int st, bool with_k) const {
-    unsigned char* base = smem + st * C::STAGE;
-    unsigned char* vbase = smem + C::VBASE + (h % 3) * C::VSTAGE;
-    const int g = (Hk == H) ? h : 0;
-#pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-      const int j = wv * C::DMA_PER_WAVE + i;
-      const int tile = j / (C::SEGS * 16), seg = (j / 16) % C::SEGS, oct = j % 16;
-      if (tile == 1 && !with_k) continue;
-      unsigned char* dst = base + tile * C::TILE + seg * C::SEG_BYTES + oct * 1024;
-      __builtin_amdgcn_global_load_lds(load_src(j, h, g), (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
-    }
-    // per-row vectors: wave 0 w, wave 1 q scale, wave 2 k scale (fp8)
-    if (wv == 0 || (DT == FP8 && wv < 3)) {
-      const float* vsrc;
-      int off;
-      if (wv == 0) {
-        vsrc = p.w + (int64_t)b * T * H + h;
-        off = C::W_OFF;
-      } else if (wv == 1) {
-        vsrc = p.q_scale + (int64_t)b * T * H + h;
-        off = C::QS_OFF;
-      } else {
-        vsrc = p.k_scale + (int64_t)b * s_cap * Hk + g;
-        off = C::KS_OFF;
-      }
-      const int64_t stride = (wv == 2) ? Hk : H;
-      const int64_t r0 = (wv == 2) ? kr0 : qr0, r1 = (wv == 2) ? kr1 : qr1;
-      __builtin_amdgcn_global_load_lds(vsrc + r0 * stride, (__attribute__((address_space(3))) void*)(vbase + off), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc + r1 * stride, (__attribute__((address_space(3))) void*)(vbase + off + 256), 4, 0, 0);
-    }
+  // copy i of head h into tile stage st (skipped for key rows of a shared key head)
+  __device__ __forceinline__ void copy_part(int i, int h, int st) const {
+    const int hh = dma_k ? ((Hk == H) ? h : 0) : h;
+    tile_dma16(dbase + (int64_t)hh * HD * C::ESZ, doff[i], smem_lds + st * C::STAGE + dma_off + i * 1024);
+  }
+
+  // head h's per-row vectors into vector stage h % NVSTAGE
+  __device__ __forceinline__ void copy_vectors(int h) const {
+    if (vsrc == nullptr) return;
+    const int64_t rs = (wv == 2) ? Hk : H;
+    const float* src = vsrc + (int64_t)h * vstride;
+    const int off = (wv == 0) ? C::W_OFF : (wv == 1 ? C::QS_OFF : C::KS_OFF);
+    const uint32_t dst = smem_lds + C::VBASE + (h % C::NVSTAGE) * C::VSTAGE + off;
+    tile_dma4(src + (int64_t)vr0 * rs, dst);
+    tile_dma4(src + (int64_t)vr1 * rs, dst + 256);
   }
 
   // 16-byte fragment of row r, logical chunk c: segment c / 8, stored chunk (c % 8) ^ tperm(r)
@@ -330,116 +376,173 @@ struct TileWork {
     return tile + (c >> 3) * C::SEG_BYTES + r * 128 + 16 * ((c & 7) ^ tperm(r));
   }
 
-  // ReLU * weight of head hh from accumulator set `acc`, weights / scales from its vector stage
-  __device__ __forceinline__ void epilogue(const f32x16 (&acc)[2][2], int hh) {
-    const unsigned char* vb = smem + C::VBASE + (hh % 3) * C::VSTAGE;
+  // elements [E0, E0 + NE) of the ReLU * weight epilogue of head hh (accumulators `acc`,
+  // weights / scales from its vector stage); element e is row tile e / 16, register e % 16
+  template <int E0, int NE>
+  __device__ __forceinline__ void epilogue_part(const f32x16 (&acc)[2], int hh) {
+    const unsigned char* vb = smem + C::VBASE + (hh % C::NVSTAGE) * C::VSTAGE;
     const float* wl = reinterpret_cast<const float*>(vb + C::W_OFF);
-    const float* ql = reinterpret_cast<const float*>(vb + C::QS_OFF);
     const float* kl = reinterpret_cast<const float*>(vb + C::KS_OFF);
+    float kc = 1.f;
+    if constexpr (DT == FP8) kc = kl[32 * wn + lr];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      float kc = 1.f;
-      if constexpr (DT == FP8) kc = kl[64 * wn + 32 * j + lr];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
-          float wv_ = wl[row];
-          if constexpr (DT == FP8) wv_ *= ql[row];
-          float v = acc[i][j][r];
-          if constexpr (DT == FP8) v *= kc;
-          tot[i][j][r] = fmaf(wv_, fmaxf(v, 0.f), tot[i][j][r]);
-        }
+    for (int e = E0; e < E0 + NE; ++e) {
+      const int i = e >> 4, r = e & 15;
+      const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * lg + (r & 3);
+      const float wv_ = wl[row];  // fp8: already times the query scale
+      float v = acc[i][r];
+      if constexpr (DT == FP8) v *= kc;
+      tot[i][r] = fmaf(wv_, fmaxf(v, 0.f), tot[i][r]);
     }
   }
 
-  // contraction of head h from tile stage st into `acc`: 2 x 2 tiles of 32 x 32 over D = 128
-  __device__ __forceinline__ void contract(f32x16 (&acc)[2][2], int st) const {
+  // k-step ks of head h's contraction (tile stage st) into `acc`; ab / bb_ are abase /
+  // bbase as seen by this head (kept opaque so the compiler forms each address when used)
+  __device__ __forceinline__ void kstep(int ks, f32x16 (&acc)[2], int st, uint32_t ab, uint32_t bb_) const {
     const unsigned char* qt = smem + st * C::STAGE;
-    const unsigned char* kt = ((Hk == H) ? qt : smem) + C::TILE;  // a shared key head stays in stage 0
+    const unsigned char* kt = (Hk == H) ? qt : smem;  // a shared key head stays in stage 0
+    if constexpr (DT == BF16) {
+      const uint32_t x = 32u * (uint32_t)(ks & 3), seg = (uint32_t)(ks >> 2) * C::SEG_BYTES;
+      const uint32_t ao = (ab ^ x) + seg, bo = (bb_ ^ x) + seg;
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(qt + ao);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(qt + ao + 32 * 128);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(kt + bo);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, acc[1], 0, 0, 0);
+    } else {
+      const uint32_t x = 64u * (uint32_t)ks;
+      const uint32_t ao = ab ^ x, bo = bb_ ^ x;
+      i32x8 a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(qt + (ao + i * 32 * 128));
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(qt + ((ao ^ 16u) + i * 32 * 128));
+        a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(kt + bo);
+      const i32x4 hi = *reinterpret_cast<const i32x4*>(kt + (bo ^ 16u));
+      const i32x8 bv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bv, acc[i], 0, 0, 0, 127, 0, 127);
+    }
+  }
+
+  // copies this wave issues for one head after the first (tile rows, per-row vectors)
+  __device__ __forceinline__ int copies_per_head() const {
+    return ((!dma_k || Hk == H) ? DPW : 0) + (vsrc != nullptr ? 2 : 0);
+  }
+
+  // wait until this wave's copies of head h have landed while the n newer ones may fly
+  __device__ __forceinline__ static void wait_copies(int n) {
+    switch (n) {
+      case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+  }
+
+  // the k-steps of head h with (COPY) a share of the copies of head hp into stage sp and
+  // (EPI) a share of head h-1's epilogue each; straight-line code, so the compiler can
+  // interleave the parts
+  template <bool COPY, bool EPI>
+  __device__ __forceinline__ void body(int h, int hp, int st, int sp, f32x16 (&cur)[2], const f32x16 (&prev)[2],
+                                       uint32_t ab, uint32_t bb_) {
+    constexpr int CPK = DPW / KS;   // copies per k-step
+    constexpr int EPK = 32 / KS;    // epilogue elements per k-step
+    static_assert(CPK * KS == DPW && EPK * KS == 32, "copies and epilogue must split evenly over the k-steps");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kstep(ks, cur, st, ab, bb_);
+      if constexpr (COPY) {
+#pragma unroll
+        for (int c = 0; c < CPK; ++c) copy_part(ks * CPK + c, hp, sp);
+      }
+      if constexpr (EPI) {
+        if constexpr (KS == 8) {
+          switch (ks) {
+            case 0: epilogue_part<0 * EPK, EPK>(prev, h - 1); break;
+            case 1: epilogue_part<1 * EPK, EPK>(prev, h - 1); break;
+            case 2: epilogue_part<2 * EPK, EPK>(prev, h - 1); break;
+            case 3: epilogue_part<3 * EPK, EPK>(prev, h - 1); break;
+            case 4: epilogue_part<4 * EPK, EPK>(prev, h - 1); break;
+            case 5: epilogue_part<5 * EPK, EPK>(prev, h - 1); break;
+            case 6: epilogue_part<6 * EPK, EPK>(prev, h - 1); break;
+            default: epilogue_part<7 * EPK, EPK>(prev, h - 1); break;
+          }
+        } else {
+          if (ks == 0) epilogue_part<0, EPK>(prev, h - 1);
+          else epilogue_part<EPK, EPK>(prev, h - 1);
+        }
+      }
+    }
+  }
+
+  // Head h (tile stage h % NSTAGE): after the barrier, its KS k-steps each carry a share
+  // of the copies of head h + NSTAGE - 1 into the stage head h-1 used and a share of head
+  // h-1's epilogue, so the copies drain and the epilogue runs while the matrix cores work.
+  __device__ __forceinline__ void head(int h, f32x16 (&cur)[2], const f32x16 (&prev)[2]) {
+    const int st = h % C::NSTAGE;
+    const int hp = h + C::NSTAGE - 1, sp = hp % C::NSTAGE;
+    wait_copies(min(C::NSTAGE - 2, H - 1 - h) * copies_per_head());
+    // stage st holds head h; stage sp is free (LDS-only barrier: later heads' copies fly on)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool next = hp < H;
+    const bool copy = next && (!dma_k || Hk == H);  // uniform per wave
+    uint32_t ab = abase, bb_ = bbase;
+    asm volatile("" : "+v"(ab), "+v"(bb_));
+    if constexpr (DT == FP8) {
+      // head h's weights times its query scales, in place; its epilogue reads them after
+      // the next barrier
+      if (wv == 1) {
+        float* vb = reinterpret_cast<float*>(smem + C::VBASE + (h % C::NVSTAGE) * C::VSTAGE);
+        vb[C::W_OFF / 4 + lane] *= vb[C::QS_OFF / 4 + lane];
+        vb[C::W_OFF / 4 + 64 + lane] *= vb[C::QS_OFF / 4 + 64 + lane];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    if constexpr (DT == BF16) {
-#pragma unroll
-      for (int ks = 0; ks < HD / 16; ++ks) {
-        const int col = 2 * ks + lg;  // elements 16ks + 8lg .. +7
-        bf16x8 a[2], bb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const bf16x8*>(frag(qt, 64 * wm + 32 * i + lr, col));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bb[j] = *reinterpret_cast<const bf16x8*>(frag(kt, 64 * wn + 32 * j + lr, col));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
-      }
+      for (int r = 0; r < 16; ++r) cur[i][r] = 0.f;
+    if (copy) {
+      if (h > 0) body<true, true>(h, hp, st, sp, cur, prev, ab, bb_);
+      else body<true, false>(h, hp, st, sp, cur, prev, ab, bb_);
     } else {
-#pragma unroll
-      for (int ks = 0; ks < HD / 64; ++ks) {
-        const int col = 4 * ks + 2 * lg;  // bytes 64ks + 32lg .. +31 = chunks col, col+1
-        i32x8 a[2], bb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = 64 * wm + 32 * i + lr;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(frag(qt, r, col));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(frag(qt, r, col + 1));
-          a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = 64 * wn + 32 * j + lr;
-          const i32x4 lo = *reinterpret_cast<const i32x4*>(frag(kt, r, col));
-          const i32x4 hi = *reinterpret_cast<const i32x4*>(frag(kt, r, col + 1));
-          bb[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0, 127, 0, 127);
-      }
+      if (h > 0) body<false, true>(h, hp, st, sp, cur, prev, ab, bb_);
+      else body<false, false>(h, hp, st, sp, cur, prev, ab, bb_);
     }
-  }
-
-  // head h lives in tile stage h & 1; its MFMAs go into `cur` while the epilogue of head
-  // h-1 (accumulators `prev`) runs
-  __device__ __forceinline__ void head(int h, int st, f32x16 (&cur)[2][2], const f32x16 (&prev)[2][2]) {
-    wait_vmem();
-    __syncthreads();  // stage st holds head h; the other stage is free
-    if (h + 1 < H) issue(h + 1, st ^ 1, Hk == H);
-    contract(cur, st);
-    if (h > 0) epilogue(prev, h - 1);
+    if (next) copy_vectors(hp);
   }
 
   __device__ __forceinline__ void run() {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int r = 0; r < 16; ++r) tot[i][r] = 0.f;
+    for (int x = 0; x < C::NSTAGE - 1 && x < H; ++x) {
+      if (x == 0 || !dma_k || Hk == H) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
-    issue(0, 0, true);
+        for (int i = 0; i < DPW; ++i) copy_part(i, x, x);
+      }
+      copy_vectors(x);
+    }
     int h = 0;
     for (; h + 1 < H; h += 2) {
-      head(h, 0, acc0, acc1);
-      head(h + 1, 1, acc1, acc0);
+      head(h, acc0, acc1);
+      head(h + 1, acc1, acc0);
     }
-    if (h < H) {
-      head(h, 0, acc0, acc1);
-      epilogue(acc0, h);
-    } else {
-      epilogue(acc1, H - 1);
-    }
+    if (h < H) head(h, acc0, acc1);
+    __syncthreads();  // (fp8) the last head's weights were scaled in LDS by wave 1
+    if (h < H) epilogue_part<0, 32>(acc0, h);
+    else epilogue_part<0, 32>(acc1, H - 1);
   }
 };
 
 template <int DT>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(TILE_THREADS, TILE_THREADS), amdgpu_waves_per_eu(2, 2)))
 void indexer_tile(IndexerParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int32_t rks[PQ], rke[PQ];
@@ -463,25 +566,20 @@ void indexer_tile(IndexerParams p) {
   if (!__syncthreads_or(live)) return;
 
   TileWork<DT> w{p, smem, lane, wave, __builtin_amdgcn_readfirstlane(wave), b, t0, p.H, p.Hk, T, s0, s_cap,
-                 wave & 1, wave >> 1, lane & 31, lane >> 5,
-                 static_cast<const unsigned char*>(p.q), static_cast<const unsigned char*>(p.k),
-                 (int64_t)p.H * HD * TileCfg<DT>::ESZ, (int64_t)p.Hk * HD * TileCfg<DT>::ESZ,
-                 min(t0 + lane, T - 1), min(t0 + 64 + lane, T - 1),
-                 min<int64_t>(s0 + lane, s_cap - 1), min<int64_t>(s0 + 64 + lane, s_cap - 1)};
+                 wave & 1, wave >> 1, lane & 31, lane >> 5};
+  w.setup(static_cast<const unsigned char*>(p.q), static_cast<const unsigned char*>(p.k),
+          (int64_t)p.H * HD * TileCfg<DT>::ESZ, (int64_t)p.Hk * HD * TileCfg<DT>::ESZ);
   w.run();
 
-  // write the candidate cells: result row m = 8(r/4) + 4lg + r%4 of tile i, column lr of tile j
+  // write the candidate cells: result row m = 8(r/4) + 4lg + r%4 of tile i, column lr
+  const int64_t s = s0 + 32 * w.wn + w.lr;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t s = s0 + 64 * w.wn + 32 * j + w.lr;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
-        const int t = t0 + m;
-        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = w.tot[i][j][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
+      const int t = t0 + m;
+      if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = w.tot[i][r];
     }
 }
 
@@ -597,10 +695,10 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
     hipError_t e;
     if (dt == BF16) {
       if ((e = DSA_ALLOW_LDS(indexer_tile<BF16>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(indexer_tile<BF16>, grid, dim3(256), lds, st, p);
+      hipLaunchKernelGGL(indexer_tile<BF16>, grid, dim3(TILE_THREADS), lds, st, p);
     } else {
       if ((e = DSA_ALLOW_LDS(indexer_tile<FP8>, lds)) != hipSuccess) return e;
-      hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(256), lds, st, p);
+      hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(TILE_THREADS), lds, st, p);
     }
   } else if (mfma && p.T <= 4 && (int64_t)p.B * p.T <= 65535 && (p.H == 16 || p.H == 32 || p.H == 64)) {
     // decode: stream the keys once per query row
