@@ -555,34 +555,52 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   }
 }
 
-// Merge the split partials of one (query, head) in split order.  grid.x = query *
-// (Hm / 4); 256 threads = 4 heads x 64 threads x 8 dims.
+// Merge the split partials of one (query, head) in split order.  grid.x = (query, group
+// of 4 heads, quarter of the 512 value dims); 256 threads = 4 heads x 64 lanes x 2 dims.
+// The loads of a batch of splits are independent of each other (an empty split's
+// partial is never written and gets weight 0 through a select), so they are all in
+// flight at once.
+constexpr int CMB_BATCH = 8;
 __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_ml) {
-  const int64_t tok = blockIdx.x / (p.Hm / 4);
-  const int head = (int)(blockIdx.x % (p.Hm / 4)) * 4 + (threadIdx.x >> 6);
-  const int d0 = (threadIdx.x & 63) * 8;
+  const int quarters = 4, groups = p.Hm / 4;
+  const int64_t tok = blockIdx.x / (groups * quarters);
+  const int rest = (int)(blockIdx.x % (groups * quarters));
+  const int head = (rest / quarters) * 4 + (threadIdx.x >> 6);
+  const int d0 = (rest % quarters) * (MDC / quarters) + (threadIdx.x & 63) * 2;
+  const float* ml = ws_ml + (tok * nsplit * p.Hm + head) * 2;  // split s at ml + s * Hm * 2
+  const int64_t mstride = (int64_t)p.Hm * 2;
   float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_ml[((tok * nsplit + s) * p.Hm + head) * 2]);
-  float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float L = 0.f;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mstride]);
+  float o0 = 0.f, o1 = 0.f, L = 0.f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ml = ws_ml + ((tok * nsplit + s) * p.Hm + head) * 2;
-      if (ml[1] == 0.f) continue;
-      const float f = exp2f(ml[0] - M);
-      L += ml[1] * f;
-      const float* src = ws_o + ((tok * nsplit + s) * p.Hm + head) * MDC + d0;
+    const float* src = ws_o + (tok * nsplit * p.Hm + head) * MDC + d0;  // split s at src + s * Hm * MDC
+    const int64_t ostride = (int64_t)p.Hm * MDC;
+    for (int s0 = 0; s0 < nsplit; s0 += CMB_BATCH) {
+      float2 v[CMB_BATCH];
+      float f[CMB_BATCH], l[CMB_BATCH];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = fmaf(src[i], f, o[i]);
+      for (int u = 0; u < CMB_BATCH; ++u) {
+        const int s = min(s0 + u, nsplit - 1);
+        v[u] = *reinterpret_cast<const float2*>(src + s * ostride);
+        l[u] = ml[s * mstride + 1];
+        f[u] = ml[s * mstride];
+      }
+#pragma unroll
+      for (int u = 0; u < CMB_BATCH; ++u) {
+        const bool use = s0 + u < nsplit && l[u] != 0.f;
+        const float w = use ? exp2f(f[u] - M) : 0.f;
+        L = use ? fmaf(l[u], w, L) : L;
+        o0 = use ? fmaf(v[u].x, w, o0) : o0;
+        o1 = use ? fmaf(v[u].y, w, o1) : o1;
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + head) * MDC + d0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) og[i] = f32_to_bf16_bits(o[i] * inv);
-  if (p.lse && (threadIdx.x & 63) == 0)
-    p.lse[tok * p.Hm + head] = L > 0.f ? (M + log2f(L)) * LN2 : -__builtin_inff();
+  og[0] = f32_to_bf16_bits(o0 * inv);
+  og[1] = f32_to_bf16_bits(o1 * inv);
+  if (p.lse && d0 == 0) p.lse[tok * p.Hm + head] = L > 0.f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
 // ----------------------------------------------------------------- generic kernel
@@ -653,8 +671,10 @@ struct SplitPlan {
 SplitPlan plan_split(int64_t rows, int Hm, int topk) {
   const int64_t wgs = rows * (Hm / MHG);
   const int tiles = (topk + MT - 1) / MT;
+  // few queries (decode): split each selection so that about one workgroup per compute
+  // unit runs (one per CU fits in LDS), each over a run of consecutive tiles
   int nsplit = 1;
-  if (wgs < 512) nsplit = (int)std::min<int64_t>(tiles, (512 + wgs - 1) / std::max<int64_t>(wgs, 1));
+  if (wgs < 256) nsplit = (int)std::min<int64_t>(tiles, (256 + wgs - 1) / std::max<int64_t>(wgs, 1));
   int tps = (tiles + nsplit - 1) / nsplit;
   tps = std::min(tps, MAX_TILES_PER_ITEM);
   nsplit = (tiles + tps - 1) / tps;
@@ -695,7 +715,7 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t, hip
     hipLaunchKernelGGL(mla_mfma, grid, dim3(256), lds, st, p, sp.nsplit, sp.tiles_per_split, ws_o, ws_ml);
     if (n_launches) ++*n_launches;
     if (sp.nsplit > 1) {
-      hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4))), dim3(256), 0, st, p, sp.nsplit,
+      hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4) * 4)), dim3(256), 0, st, p, sp.nsplit,
                          ws_o, ws_ml);
       if (n_launches) ++*n_launches;
     }
