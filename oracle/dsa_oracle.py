@@ -235,6 +235,53 @@ def sparse_mla(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float, 
     return o, lse
 
 
+def sparse_mla_backward_row(q_row: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float, Dc: int,
+                            dout_row: np.ndarray):
+    """Gradient of one query's sparse attention (sparse_mla_row) for an output
+    gradient dout_row [Hm, Dc], by the chain rule through the definition: the
+    selection is a constant (no gradient flows through top-k), P = softmax(z) over the
+    selected rows, z = sm_scale * q . c_j, o = sum_j P_j c_j[:Dc].
+
+        dP_j = dout . c_j[:Dc]         D = dout . o = sum_j P_j dP_j
+        dz_j = P_j (dP_j - D)
+        dq   = sm_scale sum_j dz_j c_j
+        dc_j = sm_scale dz_j q + [P_j dout, 0]   (summed over heads)
+
+    Returns (dq_row [Hm, R], rows [J], dc [J, R]); an empty selection gives zeros."""
+    S, R = kv.shape
+    sel = np.asarray(idx, dtype=np.int64)
+    sel = sel[(sel >= 0) & (sel < S)]
+    Hm = q_row.shape[0]
+    if sel.size == 0:
+        return np.zeros((Hm, R)), sel, np.zeros((0, R))
+    c = kv[sel]                                                 # [J, R]
+    z = sm_scale * (q_row @ c.T)                                # [Hm, J]
+    e = np.exp(z - z.max(axis=1, keepdims=True))
+    P = e / e.sum(axis=1, keepdims=True)
+    o = P @ c[:, :Dc]                                           # [Hm, Dc]
+    dP = dout_row @ c[:, :Dc].T                                 # [Hm, J]
+    D = (dout_row * o).sum(axis=1, keepdims=True)               # [Hm, 1]
+    dz = P * (dP - D)
+    dq = sm_scale * (dz @ c)                                    # [Hm, R]
+    dc = sm_scale * (dz.T @ q_row)                              # [J, R]
+    dc[:, :Dc] += P.T @ dout_row
+    return dq, sel, dc
+
+
+def sparse_mla_backward(q: np.ndarray, kv: np.ndarray, idx: np.ndarray, sm_scale: float, Dc: int,
+                        dout: np.ndarray):
+    """q [B,T,Hm,R], kv [B,S,R], idx [B,T,k], dout [B,T,Hm,Dc] -> (dq [B,T,Hm,R], dkv [B,S,R]);
+    a row selected by several queries (or listed twice) collects every contribution."""
+    B, T = q.shape[:2]
+    dq = np.zeros(q.shape)
+    dkv = np.zeros(kv.shape)
+    for b in range(B):
+        for t in range(T):
+            dq[b, t], sel, dc = sparse_mla_backward_row(q[b, t], kv[b], idx[b, t], sm_scale, Dc, dout[b, t])
+            np.add.at(dkv[b], sel, dc)
+    return dq, dkv
+
+
 # ------------------------------------------------------------------ IndexShare
 
 

@@ -462,3 +462,91 @@ def test_cache_append_writes_rows_and_skips_outside():
     assert np.array_equal(k2[4], codes[0]) and np.array_equal(s2[4], scales[0]) and np.array_equal(kv2[4], kv_new[0])
     untouched = [0, 1, 2, 3, 5]
     assert not k2[untouched].any() and (s2[untouched] == 1).all() and not kv2[untouched].any()
+
+
+# ---------------------------------------------------------------- sparse MLA backward
+
+def _sdpa_causal_grads(q, kv, Dc, scale, dout):
+    """Gradients of dense causal attention w.r.t. q and the latent rows (keys = whole
+    rows, values = their first Dc values) by torch autograd through its library
+    attention routine, float64."""
+    T, Hm, R = q.shape
+    S = kv.shape[0]
+    qt = torch.from_numpy(q).clone().requires_grad_(True)
+    kvt = torch.from_numpy(kv).clone().requires_grad_(True)
+    qq = qt.permute(1, 0, 2)[None]
+    kk = kvt[None, None].expand(1, Hm, S, R)
+    vv = kvt[:, :Dc][None, None].expand(1, Hm, S, Dc)
+    pos = np.arange(T)[:, None] + (S - T)
+    mask = torch.from_numpy(np.arange(S)[None, :] <= pos)
+    o = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask, scale=scale)
+    (o[0].permute(1, 0, 2) * torch.from_numpy(dout)).sum().backward()
+    return qt.grad.numpy(), kvt.grad.numpy()
+
+
+@pytest.mark.parametrize("T,S", [(10, 10), (3, 17)])
+def test_sparse_mla_backward_with_topk_ge_prefix_equals_dense_causal_autograd(T, S):
+    rng = np.random.default_rng(71 + T)
+    Hm, Dc, Dr, k = 3, 6, 2, 32
+    q = rng.standard_normal((1, T, Hm, Dc + Dr))
+    kv = rng.standard_normal((1, S, Dc + Dr))
+    dout = rng.standard_normal((1, T, Hm, Dc))
+    scale = 0.37
+    idx = np.full((1, T, k), -1, np.int64)
+    for t in range(T):
+        p = S - T + t
+        idx[0, t, :p + 1] = np.arange(p + 1)
+    dq, dkv = O.sparse_mla_backward(q, kv, idx, scale, Dc, dout)
+    rq, rkv = _sdpa_causal_grads(q[0], kv[0], Dc, scale, dout[0])
+    np.testing.assert_allclose(dq[0], rq, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkv[0], rkv, rtol=1e-11, atol=1e-12)
+
+
+def test_sparse_mla_backward_matches_central_differences():
+    """Scattered selections with -1 holes and a row listed twice: every gradient entry
+    against a central difference of the forward oracle's loss sum(o * dout)."""
+    rng = np.random.default_rng(73)
+    B, T, S, Hm, Dc, Dr, k = 2, 2, 7, 2, 4, 2, 5
+    q = rng.standard_normal((B, T, Hm, Dc + Dr))
+    kv = rng.standard_normal((B, S, Dc + Dr))
+    dout = rng.standard_normal((B, T, Hm, Dc))
+    idx = np.array([[[0, 3, -1, 6, 2], [5, 5, 1, -1, -1]], [[4, -1, -1, -1, -1], [6, 0, 1, 2, 3]]])
+    scale = 0.6
+    dq, dkv = O.sparse_mla_backward(q, kv, idx, scale, Dc, dout)
+
+    def loss(qq, kk):
+        return float((O.sparse_mla(qq, kk, idx, scale, Dc)[0] * dout).sum())
+
+    eps = 1e-6
+    num_q = np.zeros_like(q)
+    for i in np.ndindex(q.shape):
+        a, b = q.copy(), q.copy()
+        a[i] += eps
+        b[i] -= eps
+        num_q[i] = (loss(a, kv) - loss(b, kv)) / (2 * eps)
+    num_kv = np.zeros_like(kv)
+    for i in np.ndindex(kv.shape):
+        a, b = kv.copy(), kv.copy()
+        a[i] += eps
+        b[i] -= eps
+        num_kv[i] = (loss(q, a) - loss(q, b)) / (2 * eps)
+    np.testing.assert_allclose(dq, num_q, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dkv, num_kv, rtol=1e-6, atol=1e-8)
+    assert np.all(dkv[0, 1] != 0) and np.all(dkv[1, 5] == 0)   # row 1 of item 0 selected, row 5 of item 1 not
+
+
+def test_sparse_mla_backward_single_row_and_empty_selection():
+    """|J| = 1: P = 1, so dz = 0: no query gradient, and the row's gradient is the sum
+    of the heads' output gradients in its value part and 0 in its rope part.  An empty
+    selection contributes nothing."""
+    rng = np.random.default_rng(74)
+    Hm, Dc, Dr, S = 3, 5, 3, 6
+    q = rng.standard_normal((1, 2, Hm, Dc + Dr))
+    kv = rng.standard_normal((1, S, Dc + Dr))
+    dout = rng.standard_normal((1, 2, Hm, Dc))
+    idx = np.array([[[4, -1], [-1, -1]]])
+    dq, dkv = O.sparse_mla_backward(q, kv, idx, 0.5, Dc, dout)
+    assert np.allclose(dq, 0, atol=1e-14)
+    want = np.zeros((S, Dc + Dr))
+    want[4, :Dc] = dout[0, 0].sum(axis=0)
+    np.testing.assert_allclose(dkv[0], want, atol=1e-14)
