@@ -72,6 +72,8 @@ _SIGS = {
                                     C.c_void_p, C.POINTER(GroupStats), C.c_void_p]),
     "dsa_group_stats_compute": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int, C.c_int32, C.c_void_p, C.c_void_p,
                                           C.c_void_p, C.POINTER(GroupStats)]),
+    "dsa_sparse_mla_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float,
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dsa_index_prep": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dsa_latent_append": (C.c_int, [C.c_int32, C.c_int32, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
@@ -189,6 +191,18 @@ def sparse_mla_attention(q, kv, topk_indices, sm_scale, out, lse=None, *, Dc, wo
                                           _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
                                           _dev_ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def sparse_mla_backward(q, kv, topk_indices, sm_scale, out, lse, dout, dq, dkv, *, Dc, stream=None):
+    """dsa_sparse_mla_backward.  Forward inputs and results (out, lse), dout [B,T,Hm,Dc];
+    dq [B,T,Hm,Dc+Dr] and dkv [B,S,Dc+Dr] fp32 are written in place."""
+    B, T, Hm, R = q.shape
+    S = kv.shape[1]
+    shape = make_shape(B, T, S, topk=topk_indices.shape[-1], Hm=Hm, Dc=Dc, Dr=R - Dc)
+    _check(lib().dsa_sparse_mla_backward(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(kv),
+                                         _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
+                                         _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dkv), _stream(stream)))
+    return dq, dkv
 
 
 def index_prep(x, pos, out, out_scale=None, *, rows=None, rope_theta=8.0e6, stream=None):

@@ -199,6 +199,24 @@ dsa_status dsa_sparse_mla_attention(const dsa_shape* s, dsa_dtype dt, const void
   return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA launch");
 }
 
+dsa_status dsa_sparse_mla_backward(const dsa_shape* s, dsa_dtype dt, const void* q, const void* kv,
+                                   const int32_t* idx, float sm_scale, const void* out, const float* lse,
+                                   const void* dout, float* dq, float* dkv, void* stream) {
+  dsa_status st = check_mla_shape(s, dt);
+  if (st == DSA_OK) st = check_sm_scale(sm_scale);
+  if (st != DSA_OK) return st;
+  if (!dsa::mla_bwd_supported(s->Hm, s->Dc, s->Dr, (dsa::Dtype)dt))
+    return fail(DSA_ERR_UNSUPPORTED, "sparse MLA backward: Hm=%d Dc=%d Dr=%d need Hm <= 64, Dc <= 512, Dc+Dr <= 640",
+                s->Hm, s->Dc, s->Dr);
+  if (s->s_cap > 0 && (!kv || !dkv)) return fail(DSA_ERR_INVALID_ARG, "kv and dkv must be non-NULL");
+  if (rows_of(s) > 0 && (!q || !idx || !out || !lse || !dout || !dq))
+    return fail(DSA_ERR_INVALID_ARG, "q, topk_indices, out, lse, dout and dq must be non-NULL");
+  const dsa::MlaBwdParams p{s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, q, kv, idx, sm_scale,
+                            out, lse, dout, dq, dkv};
+  hipError_t e = dsa::launch_sparse_mla_bwd(p, (dsa::Dtype)dt, (hipStream_t)stream, nullptr);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA backward launch");
+}
+
 dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_layers,
                              const dsa_layer_type* types, const dsa_layer_io* layers, float sm_scale,
                              dsa_topk_cache* cache, uint64_t tag, void* ws, size_t ws_bytes, void* const* events,

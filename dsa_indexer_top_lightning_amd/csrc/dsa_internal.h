@@ -46,6 +46,21 @@ struct MlaParams {
   float* lse;
 };
 
+// Backward of the sparse MLA attention: forward inputs and results, output gradient.
+struct MlaBwdParams {
+  int B, T, Hm, Dc, Dr, topk;
+  int64_t s_cap;
+  const void* q;        // [B,T,Hm,Dc+Dr]
+  const void* kv;       // [B,S,Dc+Dr]
+  const int32_t* idx;   // [B,T,topk]
+  float sm_scale;
+  const void* out;      // [B,T,Hm,Dc] forward output
+  const float* lse;     // [B,T,Hm] forward log-sum-exp
+  const void* dout;     // [B,T,Hm,Dc]
+  float* dq;            // [B,T,Hm,Dc+Dr]
+  float* dkv;           // [B,S,Dc+Dr]
+};
+
 // New index vectors x [n, heads, D] fp32 -> RoPE -> out rows (bf16 or fp8 codes + scales).
 struct PrepParams {
   int n, heads, D;
@@ -77,6 +92,9 @@ bool mla_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);
 size_t mla_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt);
 hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
                              int* n_launches);
+size_t mla_bwd_lds_bytes(int Hm, int Dc, int Dr, Dtype dt);
+bool mla_bwd_supported(int Hm, int Dc, int Dr, Dtype dt);
+hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
 hipError_t launch_index_prep(const PrepParams& p, hipStream_t st);
 hipError_t launch_latent_append(const LatentAppendParams& p, hipStream_t st);
 

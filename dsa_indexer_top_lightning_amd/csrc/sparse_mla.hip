@@ -666,13 +666,12 @@ struct SplitPlan {
   int nsplit, tiles_per_split;
 };
 
-// Few queries (decode): split each query's selection over several workgroups so
-// that >= 512 run; every split covers whole 64-row tiles.
+// Few queries (decode): split each query's selection over several workgroups so that
+// about one workgroup per compute unit runs (one per CU fits in LDS); every split
+// covers a run of whole 64-row tiles.
 SplitPlan plan_split(int64_t rows, int Hm, int topk) {
   const int64_t wgs = rows * (Hm / MHG);
   const int tiles = (topk + MT - 1) / MT;
-  // few queries (decode): split each selection so that about one workgroup per compute
-  // unit runs (one per CU fits in LDS), each over a run of consecutive tiles
   int nsplit = 1;
   if (wgs < 256) nsplit = (int)std::min<int64_t>(tiles, (256 + wgs - 1) / std::max<int64_t>(wgs, 1));
   int tps = (tiles + nsplit - 1) / nsplit;

@@ -212,6 +212,27 @@ dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
                                    dsa_group_stats* out);
 
 /*
+ * Backward of dsa_sparse_mla_attention (training with shared indices: a shared layer
+ * differentiates through the donor's selection, which is a constant).  The forward is
+ * the IndexShare page's section 1 attention over the selected rows; its gradient for
+ * an output gradient dout, with P_j = exp(z_j - lse), z_j = sm_scale q.c_j, D = dout.o:
+ *   dz_j = P_j (dout.c_j[:Dc] - D),  dq = sm_scale sum_j dz_j c_j,
+ *   dkv[row j] += sm_scale dz_j q + [P_j dout, 0]   (summed over heads and queries).
+ *   q, kv, topk_indices, sm_scale: as passed to the forward (mla dtype F32 or BF16)
+ *   out [B,T,Hm,Dc] (mla dtype), lse [B,T,Hm] fp32: the forward's results
+ *   dout [B,T,Hm,Dc] (mla dtype)
+ *   dq  [B,T,Hm,Dc+Dr] fp32, overwritten
+ *   dkv [B,S,Dc+Dr] fp32, overwritten: zeroed by the call, then every selected row
+ *       collects its contributions with fp32 atomics (their order is not fixed, so dkv
+ *       is reproducible to fp32 rounding, not bit for bit)
+ * Requires Hm <= 64, Dc <= 512, Dc + Dr <= 640 (DSA_ERR_UNSUPPORTED otherwise);
+ * DSA_ERR_INVALID_ARG on NULL pointers or a bad sm_scale.  No workspace.
+ */
+dsa_status dsa_sparse_mla_backward(const dsa_shape* shape, dsa_dtype mla_dtype, const void* q, const void* kv,
+                                   const int32_t* topk_indices, float sm_scale, const void* out,
+                                   const float* lse, const void* dout, float* dq, float* dkv, void* stream);
+
+/*
  * Decode-step preparation of new index vectors (the Megatron-Bridge pull request's
  * commit on the indexer RoPE half swap: the LAST D/2 dims of every index head are
  * rotated; rope_theta = 8e6 in its config fix).  For each vector x[i, h, :] (fp32,
