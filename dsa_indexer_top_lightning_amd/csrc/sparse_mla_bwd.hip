@@ -13,12 +13,14 @@
 //
 // mla_bwd: one workgroup of 8 waves per query token; the token's queries and output
 // gradients sit in LDS in their storage type, wave w takes heads w, w+8, ... with its
-// lanes over the row's values (lane + 64 i).  Selected rows are taken two at a time
+// lanes over the row's values (lane + 64 i) and sums over lanes by DPP moves.  Selected rows are taken two at a time
 // into LDS as fp32; each wave adds its heads' share of the two rows' gradients into an
 // LDS sum (ds_add_f32), and the workgroup then adds the sums to the latent-row
 // gradient in global memory with one fp32 atomic per value (rows shared by several
 // queries, or listed twice, collect every contribution; the order of those additions
-// is not fixed, so dkv is reproducible to fp32 rounding only).  dq is written whole.
+// is not fixed, so dkv is reproducible to fp32 rounding only).  dq is written whole,
+// except for few query tokens (decode), whose selections are split over several
+// workgroups that add their shares of dq with atomics.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -48,14 +50,29 @@ __device__ __forceinline__ float bw_lds(const unsigned char* base, int i) {
   else return bw_bf16(reinterpret_cast<const uint16_t*>(base)[i]);
 }
 
+// Sum over the 64 lanes with data-parallel-primitive moves (no LDS round trips): swap
+// neighbours, swap pairs, mirror within 8 and within 16 lanes (each lane then holds its
+// row's sum), add row 0 into row 1 and row 2 into row 3 (broadcast of lane 15), then
+// rows 0+1 into rows 2 and 3 (broadcast of lane 31); lane 63 holds the total.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v += dpp_move<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_move<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_move<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_move<0x140, 0xF>(v);  // row_mirror
+  v += dpp_move<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_move<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// grid.x = (query token, split): split s takes the token's selection slots
+// [s * per_split, (s + 1) * per_split); with more than one split dq is accumulated with
+// atomics too (cleared beforehand).
 template <int DT>
-__global__ __launch_bounds__(BW_THREADS) void mla_bwd(MlaBwdParams p) {
+__global__ __launch_bounds__(BW_THREADS) void mla_bwd(MlaBwdParams p, int nsplit, int per_split) {
   constexpr int ESZ = (DT == F32) ? 4 : 2;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int Hm = p.Hm, Dc = p.Dc, R = p.Dc + p.Dr;
@@ -68,8 +85,10 @@ __global__ __launch_bounds__(BW_THREADS) void mla_bwd(MlaBwdParams p) {
   __shared__ int32_t rows[BW_JB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t tok = blockIdx.x;
+  const int64_t tok = blockIdx.x / nsplit;
+  const int split = (int)(blockIdx.x % nsplit);
   const int64_t b = tok / p.T;
+  const int jbeg = split * per_split, jend = min(p.topk, jbeg + per_split);
   const float s = p.sm_scale, s2 = p.sm_scale * BW_LOG2E;
 
   // the token's queries and output gradients into LDS
@@ -100,11 +119,11 @@ __global__ __launch_bounds__(BW_THREADS) void mla_bwd(MlaBwdParams p) {
     for (int i = 0; i < BW_RI; ++i) dq[k][i] = 0.f;
 
   const int32_t* idx = p.idx + tok * (int64_t)p.topk;
-  for (int j0 = 0; j0 < p.topk; j0 += BW_JB) {
+  for (int j0 = jbeg; j0 < jend; j0 += BW_JB) {
     __syncthreads();  // previous step's LDS sums are flushed; the token's data is in place
     if (tid < BW_JB) {
       const int j = j0 + tid;
-      const int32_t e = j < p.topk ? idx[j] : -1;
+      const int32_t e = j < jend ? idx[j] : -1;
       rows[tid] = (e >= 0 && (int64_t)e < p.s_cap) ? e : -1;
     }
     __syncthreads();
@@ -194,7 +213,10 @@ __global__ __launch_bounds__(BW_THREADS) void mla_bwd(MlaBwdParams p) {
 #pragma unroll
     for (int i = 0; i < BW_RI; ++i) {
       const int d = lane + 64 * i;
-      if (d < R) p.dq[(tok * Hm + h) * R + d] = dq[k][i];
+      if (d < R) {
+        if (nsplit == 1) p.dq[(tok * Hm + h) * R + d] = dq[k][i];
+        else atomicAdd(&p.dq[(tok * Hm + h) * R + d], dq[k][i]);
+      }
     }
   }
 }
@@ -218,9 +240,21 @@ bool mla_bwd_supported(int Hm, int Dc, int Dr, Dtype dt) {
 hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st, int* n_launches) {
   const int64_t rows = (int64_t)p.B * p.T;
   const int64_t nkv = (int64_t)p.B * p.s_cap * (p.Dc + p.Dr);
+  // few query tokens (decode): split each selection so that >= 1024 workgroups run
+  int nsplit = 1;
+  if (rows > 0 && rows < 1024) nsplit = (int)std::min<int64_t>((p.topk + BW_JB - 1) / BW_JB, (1024 + rows - 1) / rows);
+  int per_split = (p.topk + nsplit - 1) / nsplit;
+  per_split = (per_split + BW_JB - 1) / BW_JB * BW_JB;
+  nsplit = per_split > 0 ? (p.topk + per_split - 1) / per_split : 1;
   if (nkv > 0) {
     hipLaunchKernelGGL(bw_zero, dim3((unsigned)std::min<int64_t>((nkv + 255) / 256, 4096)), dim3(256), 0, st,
                        p.dkv, nkv);
+    if (n_launches) ++*n_launches;
+  }
+  const int64_t nq = rows * p.Hm * (p.Dc + p.Dr);
+  if (nsplit > 1 && nq > 0) {
+    hipLaunchKernelGGL(bw_zero, dim3((unsigned)std::min<int64_t>((nq + 255) / 256, 4096)), dim3(256), 0, st,
+                       p.dq, nq);
     if (n_launches) ++*n_launches;
   }
   if (rows == 0) return hipGetLastError();
@@ -229,11 +263,11 @@ hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st
   if (dt == F32) {
     static std::atomic<size_t> high{0};
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd<F32>), lds, high)) != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_bwd<F32>, dim3((unsigned)rows), dim3(BW_THREADS), lds, st, p);
+    hipLaunchKernelGGL(mla_bwd<F32>, dim3((unsigned)(rows * nsplit)), dim3(BW_THREADS), lds, st, p, nsplit, per_split);
   } else {
     static std::atomic<size_t> high{0};
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd<BF16>), lds, high)) != hipSuccess) return e;
-    hipLaunchKernelGGL(mla_bwd<BF16>, dim3((unsigned)rows), dim3(BW_THREADS), lds, st, p);
+    hipLaunchKernelGGL(mla_bwd<BF16>, dim3((unsigned)(rows * nsplit)), dim3(BW_THREADS), lds, st, p, nsplit, per_split);
   }
   if (n_launches) ++*n_launches;
   return hipGetLastError();

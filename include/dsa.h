@@ -221,7 +221,9 @@ dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
  *   q, kv, topk_indices, sm_scale: as passed to the forward (mla dtype F32 or BF16)
  *   out [B,T,Hm,Dc] (mla dtype), lse [B,T,Hm] fp32: the forward's results
  *   dout [B,T,Hm,Dc] (mla dtype)
- *   dq  [B,T,Hm,Dc+Dr] fp32, overwritten
+ *   dq  [B,T,Hm,Dc+Dr] fp32, overwritten (for fewer than 1024 query tokens each
+ *       selection is split over several workgroups that add their shares with fp32
+ *       atomics: then dq too is reproducible to fp32 rounding only)
  *   dkv [B,S,Dc+Dr] fp32, overwritten: zeroed by the call, then every selected row
  *       collects its contributions with fp32 atomics (their order is not fixed, so dkv
  *       is reproducible to fp32 rounding, not bit for bit)
