@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--workload", default="prefill4k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the sparse MLA backward of layer 0 (its forward's indices, output and lse, a "
+                         "seeded output gradient) instead of the forward group")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (3 times) and exit: the reference "
                          "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
@@ -90,14 +93,19 @@ def upload(w, inputs, torch):
     return out
 
 
+def blas_threads():
+    """Threads the oracle's NumPy BLAS runs on."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:
+        return 1
+
+
 def cpu_baseline(w, inputs, rows):
     """The oracle, as it stands, on `rows` query rows spread over the workload (all layers)."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        blas = 1
+    blas = blas_threads()
     types = ["full" if c == "F" else "shared" for c in w.layers]
     ke, ks = w.key_end(), w.key_start()
     picks = [(b, t) for b in range(w.B) for t in range(w.T)]
@@ -258,12 +266,83 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
-    if not args.no_cpu_baseline:
+    if args.backward:
+        res = backward(args, w, inputs, dev, cache, torch, B, stream)
+    elif not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_rows)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))
+
+
+# vector ALU fp32 peak without packed math: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP (FMA) x 2.4 GHz
+PEAK_VALU_F32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def backward(args, w, inputs, dev, cache, torch, B, stream):
+    """Sparse MLA backward of layer 0 on the forward group's indices and layer-0 results."""
+    L = dev[0]
+    R = w.Dc + w.Dr
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
+    dout = torch.randn(w.B, w.T, w.Hm, w.Dc, device="cuda", generator=g).to(L["out"].dtype)
+    dq = torch.empty(w.B, w.T, w.Hm, R, device="cuda")
+    dkv = torch.empty(w.B, w.S, R, device="cuda")
+    idx = cache.indices
+
+    def call():
+        B.sparse_mla_backward(L["q"], L["kv"], idx, w.sm_scale, L["out"], L["lse"], dout, dq, dkv, Dc=w.Dc,
+                              stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    pairs = float((idx >= 0).sum().item())
+    flops = pairs * w.Hm * 2.0 * (3 * R + 2 * w.Dc)
+    ach = flops / (t_ms * 1e-3) / 1e12
+    res = {
+        "metric": "query tokens/s through one layer's sparse MLA backward (dq, dkv)", "value":
+            w.B * w.T / (elapsed / args.steps), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.mla_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "sparse MLA backward, layer 0", "batch": w.B,
+                   "queries_per_item": w.T, "prefix": w.S, "topk": w.topk, "mla_heads": w.Hm,
+                   "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_VALU_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_VALU_F32_TFLOPS, "traffic": None, "kernel": "mla_bwd",
+                     "algorithmic_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        print("[bench] timing the CPU oracle backward on a row sample", file=sys.stderr, flush=True)
+        idx_h = idx.cpu().numpy()
+        dout_h = dout.to(torch.float64).cpu().numpy()
+        q_h = O.decode(inputs[0]["mla_q"], w.mla_dtype)
+        picks = [(b, t) for b in range(w.B) for t in range(w.T)]
+        n = min(len(picks), max(1, args.cpu_rows))
+        sel = [picks[i] for i in np.linspace(0, len(picks) - 1, n).astype(int)]
+        kv_h = {}
+        t0 = time.perf_counter()
+        for (b, t) in sel:
+            if b not in kv_h:
+                kv_h[b] = O.decode(inputs[0]["kv"][b], w.mla_dtype)
+            O.sparse_mla_backward_row(q_h[b, t], kv_h[b], idx_h[b, t], w.sm_scale, w.Dc, dout_h[b, t])
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n / dt, "unit": "query tokens/s", "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{n} query rows evenly spaced over the {w.B}x{w.T} rows of {w.name}, "
+                                         f"layer 0 backward, float64 NumPy, {dt:.1f} s (input decoding included)"}
+    return res
 
 
 if __name__ == "__main__":
