@@ -136,6 +136,46 @@ def index_scores(q: np.ndarray, k: np.ndarray, w: np.ndarray,
     return out
 
 
+def index_scores_backward_selected(q: np.ndarray, k: np.ndarray, w: np.ndarray, idx: np.ndarray,
+                                   dI: np.ndarray):
+    """Gradient of the index scores at the selected positions, by the chain rule through
+    I[t, s] = sum_h w[t, h] max(0, q[t, h] . k[s, g(h)]) (section 1 of the IndexShare page;
+    reading as in index_scores).  q [B,T,H,D] and k [B,S,Hk,D] are the dequantised inputs,
+    w [B,T,H]; dI [B,T,kk] is a loss gradient with respect to I[b, t, idx[b, t, j]] (slots
+    whose position lies outside [0, S) are ignored).  With s = q[t,h] . k[j,g(h)]:
+
+        dw[t, h]      = sum_j dI_j max(0, s)
+        dq[t, h]      = sum_j dI_j w[t, h] [s > 0] k[j, g(h)]
+        dk[j, g(h)]  += dI_j w[t, h] [s > 0] q[t, h]
+
+    The derivative of max(0, s) at s = 0 is taken as 0.  Returns (dq, dk, dw) float64."""
+    B, T, H, D = q.shape
+    S, Hk = k.shape[1], k.shape[2]
+    g = np.arange(H) if Hk == H else np.zeros(H, np.int64)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dw = np.zeros(w.shape)
+    for b in range(B):
+        for t in range(T):
+            sel = np.asarray(idx[b, t], dtype=np.int64)
+            ok = (sel >= 0) & (sel < S)
+            sel, gr = sel[ok], np.asarray(dI[b, t], dtype=np.float64)[ok]
+            if sel.size == 0:
+                continue
+            kk = k[b][sel][:, g, :]                                   # [J, H, D]
+            sc = np.einsum("hd,jhd->jh", q[b, t], kk)                 # [J, H]
+            on = sc > 0
+            dw[b, t] = (gr[:, None] * np.where(on, sc, 0.0)).sum(axis=0)
+            coef = gr[:, None] * w[b, t][None, :] * on                # [J, H]
+            dq[b, t] = np.einsum("jh,jhd->hd", coef, kk)
+            contrib = coef[:, :, None] * q[b, t][None, :, :]          # [J, H, D]
+            if Hk == H:
+                np.add.at(dk[b], sel, contrib)
+            else:
+                np.add.at(dk[b], sel, contrib.sum(axis=1, keepdims=True))
+    return dq, dk, dw
+
+
 # ------------------------------------------------------------------ top-k
 
 

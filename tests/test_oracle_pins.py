@@ -550,3 +550,71 @@ def test_sparse_mla_backward_single_row_and_empty_selection():
     want = np.zeros((S, Dc + Dr))
     want[4, :Dc] = dout[0, 0].sum(axis=0)
     np.testing.assert_allclose(dkv[0], want, atol=1e-14)
+
+
+# ---------------------------------------------------------------- index score backward
+
+def _index_loss(q, k, w, idx, dI):
+    """sum over selected slots of dI * I at the slot's position, from the forward oracle."""
+    B, T = q.shape[:2]
+    S = k.shape[1]
+    I = O.index_scores(q, k, w, np.zeros((B, T), np.int64), np.full((B, T), S, np.int64))
+    tot = 0.0
+    for b in range(B):
+        for t in range(T):
+            for j, s in enumerate(idx[b, t]):
+                if 0 <= s < S:
+                    tot += dI[b, t, j] * I[b, t, s]
+    return tot
+
+
+@pytest.mark.parametrize("Hk", [3, 1])
+def test_index_backward_matches_central_differences(Hk):
+    """Every gradient entry against a central difference of the forward oracle; scores are
+    kept away from the ReLU kink so that the difference quotient is that of one branch."""
+    rng = np.random.default_rng(81 + Hk)
+    B, T, S, H, D, kk = 2, 2, 6, 3, 4, 4
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, S, Hk, D))
+    w = rng.random((B, T, H))
+    idx = np.array([[[0, 5, -1, 2], [3, 3, 1, 4]], [[5, -1, -1, -1], [1, 0, 2, 3]]])
+    dI = rng.standard_normal((B, T, kk))
+    g = np.arange(H) if Hk == H else np.zeros(H, int)
+    for b in range(B):
+        for t in range(T):
+            for s in range(S):
+                for h in range(H):
+                    while abs(q[b, t, h] @ k[b, s, g[h]]) < 0.05:
+                        k[b, s, g[h]] += 0.1
+    dq, dk, dw = O.index_scores_backward_selected(q, k, w, idx, dI)
+    eps = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (w, dw)):
+        num = np.zeros_like(arr)
+        for i in np.ndindex(arr.shape):
+            a0 = arr[i]
+            arr[i] = a0 + eps
+            lp = _index_loss(q, k, w, idx, dI)
+            arr[i] = a0 - eps
+            lm = _index_loss(q, k, w, idx, dI)
+            arr[i] = a0
+            num[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_index_backward_closed_forms():
+    """w = 0: no q or k gradient, dw = sum_j dI_j max(0, s); a single selected key with
+    all scores positive: dq = dI w k, dk = dI sum_h w_h q_h (shared key)."""
+    rng = np.random.default_rng(83)
+    q = np.abs(rng.standard_normal((1, 1, 4, 8)))
+    k = np.abs(rng.standard_normal((1, 5, 1, 8)))
+    w = rng.random((1, 1, 4))
+    idx = np.array([[[2, -1]]])
+    dI = np.array([[[0.7, 5.0]]])
+    dq, dk, dw = O.index_scores_backward_selected(q, k, np.zeros_like(w), idx, dI)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_allclose(dw[0, 0], 0.7 * (q[0, 0] @ k[0, 2, 0]), rtol=1e-14)
+    dq, dk, dw = O.index_scores_backward_selected(q, k, w, idx, dI)
+    np.testing.assert_allclose(dq[0, 0], 0.7 * w[0, 0][:, None] * k[0, 2, 0][None, :], rtol=1e-14)
+    want = np.zeros((5, 1, 8))
+    want[2, 0] = 0.7 * (w[0, 0][:, None] * q[0, 0]).sum(axis=0)
+    np.testing.assert_allclose(dk[0], want, rtol=1e-14)
