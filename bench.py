@@ -50,8 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--backward", action="store_true",
-                    help="time the sparse MLA backward of layer 0 (its forward's indices, output and lse, a "
-                         "seeded output gradient) instead of the forward group")
+                    help="time layer 0's backward instead of the forward group: the sparse MLA backward (its "
+                         "forward's indices, output and lse, a seeded output gradient) and the index-score "
+                         "backward at the selected positions (a seeded score gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (3 times) and exit: the reference "
                          "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
@@ -281,46 +282,65 @@ PEAK_VALU_F32_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
 def backward(args, w, inputs, dev, cache, torch, B, stream):
-    """Sparse MLA backward of layer 0 on the forward group's indices and layer-0 results."""
+    """Layer 0's backward on the forward group's indices and layer-0 results: the sparse MLA
+    backward and the index-score backward at the selected positions, back to back."""
     L = dev[0]
     R = w.Dc + w.Dr
     g = torch.Generator(device="cuda").manual_seed(w.seed + 1000)
     dout = torch.randn(w.B, w.T, w.Hm, w.Dc, device="cuda", generator=g).to(L["out"].dtype)
+    dI = torch.randn(w.B, w.T, w.topk, device="cuda", generator=g)
     dq = torch.empty(w.B, w.T, w.Hm, R, device="cuda")
     dkv = torch.empty(w.B, w.S, R, device="cuda")
+    I = L["index"]
+    dqi = torch.empty(w.B, w.T, w.H, w.D, device="cuda")
+    dki = torch.empty(w.B, w.S, w.Hk, w.D, device="cuda")
+    dwi = torch.empty(w.B, w.T, w.H, device="cuda")
     idx = cache.indices
 
-    def call():
+    def call(ev=None):
+        if ev:
+            ev[0].record(stream)
         B.sparse_mla_backward(L["q"], L["kv"], idx, w.sm_scale, L["out"], L["lse"], dout, dq, dkv, Dc=w.Dc,
                               stream=stream)
+        if ev:
+            ev[1].record(stream)
+        B.index_backward(I["q"], I["k"], I["w"], idx, dI, dqi, dki, dwi, q_scale=I.get("q_scale"),
+                         k_scale=I.get("k_scale"), stream=stream)
+        if ev:
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         call()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
-    for _ in range(args.steps):
-        call()
-    ev[1].record(stream)
+    for st in range(args.steps):
+        call(evs[st])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    t_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    t_mla = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_idx = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     pairs = float((idx >= 0).sum().item())
     flops = pairs * w.Hm * 2.0 * (3 * R + 2 * w.Dc)
-    ach = flops / (t_ms * 1e-3) / 1e12
+    iflops = pairs * w.H * 2.0 * 3 * w.D
+    ach = flops / (t_mla * 1e-3) / 1e12
+    iach = iflops / (t_idx * 1e-3) / 1e12
+    dom_mla = t_mla >= t_idx
     res = {
-        "metric": "query tokens/s through one layer's sparse MLA backward (dq, dkv)", "value":
-            w.B * w.T / (elapsed / args.steps), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": "query tokens/s through one layer's backward (sparse MLA dq, dkv; index score dq, dk, dw)",
+        "value": w.B * w.T / (elapsed / args.steps), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.mla_dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "pass": "sparse MLA backward, layer 0", "batch": w.B,
-                   "queries_per_item": w.T, "prefix": w.S, "topk": w.topk, "mla_heads": w.Hm,
-                   "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": ach, "peak": PEAK_VALU_F32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_VALU_F32_TFLOPS, "traffic": None, "kernel": "mla_bwd",
-                     "algorithmic_per_launch": flops},
+        "config": {"workload": w.name, "pass": "backward, layer 0", "batch": w.B, "queries_per_item": w.T,
+                   "prefix": w.S, "topk": w.topk, "index_heads": w.H, "index_dim": w.D, "index_key_heads": w.Hk,
+                   "index_dtype": w.idx_dtype, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": ach if dom_mla else iach, "peak": PEAK_VALU_F32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": (ach if dom_mla else iach) / PEAK_VALU_F32_TFLOPS, "traffic": None,
+                     "kernel": "mla_bwd" if dom_mla else "index_bwd",
+                     "algorithmic_per_launch": flops if dom_mla else iflops},
+        "kernels": {"sparse_mla_bwd": {"ms": t_mla, "tflops": ach}, "index_bwd": {"ms": t_idx, "tflops": iach}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -330,18 +350,30 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
         dout_h = dout.to(torch.float64).cpu().numpy()
         q_h = O.decode(inputs[0]["mla_q"], w.mla_dtype)
         picks = [(b, t) for b in range(w.B) for t in range(w.T)]
-        n = min(len(picks), max(1, args.cpu_rows))
+        n = min(len(picks), max(1, args.cpu_rows // 8))
         sel = [picks[i] for i in np.linspace(0, len(picks) - 1, n).astype(int)]
-        kv_h = {}
+        dI_h = dI.to(torch.float64).cpu().numpy()
+        I0 = inputs[0]
+        kv_h, k_h = {}, {}
         t0 = time.perf_counter()
         for (b, t) in sel:
             if b not in kv_h:
                 kv_h[b] = O.decode(inputs[0]["kv"][b], w.mla_dtype)
+                k_h[b] = O.decode(I0["idx_k"][b], w.idx_dtype, I0["idx_k_scale"][b] if "idx_k_scale" in I0 else None)
             O.sparse_mla_backward_row(q_h[b, t], kv_h[b], idx_h[b, t], w.sm_scale, w.Dc, dout_h[b, t])
+            qi = O.decode(I0["idx_q"][b, t], w.idx_dtype, I0["idx_q_scale"][b, t] if "idx_q_scale" in I0 else None)
+            # the oracle on the row's selected keys only (same arithmetic, no full-size dk)
+            row = idx_h[b, t]
+            keys, pos = np.unique(row[row >= 0], return_inverse=True)
+            ridx = np.full_like(row, -1)
+            ridx[row >= 0] = pos
+            O.index_scores_backward_selected(qi[None, None], k_h[b][keys][None],
+                                             I0["w"][b, t][None, None].astype(np.float64), ridx[None, None],
+                                             dI_h[b, t][None, None])
         dt = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": n / dt, "unit": "query tokens/s", "cores": blas_threads(), "kind": "oracle",
                                "sample": f"{n} query rows evenly spaced over the {w.B}x{w.T} rows of {w.name}, "
-                                         f"layer 0 backward, float64 NumPy, {dt:.1f} s (input decoding included)"}
+                                         f"layer 0 backward (both), float64 NumPy, {dt:.1f} s (input decoding included)"}
     return res
 
 

@@ -72,6 +72,9 @@ _SIGS = {
                                     C.c_void_p, C.POINTER(GroupStats), C.c_void_p]),
     "dsa_group_stats_compute": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int, C.c_int32, C.c_void_p, C.c_void_p,
                                           C.c_void_p, C.POINTER(GroupStats)]),
+    "dsa_index_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                     C.c_void_p]),
     "dsa_sparse_mla_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dsa_index_prep": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
@@ -191,6 +194,18 @@ def sparse_mla_attention(q, kv, topk_indices, sm_scale, out, lse=None, *, Dc, wo
                                           _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
                                           _dev_ptr(workspace), ws_bytes, _stream(stream)))
     return out
+
+
+def index_backward(q, k, w, topk_indices, dI, dq, dk, dw, *, q_scale=None, k_scale=None, stream=None):
+    """dsa_index_backward.  Index inputs as for indexer_scores, topk_indices and dI [B,T,topk];
+    dq [B,T,H,D], dk [B,S,Hk,D] and dw [B,T,H] fp32 are written in place."""
+    B, T, H, D = q.shape
+    S, Hk = k.shape[1], k.shape[2]
+    shape = make_shape(B, T, S, H=H, D=D, Hk=Hk, topk=topk_indices.shape[-1])
+    _check(lib().dsa_index_backward(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(q_scale), _dev_ptr(k),
+                                    _dev_ptr(k_scale), _dev_ptr(w), _dev_ptr(topk_indices), _dev_ptr(dI),
+                                    _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dw), _stream(stream)))
+    return dq, dk, dw
 
 
 def sparse_mla_backward(q, kv, topk_indices, sm_scale, out, lse, dout, dq, dkv, *, Dc, stream=None):

@@ -217,6 +217,29 @@ dsa_status dsa_sparse_mla_backward(const dsa_shape* s, dsa_dtype dt, const void*
   return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA backward launch");
 }
 
+dsa_status dsa_index_backward(const dsa_shape* s, dsa_dtype dt, const void* q, const float* qs, const void* k,
+                              const float* ksc, const float* w, const int32_t* idx, const float* dI, float* dq,
+                              float* dk, float* dw, void* stream) {
+  dsa_status st = check_indexer_shape(s, dt);
+  if (st == DSA_OK) st = check_topk_shape(s);
+  if (st != DSA_OK) return st;
+  if (!dsa::index_bwd_supported(s->H, s->D, s->Hk))
+    return fail(DSA_ERR_UNSUPPORTED, "index backward: H=%d D=%d need H <= 64", s->H, s->D);
+  if (rows_of(s) > 0) {
+    if (!q || !w || !idx || !dI || !dq || !dw)
+      return fail(DSA_ERR_INVALID_ARG, "q, w, topk_indices, dI, dq and dw must be non-NULL");
+    if (dt == DSA_FP8_E4M3 && !qs) return fail(DSA_ERR_INVALID_ARG, "fp8 inputs need q_scale and k_scale");
+  }
+  if (s->s_cap > 0) {
+    if (!k || !dk) return fail(DSA_ERR_INVALID_ARG, "k and dk must be non-NULL");
+    if (dt == DSA_FP8_E4M3 && !ksc) return fail(DSA_ERR_INVALID_ARG, "fp8 inputs need q_scale and k_scale");
+  }
+  const dsa::IndexBwdParams p{s->B, s->T, s->H, s->D, s->Hk, s->topk, s->s_cap, q, qs, k, ksc, w, idx, dI,
+                              dq, dk, dw};
+  hipError_t e = dsa::launch_index_bwd(p, (dsa::Dtype)dt, (hipStream_t)stream, nullptr);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "index backward launch");
+}
+
 dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_layers,
                              const dsa_layer_type* types, const dsa_layer_io* layers, float sm_scale,
                              dsa_topk_cache* cache, uint64_t tag, void* ws, size_t ws_bytes, void* const* events,

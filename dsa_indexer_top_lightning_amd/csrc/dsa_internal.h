@@ -61,6 +61,22 @@ struct MlaBwdParams {
   float* dkv;           // [B,S,Dc+Dr]
 };
 
+// Backward of the index score at the selected positions.
+struct IndexBwdParams {
+  int B, T, H, D, Hk, topk;
+  int64_t s_cap;
+  const void* q;          // [B,T,H,D]
+  const float* q_scale;   // [B,T,H] (fp8)
+  const void* k;          // [B,S,Hk,D]
+  const float* k_scale;   // [B,S,Hk] (fp8)
+  const float* w;         // [B,T,H]
+  const int32_t* idx;     // [B,T,topk]
+  const float* dI;        // [B,T,topk]
+  float* dq;              // [B,T,H,D]
+  float* dk;              // [B,S,Hk,D]
+  float* dw;              // [B,T,H]
+};
+
 // New index vectors x [n, heads, D] fp32 -> RoPE -> out rows (bf16 or fp8 codes + scales).
 struct PrepParams {
   int n, heads, D;
@@ -95,6 +111,8 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_b
 size_t mla_bwd_lds_bytes(int Hm, int Dc, int Dr, Dtype dt);
 bool mla_bwd_supported(int Hm, int Dc, int Dr, Dtype dt);
 hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
+bool index_bwd_supported(int H, int D, int Hk);
+hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
 hipError_t launch_index_prep(const PrepParams& p, hipStream_t st);
 hipError_t launch_latent_append(const LatentAppendParams& p, hipStream_t st);
 

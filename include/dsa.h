@@ -235,6 +235,27 @@ dsa_status dsa_sparse_mla_backward(const dsa_shape* shape, dsa_dtype mla_dtype, 
                                    const float* lse, const void* dout, float* dq, float* dkv, void* stream);
 
 /*
+ * Backward of the index score at the selected positions (training the indexer: a loss
+ * on the scores of the kept positions, e.g. an auxiliary indexer loss, supplies dI).
+ * The score is dsa_indexer_scores' I[t,s] = sum_h w[t,h] max(0, q[t,h].k[s,g(h)]); with
+ * s = q[t,h].k[j,g(h)] and the ReLU derivative 0 at 0:
+ *   dw[t,h] = sum_j dI_j max(0, s),   dq[t,h] = sum_j dI_j w[t,h] [s > 0] k[j,g(h)],
+ *   dk[j,g(h)] += dI_j w[t,h] [s > 0] q[t,h].
+ * Gradients are with respect to the dequantised values (fp8 codes times their scales).
+ *   q, q_scale, k, k_scale, w: as for dsa_indexer_scores (shape->H, D, Hk, s_cap)
+ *   topk_indices [B,T,topk] int32 (slots outside [0, s_cap) are ignored)
+ *   dI  [B,T,topk] fp32, the gradient at each slot's position
+ *   dq  [B,T,H,D] fp32, dk [B,S,Hk,D] fp32, dw [B,T,H] fp32, all overwritten (dk is zeroed
+ *       by the call and collects contributions with fp32 atomics; for fewer than 1024
+ *       query tokens dq and dw do too: reproducible to fp32 rounding only)
+ * Requires H <= 64 (DSA_ERR_UNSUPPORTED otherwise) and the indexer's shape rules;
+ * DSA_ERR_INVALID_ARG on NULL pointers.  No workspace.
+ */
+dsa_status dsa_index_backward(const dsa_shape* shape, dsa_dtype idx_dtype, const void* q, const float* q_scale,
+                              const void* k, const float* k_scale, const float* w, const int32_t* topk_indices,
+                              const float* dI, float* dq, float* dk, float* dw, void* stream);
+
+/*
  * Decode-step preparation of new index vectors (the Megatron-Bridge pull request's
  * commit on the indexer RoPE half swap: the LAST D/2 dims of every index head are
  * rotated; rope_theta = 8e6 in its config fix).  For each vector x[i, h, :] (fp32,

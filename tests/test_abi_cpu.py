@@ -205,3 +205,20 @@ def test_index_prep_and_latent_append_validation(L):
     assert g(2, 576, b.FP8_E4M3, FAKE, FAKE, 10, FAKE, None) == 1
     assert g(2, 576, b.BF16, None, FAKE, 10, FAKE, None) == 1
     assert g(0, 576, b.BF16, None, None, 0, None, None) == 0
+
+
+def test_backward_validation(L):
+    shape = _shape(topk=8)
+    # sparse MLA backward: bad scale, unsupported head count, NULL pointers
+    f = L.dsa_sparse_mla_backward
+    args = lambda sh, sc=0.1, dq=FAKE: f(C.byref(sh), b.BF16, FAKE, FAKE, FAKE, sc, FAKE, FAKE, FAKE, dq, FAKE, None)
+    assert args(shape, sc=0.0) == 1
+    assert args(shape, dq=None) == 1
+    assert args(_shape(topk=8, Hm=128)) == 2
+    # index backward: unsupported heads, NULL pointers, fp8 without scales
+    g = L.dsa_index_backward
+    call = lambda sh, dt=b.BF16, qs=None, dI=FAKE: g(C.byref(sh), dt, FAKE, qs, FAKE, FAKE, FAKE, FAKE, dI, FAKE,
+                                                       FAKE, FAKE, None)
+    assert call(shape, dI=None) == 1
+    assert call(shape, dt=b.FP8_E4M3) == 1
+    assert call(_shape(topk=8, H=128, Hk=128)) == 2

@@ -1,10 +1,14 @@
-"""GPU parity of the sparse MLA backward (dsa_sparse_mla_backward) against the oracle.
+"""GPU parity of the backward calls (dsa_sparse_mla_backward, dsa_index_backward) against
+the oracle.
 
 The GPU takes the forward's own results (output, log-sum-exp) from dsa_sparse_mla_attention
 on the same inputs; the oracle recomputes everything in float64 from the stored inputs.
 Bars as for the forward: max-abs-relative error <= 1e-5 (fp32) and <= 2e-2 (bf16) per
 gradient tensor.  The latent-row gradient collects its contributions with fp32 atomics
-in no fixed order, which the fp32 bar covers.
+in no fixed order, which the fp32 bar covers.  The index-score backward computes with
+exact products and fp32 sums, so all of its gradients are held to 1e-5 for every input
+type; slots whose score lies within rounding of the ReLU kink get no gradient in the
+test (the two sides could take different branches there).
 """
 import numpy as np
 import pytest
@@ -88,3 +92,81 @@ def test_sparse_mla_backward_empty_selections():
     idx[:] = -1
     dq, dkv = _run(q, kv, dout, idx, Dc, 0.1, "f32")
     assert np.all(dq == 0) and np.all(dkv == 0)
+
+
+# ------------------------------------------------------------------ index score backward
+
+def _index_inputs(rng, B, T, S, H, D, Hk, k, dtype):
+    """Stored device inputs and their dequantised float64 values (oracle side)."""
+    if dtype == "fp8":
+        def codes(shape):
+            c = rng.integers(0, 126, shape).astype(np.uint8) | (rng.integers(0, 2, shape).astype(np.uint8) << 7)
+            return c
+        qc, kc = codes((B, T, H, D)), codes((B, S, Hk, D))
+        qs = (rng.random((B, T, H)) * 0.02 + 0.001).astype(np.float32)
+        ks = (rng.random((B, S, Hk)) * 0.02 + 0.001).astype(np.float32)
+        qh = O.decode(qc, "fp8", qs)
+        kh = O.decode(kc, "fp8", ks)
+        dev = (torch.from_numpy(qc).cuda().view(torch.float8_e4m3fn), torch.from_numpy(kc).cuda().view(torch.float8_e4m3fn),
+               torch.from_numpy(qs).cuda(), torch.from_numpy(ks).cuda())
+    else:
+        q = torch.from_numpy(rng.standard_normal((B, T, H, D)).astype(np.float32))
+        kk = torch.from_numpy(rng.standard_normal((B, S, Hk, D)).astype(np.float32))
+        if dtype == "bf16":
+            q, kk = q.to(torch.bfloat16), kk.to(torch.bfloat16)
+        qh, kh = q.to(torch.float64).numpy(), kk.to(torch.float64).numpy()
+        dev = (q.cuda(), kk.cuda(), None, None)
+    w = rng.random((B, T, H)).astype(np.float32)
+    idx = np.full((B, T, k), -1, np.int32)
+    for bb in range(B):
+        for t in range(T):
+            n = int(rng.integers(1, k + 1)) if t % 2 else k
+            idx[bb, t, :n] = rng.choice(S, size=n, replace=False)
+    if T > 1 and k > 2:
+        idx[0, 1, 1] = idx[0, 1, 0]        # a key listed twice
+    dI = rng.standard_normal((B, T, k)).astype(np.float32)
+    # a score within rounding of 0 could take the other ReLU branch on the GPU: give
+    # such slots no gradient, so that both sides agree on every branch that counts
+    g = np.arange(H) if Hk == H else np.zeros(H, int)
+    for bb in range(B):
+        for t in range(T):
+            for j in range(k):
+                e = idx[bb, t, j]
+                if e < 0:
+                    continue
+                prod = qh[bb, t] * kh[bb, e][g]
+                if np.any(np.abs(prod.sum(axis=1)) <= 1e-4 * np.abs(prod).sum(axis=1)):
+                    dI[bb, t, j] = 0.0
+    return dev, qh, kh, w, idx, dI
+
+
+INDEX_BWD_CASES = {
+    # name: (B, T, S, H, D, Hk, k, dtype)
+    "fp32_small": (2, 5, 60, 4, 32, 4, 10, "f32"),
+    "bf16_heads": (1, 6, 300, 32, 128, 32, 64, "bf16"),
+    "bf16_shared_key": (1, 6, 300, 32, 128, 1, 64, "bf16"),
+    "fp8_heads": (1, 5, 200, 32, 128, 32, 48, "fp8"),
+    "fp8_shared_key": (2, 3, 200, 32, 128, 1, 48, "fp8"),
+    "bf16_decode": (3, 1, 3000, 32, 128, 32, 2048, "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(INDEX_BWD_CASES))
+def test_index_backward_matches_oracle(name):
+    B, T, S, H, D, Hk, k, dtype = INDEX_BWD_CASES[name]
+    rng = np.random.default_rng(200 + list(INDEX_BWD_CASES).index(name))
+    (qd, kd, qsd, ksd), qh, kh, w, idx, dI = _index_inputs(rng, B, T, S, H, D, Hk, k, dtype)
+    dq = torch.full((B, T, H, D), float("nan"), device="cuda")
+    dk = torch.full((B, S, Hk, D), float("nan"), device="cuda")
+    dw = torch.full((B, T, H), float("nan"), device="cuda")
+    b.index_backward(qd, kd, torch.from_numpy(w).cuda(), torch.from_numpy(idx).cuda(), torch.from_numpy(dI).cuda(),
+                     dq, dk, dw, q_scale=qsd, k_scale=ksd)
+    torch.cuda.synchronize()
+    rq, rk, rw = O.index_scores_backward_selected(qh, kh, w.astype(np.float64), idx, dI.astype(np.float64))
+    for got, ref in ((dq, rq), (dk, rk), (dw, rw)):
+        g = got.cpu().numpy().astype(np.float64)
+        assert max_abs_rel(g, ref) <= 1e-5, (max_abs_rel(g, ref), got.shape)
+    sel = np.zeros((B, S), bool)
+    for bb in range(B):
+        sel[bb, idx[bb][idx[bb] >= 0]] = True
+    assert np.all(dk.cpu().numpy()[~sel] == 0.0)     # keys nobody selected: exactly zero
