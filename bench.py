@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--workload", default="prefill4k_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one group call as a HIP graph and time K replays (reported beside the "
+                         "eager figures)")
     ap.add_argument("--backward", action="store_true",
                     help="time layer 0's backward instead of the forward group: the sparse MLA backward (its "
                          "forward's indices, output and lse, a seeded output gradient) and the index-score "
@@ -94,6 +97,24 @@ def upload(w, inputs, torch):
     return out
 
 
+def host_info():
+    """CPU model, logical CPUs and the CPUs this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity": aff, "blas_threads": blas_threads()}
+
+
 def blas_threads():
     """Threads the oracle's NumPy BLAS runs on."""
     try:
@@ -118,6 +139,7 @@ def cpu_baseline(w, inputs, rows):
         if types[l] == "full":
             dec[l]["k"] = {}
     done = 0
+    phase = {"score": 0.0, "sort": 0.0, "attention": 0.0}
     for (b, t) in sel:
         idx = None
         for l, L in enumerate(inputs):
@@ -126,19 +148,27 @@ def cpu_baseline(w, inputs, rows):
                     dec[l]["k"][b] = O.decode(L["idx_k"][b], w.idx_dtype, L.get("idx_k_scale", [None] * w.B)[b]
                                               if "idx_k_scale" in L else None)
                 qs = L["idx_q_scale"][b, t] if "idx_q_scale" in L else None
+                p0 = time.perf_counter()
                 q = O.decode(L["idx_q"][b, t], w.idx_dtype, qs)
                 row = O.index_scores_row(q, dec[l]["k"][b], L["w"][b, t].astype(np.float64),
                                          int(ks[b, t]), int(ke[b, t]))
+                p1 = time.perf_counter()
                 idx, _ = O.topk_row(row, int(ks[b, t]), int(ke[b, t]), w.topk)
+                p2 = time.perf_counter()
+                phase["score"] += p1 - p0
+                phase["sort"] += p2 - p1
             if b not in dec[l]["kv"]:
                 dec[l]["kv"][b] = O.decode(L["kv"][b], w.mla_dtype)
+            p0 = time.perf_counter()
             O.sparse_mla_row(O.decode(L["mla_q"][b, t], w.mla_dtype), dec[l]["kv"][b], idx, w.sm_scale, w.Dc)
+            phase["attention"] += time.perf_counter() - p0
         done += 1
     dt = time.perf_counter() - t0
     return {"value": done / dt * w.n_layers / 4.0, "unit": "query tokens/s", "cores": int(blas),
             "kind": "oracle",
             "sample": f"{done} query rows evenly spaced over the {w.B}x{w.T} rows of {w.name}, all "
-                      f"{w.n_layers} layers, float64 NumPy, {dt:.1f} s (input decoding included)"}
+                      f"{w.n_layers} layers, float64 NumPy, {dt:.1f} s (input decoding included)",
+            "phase_s": {k: round(v, 2) for k, v in phase.items()}, "host": host_info()}
 
 
 def main():
@@ -255,7 +285,29 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = MEASURED_TRAFFIC_BYTES.get((w.name, roof["kernel"])) if MEASURED_TRAFFIC_BYTES else None
 
+    # per-step device times from the library's first and last event records of each call
+    step_dev = [events[s][0].elapsed_time(events[s][6 * n - 1]) for s in range(steps)]
+    pct = {f"p{q}": float(np.percentile(step_dev, q)) for q in (10, 50, 90)}
+
     tokens = w.B * w.T
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=side)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gel = time.perf_counter() - t0
+        graph = {"ms_per_step": gel / steps * 1e3, "value": tokens / (gel / steps) * n / 4.0}
     value = tokens / (elapsed / steps) * n / 4.0
     res = {
         "metric": METRIC, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": steps,
@@ -266,12 +318,22 @@ def main():
                    "topk": w.topk, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"},
         "roofline": roof,
         "kernels": kernels,
+        "step_device_ms": pct,
+        "graph": graph,
     }
     if args.backward:
         res = backward(args, w, inputs, dev, cache, torch, B, stream)
     elif not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_rows)
+        try:  # the same oracle on one thread, on a smaller sample
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(limits=1):
+                one = cpu_baseline(w, inputs, max(1, args.cpu_rows // 16))
+            res["cpu_baseline"]["one_core"] = {"value": one["value"], "sample": one["sample"],
+                                               "blas_threads": one["host"]["blas_threads"]}
+        except ImportError:
+            pass
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res))
