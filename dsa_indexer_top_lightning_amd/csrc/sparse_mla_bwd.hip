@@ -13,14 +13,14 @@
 //
 // mla_bwd: one workgroup of 8 waves per query token; the token's queries and output
 // gradients sit in LDS in their storage type, wave w takes heads w, w+8, ... with its
-// lanes over the row's values (lane + 64 i) and sums over lanes by DPP moves.  Selected rows are taken two at a time
-// into LDS as fp32; each wave adds its heads' share of the two rows' gradients into an
-// LDS sum (ds_add_f32), and the workgroup then adds the sums to the latent-row
-// gradient in global memory with one fp32 atomic per value (rows shared by several
-// queries, or listed twice, collect every contribution; the order of those additions
-// is not fixed, so dkv is reproducible to fp32 rounding only).  dq is written whole,
-// except for few query tokens (decode), whose selections are split over several
-// workgroups that add their shares of dq with atomics.
+// lanes over the row's values (lane + 64 i) and sums over lanes by DPP moves.  Selected
+// rows are taken two at a time into LDS as fp32; each wave adds its heads' share of the
+// two rows' gradients into an LDS sum (ds_add_f32), and the workgroup then adds the sums
+// to the latent-row gradient in global memory with one fp32 atomic per value (rows
+// shared by several queries, or listed twice, collect every contribution; the order of
+// those additions is not fixed, so dkv is reproducible to fp32 rounding only).  dq is
+// written whole, except for few query tokens (decode), whose selections are split over
+// several workgroups that add their shares of dq with atomics.
 #include "dsa_internal.h"
 
 namespace dsa {
