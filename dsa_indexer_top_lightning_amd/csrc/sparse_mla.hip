@@ -168,57 +168,11 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   const int topk = p.topk;
   const int32_t* gidx = p.idx + tok * (int64_t)topk;
 
-  // ---- tiles of this split up to the last one holding a valid entry: [t0, t0 + ntiles)
+  // ---- prologue: the entry copies of the first two tiles, the query copy and the scan
+  //      for the last valid entry are all issued before any of them is waited for, so
+  //      the workgroup pays one global round trip before its first gather
   const int t0 = split * tiles_per_split;
   const int e_lo = t0 * MT, e_hi = min(topk, (t0 + tiles_per_split) * MT);
-  int emax = -1;
-  for (int e0 = e_lo; e0 < e_hi; e0 += 16 * 64) {  // 16 independent loads in flight per lane
-    int32_t v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = e0 + 64 * u + lane;
-      v[u] = e < e_hi ? gidx[e] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (v[u] >= 0 && (int64_t)v[u] < s_cap) emax = e0 + 64 * u + lane;
-  }
-  for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
-  const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
-
-  const int head0 = hg * MHG + 32 * hh;
-  const int myhead = head0 + lr;
-  if (ntiles == 0) {
-    if (nsplit == 1) {
-      uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + hg * MHG) * MDC;
-      for (int i = tid; i < MHG * MDC; i += 256) og[i] = 0;
-      if (p.lse && vv == 0 && lg == 0) p.lse[tok * p.Hm + myhead] = -__builtin_inff();
-    } else if (vv == 0 && lg == 0) {
-      float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + myhead) * 2;
-      ml[0] = -__builtin_inff();
-      ml[1] = 0.f;
-    }
-    return;
-  }
-
-  // ---- Q^T fragments for the whole kernel: lane (head lr, group lg) holds
-  //      q[head][16*st + 8*lg .. +7] for st = 0..35
-  bf16x8 qf[MROW / 16];
-  {
-    const unsigned char* qg = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + myhead) * MRB;
-#pragma unroll
-    for (int st = 0; st < MROW / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8*>(qg + (16 * st + 8 * lg) * 2);
-    // opaque to the compiler from here on (under register pressure it would otherwise
-    // re-load the query from global memory on every tile); the 512 latent dims live in
-    // accumulation registers, which the matrix cores read directly, leaving the vector
-    // registers for deeper LDS prefetch
-#pragma unroll
-    for (int st = 0; st < MDC / 16; ++st) asm volatile("" : "+a"(qf[st]));
-#pragma unroll
-    for (int st = MDC / 16; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
-  }
-
-  const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
   // The entries of tile t are copied by each wave into its own LDS ring slot t % 4 with
   // one 4-byte global-to-LDS load (lane i writes word i), so that no register carries a
   // pending load across tiles.  Past the end the loads re-read the last entry (never used).
@@ -226,6 +180,8 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   const uint32_t ering_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int32_t*)ering;
   auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
   auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
+
+  const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
   auto valid = [&](int32_t v) -> bool { return v >= 0 && (int64_t)v < s_cap; };
   struct GatherSrc {
     const unsigned char* a[2];
@@ -288,13 +244,81 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     for (int k = 0; k < 6; ++k) gather_part(k, bf, g);
   };
 
+
+  fetch_entries(0);
+  fetch_entries(1);
+  // The query's 64 head rows (1152 contiguous bytes each) are copied into the second tile
+  // buffer in the tile layout, whole cache lines per load, by the same copies as a tile's
+  // gather (row r = head 64hg + r); the first gather into that buffer is issued in tile 0,
+  // after every wave has read its fragments.
+  {
+    const unsigned char* qrows = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + hg * MHG) * MRB;
+    GatherSrc gq;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * wave + 8 * q + (lane >> 3);
+      gq.a[q] = qrows + row * MRB + 16 * ((lane & 7) ^ perm(row));
+    }
+    gather(1, gq);
+  }
+
+  // tiles of this split up to the last one holding a valid entry: [t0, t0 + ntiles)
+  int emax = -1;
+  for (int e0 = e_lo; e0 < e_hi; e0 += 32 * 64) {  // 32 independent loads in flight per lane
+    int32_t v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      const int e = e0 + 64 * u + lane;
+      v[u] = e < e_hi ? gidx[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u)
+      if (v[u] >= 0 && (int64_t)v[u] < s_cap) emax = e0 + 64 * u + lane;
+  }
+  for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+  const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
+
+  const int head0 = hg * MHG + 32 * hh;
+  const int myhead = head0 + lr;
+  wait_vmem();  // entry and query copies of this wave have landed
+  if (ntiles == 0) {
+    if (nsplit == 1) {
+      uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + hg * MHG) * MDC;
+      for (int i = tid; i < MHG * MDC; i += 256) og[i] = 0;
+      if (p.lse && vv == 0 && lg == 0) p.lse[tok * p.Hm + myhead] = -__builtin_inff();
+    } else if (vv == 0 && lg == 0) {
+      float* ml = ws_ml + ((tok * nsplit + split) * p.Hm + myhead) * 2;
+      ml[0] = -__builtin_inff();
+      ml[1] = 0.f;
+    }
+    return;
+  }
+  lds_barrier();  // ... and those of every wave
+
+  // Q^T fragments for the whole kernel: lane (head lr, group lg) holds
+  // q[head][16*st + 8*lg .. +7] for st = 0..35 (row 32hh + lr of the copy, logical chunk
+  // 2st + lg: segment st/4, chunk-in-segment 2(st%4) + lg)
+  bf16x8 qf[MROW / 16];
+  {
+    const int qr = 32 * hh + lr;
+    const unsigned char* qt = smem + TILE_BYTES + qr * SEG;
+#pragma unroll
+    for (int st = 0; st < MROW / 16; ++st)
+      qf[st] = *reinterpret_cast<const bf16x8*>(qt + (st >> 2) * GROUP_BYTES + 16 * ((2 * (st & 3) + lg) ^ perm(qr)));
+  }
+  // the query fragments are opaque to the compiler from here on (under register pressure
+  // it would otherwise re-read them on every tile); the 512 latent dims live in
+  // accumulation registers, which the matrix cores read directly, leaving the vector
+  // registers for deeper LDS prefetch
+#pragma unroll
+  for (int st = 0; st < MDC / 16; ++st) asm volatile("" : "+a"(qf[st]));
+#pragma unroll
+  for (int st = MDC / 16; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
+
   // Entries are fetched two tiles ahead of their gather and every gather is followed by
   // exactly one entry fetch, so at the top of tile i `vmcnt(1)` leaves only the newest
   // entry fetch in flight: the gather of tile i has landed and so have the entries of
   // tile i + 1, without waiting for anything issued later.
-  fetch_entries(0);
-  fetch_entries(1);
-  wait_vmem();
   uint64_t vmask_nxt;
   {
     const int32_t e0 = read_entry(0);
@@ -416,17 +440,12 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = 32 * vv + 8 * (r >> 2) + 4 * lg + (r & 3);
-        s[r] = ((vmask >> m) & 1ull) ? s[r] * qk_scale : -__builtin_inff();
-        mx = fmaxf(mx, s[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] *= qk_scale;
-        mx = fmaxf(mx, s[r]);
+        s[r] = ((vmask >> m) & 1ull) ? s[r] : -__builtin_inff();
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qk_scale;
 
     // P of the own block against the running max.  A wave whose tile maximum exceeds the
     // running max of one of its heads by more than 2^8 raises a flag; the flags travel
@@ -435,10 +454,11 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     uint32_t own[8];
     auto make_p = [&]() {
       const float m_own = hh ? m1 : m0;
-      const float m_use = m_own == -__builtin_inff() ? 0.f : m_own;
+      const float m_neg = m_own == -__builtin_inff() ? 0.f : -m_own;
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * r] - m_use), __builtin_amdgcn_exp2f(s[2 * r + 1] - m_use));
+        own[r] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[2 * r], qk_scale, m_neg)),
+                             __builtin_amdgcn_exp2f(fmaf(s[2 * r + 1], qk_scale, m_neg)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         xpv[(2 * wave + j) * 64 + lane] = i32x4{(int)own[4 * j], (int)own[4 * j + 1], (int)own[4 * j + 2], (int)own[4 * j + 3]};
@@ -471,8 +491,9 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
     {
       float ls = 0.f;  // the probabilities actually used, as rounded to bf16
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int r = 0; r < 8; ++r) ls += __uint_as_float(own[r] << 16) + __uint_as_float(own[r] & 0xffff0000u);
+      for (int r = 0; r < 8; ++r) ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, own[r]), ones, ls, false);
       l_part += ls;
     }
 
