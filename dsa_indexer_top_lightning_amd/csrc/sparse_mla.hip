@@ -262,25 +262,32 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     gather(1, gq);
   }
 
-  // tiles of this split up to the last one holding a valid entry: [t0, t0 + ntiles)
+  // The last valid entry: each wave scans every fourth 64-entry block of the split's
+  // entries (8 independent loads in flight per lane) and the four wave maxima meet in LDS
+  // at the barrier that also publishes the query copy.
   int emax = -1;
-  for (int e0 = e_lo; e0 < e_hi; e0 += 32 * 64) {  // 32 independent loads in flight per lane
-    int32_t v[32];
+  for (int e0 = e_lo + 64 * wv; e0 < e_hi; e0 += 8 * 256) {
+    int32_t v[8];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      const int e = e0 + 64 * u + lane;
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 256 * u + lane;
       v[u] = e < e_hi ? gidx[e] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < 32; ++u)
-      if (v[u] >= 0 && (int64_t)v[u] < s_cap) emax = e0 + 64 * u + lane;
+    for (int u = 0; u < 8; ++u)
+      if (v[u] >= 0 && (int64_t)v[u] < s_cap) emax = e0 + 256 * u + lane;
   }
   for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
-  const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
+  int* xemax = reinterpret_cast<int*>(xmax);  // free until the first tile
+  if (lane == 0) xemax[wv] = emax;
 
   const int head0 = hg * MHG + 32 * hh;
   const int myhead = head0 + lr;
-  wait_vmem();  // entry and query copies of this wave have landed
+  wait_vmem();    // entry and query copies of this wave have landed
+  lds_barrier();  // ... and those of every wave, and every wave's scan result
+  emax = max(max(xemax[0], xemax[1]), max(xemax[2], xemax[3]));
+  // tiles of this split up to the last one holding a valid entry: [t0, t0 + ntiles)
+  const int ntiles = emax < 0 ? 0 : emax / MT - t0 + 1;
   if (ntiles == 0) {
     if (nsplit == 1) {
       uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + hg * MHG) * MDC;
@@ -293,7 +300,6 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
     return;
   }
-  lds_barrier();  // ... and those of every wave
 
   // Q^T fragments for the whole kernel: lane (head lr, group lg) holds
   // q[head][16*st + 8*lg .. +7] for st = 0..35 (row 32hh + lr of the copy, logical chunk
