@@ -180,6 +180,9 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   const uint32_t ering_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int32_t*)ering;
   auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
   auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
+  // lanes of tile t past the split's last entry hold a clamped copy of that entry, not one
+  // of their own: they never count as selected
+  auto in_split = [&](int t) -> bool { return (t0 + t) * MT + lane < e_hi; };
 
   const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
   auto valid = [&](int32_t v) -> bool { return v >= 0 && (int64_t)v < s_cap; };
@@ -328,7 +331,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
   uint64_t vmask_nxt;
   {
     const int32_t e0 = read_entry(0);
-    vmask_nxt = __ballot(valid(e0));
+    vmask_nxt = __ballot(valid(e0) && in_split(0));
     gather(0, gather_src(e0));
   }
   fetch_entries(2);
@@ -396,7 +399,7 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     GatherSrc gnext;
     if (more) {
       const int32_t e_next = read_entry(i + 1);
-      vmask_nxt = __ballot(valid(e_next));
+      vmask_nxt = __ballot(valid(e_next) && in_split(i + 1));
       gnext = gather_src(e_next);
     }
     const unsigned char* tb = smem + bf * TILE_BYTES;

@@ -154,6 +154,10 @@ MLA_CASES = {
     "bf16_mfma": dict(B=2, T=20, S=600, topk=256),
     "bf16_mfma_h128": dict(B=1, T=9, S=700, topk=192, Hm=128),
     "bf16_decode_split": dict(B=3, T=1, S=3000, topk=2048),
+    # k not a multiple of the 64-row tile, rows that fill all k slots: the last tile's lanes
+    # past k must not count (prefill, and a decode split whose last split is a partial tile)
+    "bf16_mfma_ragged_topk": dict(B=2, T=20, S=600, topk=100),
+    "bf16_decode_split_ragged_topk": dict(B=3, T=1, S=3000, topk=2000),
     "bf16_generic_small_heads": dict(B=1, T=12, S=200, topk=64, Hm=16, Dc=128, Dr=32),
 }
 
