@@ -56,9 +56,10 @@ __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask, int lane) {
 // count must be >= rem.  Callers synchronise before and after.
 __device__ __forceinline__ void hist_find(const uint32_t* hist, uint32_t rem, uint32_t* digit, uint32_t* rank) {
   const int lane = threadIdx.x & 63;
-  // lane L owns digits [32L, 32L+32); suffix sums over lanes
+  // lane L owns digits [32L, 32L+32) and sums them starting at bin L % 32 of its range, so
+  // that the 64 lanes of each read hit different LDS banks; then suffix sums over lanes
   uint32_t c = 0;
-  for (int d = 0; d < 32; ++d) c += hist[32 * lane + d];
+  for (int d = 0; d < 32; ++d) c += hist[32 * lane + ((d + lane) & 31)];
   uint32_t x = c;
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t v = __shfl_down(x, off, 64);
@@ -67,16 +68,20 @@ __device__ __forceinline__ void hist_find(const uint32_t* hist, uint32_t rem, ui
   // x = number of candidates with digit >= 32*lane; non-increasing in lane
   const uint64_t ge = __ballot(x >= rem);
   const int L = __popcll(ge) - 1;  // last lane whose suffix reaches rem (>= 0: total >= rem)
-  if (lane == L) {
-    uint32_t above = x - c;
-    int d = 32 * lane + 31;
-    for (; d > 32 * lane; --d) {
-      const uint32_t h = hist[d];
-      if (above + h >= rem) break;
-      above += h;
-    }
-    *digit = (uint32_t)d;
-    *rank = rem - above;
+  const uint32_t above = __shfl(x - c, L, 64);  // candidates with a digit above lane L's range
+  // inside lane L's range: lane i < 32 takes digit 32L + i; s = candidates with a digit in
+  // [32L + i, 32L + 32); the digit is the highest i with above + s >= rem
+  const uint32_t h = lane < 32 ? hist[32 * L + lane] : 0u;
+  uint32_t sfx = h;
+  for (int off = 1; off < 32; off <<= 1) {
+    const uint32_t v = __shfl_down(sfx, off, 64);
+    if (lane + off < 32) sfx += v;
+  }
+  const uint64_t hit = __ballot(lane < 32 && above + sfx >= rem);
+  const int i = hit ? 63 - __clzll(hit) : 0;
+  if (lane == i) {
+    *digit = (uint32_t)(32 * L + i);
+    *rank = rem - (above + sfx - h);
   }
 }
 
