@@ -8,7 +8,7 @@
 // Megatron-Bridge pull request's fix for packed sequences shorter than
 // index_topk).
 //
-// Method (one workgroup of 1024 threads per row):
+// Method (one workgroup of 512 threads per row, several rows per compute unit):
 //  1. scores -> uint32 keys that order like the floats (-0.0 folded onto +0.0);
 //     rows that fit are cached in LDS so HBM is read once;
 //  2. radix select of the k-th largest key tau in three passes over 11/11/10-bit
@@ -36,7 +36,7 @@
 namespace dsa {
 namespace {
 
-constexpr int TK_THREADS = 1024;
+constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int64_t TK_CACHE_KEYS = 32768;  // 128 KiB of LDS
 
