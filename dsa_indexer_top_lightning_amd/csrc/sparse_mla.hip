@@ -476,7 +476,22 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     const uint64_t need = __ballot(mx > (hh ? m1 : m0) + RESCALE_LOG2);
     if (lane == 0) xflag[wave] = need != 0ull;
     lds_barrier();
-    if (xflag[0] | xflag[1] | xflag[2] | xflag[3]) {  // the same in every wave
+    // P^T fragment of k-step ks and head half hb: k-step ks uses C-layout values
+    // 8(ks%2) .. +7 of the S^T block of rows 32(ks/2) .. +32 (every wave's block, own included)
+    auto p_frag = [&](int ks, int hb) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, xpv[(2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane]);
+    };
+    // the flags and the first two k-steps' P fragments are read together; in the rare case
+    // of a raised flag every wave rewrites its block and the fragments are read again
+    const i32x4 flags = *reinterpret_cast<const i32x4*>(xflag);
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) pf[ks][hb] = p_frag(ks, hb);
+    // one use of all four: issued here with the flag read (not sunk past the branch), one wait
+    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[1][0]), "+v"(pf[1][1]));
+    if (flags[0] | flags[1] | flags[2] | flags[3]) {  // the same in every wave
       if (lg == 0) xmax[wave * 32 + lr] = mx;
       lds_barrier();
       // tile maxima of head lr of each half (waves 0, 2 hold half 0; waves 1, 3 half 1)
@@ -497,6 +512,10 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
       }
       make_p();
       lds_barrier();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) pf[ks][hb] = p_frag(ks, hb);
     }
     {
       float ls = 0.f;  // the probabilities actually used, as rounded to bf16
@@ -507,16 +526,11 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
     }
 
     // ---- O^T[dims 128wave + 32db][heads 32hb] += V^T . P^T over the tile's 4 k-steps of
-    // 16 rows; k-step ks uses C-layout values 8(ks%2) .. +7 of the S^T block of rows
-    // 32(ks/2) .. +32 (the P^T fragments of every wave's block, own included).  The V^T
-    // reads of step ks+2 are issued while step ks's matrix-core steps run.
+    // 16 rows.  The V^T reads of step ks+2 are issued while step ks's matrix-core steps run.
     {
-      auto p_frag = [&](int ks, int hb) -> bf16x8 {
-        return __builtin_bit_cast(bf16x8, xpv[(2 * (hb + 2 * (ks >> 1)) + (ks & 1)) * 64 + lane]);
-      };
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 p0 = p_frag(ks, 0), p1 = p_frag(ks, 1);
+        const bf16x8 p0 = ks < 2 ? pf[ks][0] : p_frag(ks, 0), p1 = ks < 2 ? pf[ks][1] : p_frag(ks, 1);
         if (ks + 2 < 4) load_v(tb, ks + 2, vf[(ks + 2) % 3]);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
