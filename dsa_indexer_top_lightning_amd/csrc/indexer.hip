@@ -549,8 +549,30 @@ void indexer_tile(IndexerParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.z;
-  const int t0 = blockIdx.y * PQ;
-  const int64_t s0 = (int64_t)blockIdx.x * PK;
+  int qy = blockIdx.y, kx = blockIdx.x;  // query tile, key tile
+  if (gridDim.x == gridDim.y && gridDim.x <= 16384) {
+    // A square tile grid (a prefill over its own prefix) is walked lower triangle first
+    // (key tile <= query tile: the causal tiles, all the work), then the upper triangle,
+    // so that the live tiles are the first blocks dispatched and spread evenly over the
+    // compute units instead of piling up on those that the triangle's rows map to.
+    const int n = (int)gridDim.x, id = (int)(blockIdx.y * gridDim.x + blockIdx.x), ntri = n * (n + 1) / 2;
+    if (id < ntri) {
+      int y = (int)((sqrtf(8.f * (float)id + 1.f) - 1.f) * 0.5f);
+      while (y * (y + 1) / 2 > id) --y;
+      while ((y + 1) * (y + 2) / 2 <= id) ++y;
+      qy = y;
+      kx = id - y * (y + 1) / 2;
+    } else {
+      const int j = id - ntri;  // upper triangle, key tile x > query tile y, x-major
+      int x = (int)((sqrtf(8.f * (float)j + 1.f) + 1.f) * 0.5f);
+      while (x * (x - 1) / 2 > j) --x;
+      while ((x + 1) * x / 2 <= j) ++x;
+      kx = x;
+      qy = j - x * (x - 1) / 2;
+    }
+  }
+  const int t0 = qy * PQ;
+  const int64_t s0 = (int64_t)kx * PK;
   const int T = p.T;
   const int64_t s_cap = p.s_cap;
 
