@@ -458,8 +458,18 @@ struct TileWork {
     for (int ks = 0; ks < KS; ++ks) {
       kstep(ks, cur, st, ab, bb_);
       if constexpr (COPY) {
+        if constexpr (DT == BF16 && KS == 8 && CPK == 1) {
+          // front-loaded: four copies in each of the first two k-steps, so the last ones have
+          // most of this head's k-steps to land before the next head waits for them (spread
+          // one per k-step, the last landed about 1,100 cycles into the next head)
+          if (ks < 2) {
 #pragma unroll
-        for (int c = 0; c < CPK; ++c) copy_part(ks * CPK + c, hp, sp);
+            for (int c = 0; c < 4; ++c) copy_part(4 * ks + c, hp, sp);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < CPK; ++c) copy_part(ks * CPK + c, hp, sp);
+        }
       }
       if constexpr (EPI) {
         if constexpr (KS == 8) {
