@@ -507,7 +507,7 @@ struct TileWork {
     if constexpr (DT == FP8) {
       // head h's weights times its query scales, in place; its epilogue reads them after
       // the next barrier
-      if (wv == 1) {
+      if (wv == 7) {  // a wave that copies no per-row vectors (balances the per-head barrier)
         float* vb = reinterpret_cast<float*>(smem + C::VBASE + (h % C::NVSTAGE) * C::VSTAGE);
         vb[C::W_OFF / 4 + lane] *= vb[C::QS_OFF / 4 + lane];
         vb[C::W_OFF / 4 + 64 + lane] *= vb[C::QS_OFF / 4 + 64 + lane];
