@@ -600,33 +600,34 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 }
 
 // Merge the split partials of one (query, head) in split order.  grid.x = (query, group
-// of 4 heads, quarter of the 512 value dims); 256 threads = 4 heads x 64 lanes x 2 dims.
+// of 4 heads, half of the 512 value dims); 256 threads = 4 heads x 64 lanes x 4 dims
+// (16-byte loads of the partials).
 // The loads of a batch of splits are independent of each other (an empty split's
 // partial is never written and gets weight 0 through a select), so they are all in
 // flight at once.
 constexpr int CMB_BATCH = 8;
 __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_ml) {
-  const int quarters = 4, groups = p.Hm / 4;
-  const int64_t tok = blockIdx.x / (groups * quarters);
-  const int rest = (int)(blockIdx.x % (groups * quarters));
-  const int head = (rest / quarters) * 4 + (threadIdx.x >> 6);
-  const int d0 = (rest % quarters) * (MDC / quarters) + (threadIdx.x & 63) * 2;
+  const int halves = 2, groups = p.Hm / 4;
+  const int64_t tok = blockIdx.x / (groups * halves);
+  const int rest = (int)(blockIdx.x % (groups * halves));
+  const int head = (rest / halves) * 4 + (threadIdx.x >> 6);
+  const int d0 = (rest % halves) * (MDC / halves) + (threadIdx.x & 63) * 4;
   const float* ml = ws_ml + (tok * nsplit * p.Hm + head) * 2;  // split s at ml + s * Hm * 2
   const int64_t mstride = (int64_t)p.Hm * 2;
   float M = -__builtin_inff();
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mstride]);
-  float o0 = 0.f, o1 = 0.f, L = 0.f;
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, L = 0.f;
   if (M != -__builtin_inff()) {
     const float* src = ws_o + (tok * nsplit * p.Hm + head) * MDC + d0;  // split s at src + s * Hm * MDC
     const int64_t ostride = (int64_t)p.Hm * MDC;
     for (int s0 = 0; s0 < nsplit; s0 += CMB_BATCH) {
-      float2 v[CMB_BATCH];
+      float4 v[CMB_BATCH];
       float f[CMB_BATCH], l[CMB_BATCH];
 #pragma unroll
       for (int u = 0; u < CMB_BATCH; ++u) {
         const int s = min(s0 + u, nsplit - 1);
-        v[u] = *reinterpret_cast<const float2*>(src + s * ostride);
+        v[u] = *reinterpret_cast<const float4*>(src + s * ostride);
         l[u] = ml[s * mstride + 1];
         f[u] = ml[s * mstride];
       }
@@ -637,6 +638,8 @@ __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, cons
         L = use ? fmaf(l[u], w, L) : L;
         o0 = use ? fmaf(v[u].x, w, o0) : o0;
         o1 = use ? fmaf(v[u].y, w, o1) : o1;
+        o2 = use ? fmaf(v[u].z, w, o2) : o2;
+        o3 = use ? fmaf(v[u].w, w, o3) : o3;
       }
     }
   }
@@ -644,6 +647,8 @@ __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, cons
   uint16_t* og = static_cast<uint16_t*>(p.out) + (tok * p.Hm + head) * MDC + d0;
   og[0] = f32_to_bf16_bits(o0 * inv);
   og[1] = f32_to_bf16_bits(o1 * inv);
+  og[2] = f32_to_bf16_bits(o2 * inv);
+  og[3] = f32_to_bf16_bits(o3 * inv);
   if (p.lse && d0 == 0) p.lse[tok * p.Hm + head] = L > 0.f ? (M + log2f(L)) * LN2 : -__builtin_inff();
 }
 
@@ -758,7 +763,7 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t, hip
     hipLaunchKernelGGL(mla_mfma, grid, dim3(256), lds, st, p, sp.nsplit, sp.tiles_per_split, ws_o, ws_ml);
     if (n_launches) ++*n_launches;
     if (sp.nsplit > 1) {
-      hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4) * 4)), dim3(256), 0, st, p, sp.nsplit,
+      hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4) * 2)), dim3(256), 0, st, p, sp.nsplit,
                          ws_o, ws_ml);
       if (n_launches) ++*n_launches;
     }
