@@ -605,7 +605,9 @@ void mla_mfma(MlaParams p, int nsplit, int tiles_per_split, float* __restrict__ 
 // The loads of a batch of splits are independent of each other (an empty split's
 // partial is never written and gets weight 0 through a select), so they are all in
 // flight at once.
-constexpr int CMB_BATCH = 8;
+// CMB_BATCH splits are loaded per round trip: 8, or 32 when there are more than 8 splits
+// (few query rows, e.g. a 4-sequence decode over 32 splits: one round trip instead of four)
+template <int CMB_BATCH>
 __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_ml) {
   const int halves = 2, groups = p.Hm / 4;
@@ -615,8 +617,16 @@ __global__ __launch_bounds__(256) void mla_combine(MlaParams p, int nsplit, cons
   const int d0 = (rest % halves) * (MDC / halves) + (threadIdx.x & 63) * 4;
   const float* ml = ws_ml + (tok * nsplit * p.Hm + head) * 2;  // split s at ml + s * Hm * 2
   const int64_t mstride = (int64_t)p.Hm * 2;
+  // the largest split max, from batches of independent loads (a repeated last split does
+  // not change it)
   float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mstride]);
+  for (int s0 = 0; s0 < nsplit; s0 += CMB_BATCH) {
+    float f[CMB_BATCH];
+#pragma unroll
+    for (int u = 0; u < CMB_BATCH; ++u) f[u] = ml[min(s0 + u, nsplit - 1) * mstride];
+#pragma unroll
+    for (int u = 0; u < CMB_BATCH; ++u) M = fmaxf(M, f[u]);
+  }
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, L = 0.f;
   if (M != -__builtin_inff()) {
     const float* src = ws_o + (tok * nsplit * p.Hm + head) * MDC + d0;  // split s at src + s * Hm * MDC
@@ -763,8 +773,9 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t, hip
     hipLaunchKernelGGL(mla_mfma, grid, dim3(256), lds, st, p, sp.nsplit, sp.tiles_per_split, ws_o, ws_ml);
     if (n_launches) ++*n_launches;
     if (sp.nsplit > 1) {
-      hipLaunchKernelGGL(mla_combine, dim3((unsigned)(rows * (p.Hm / 4) * 2)), dim3(256), 0, st, p, sp.nsplit,
-                         ws_o, ws_ml);
+      const dim3 cgrid((unsigned)(rows * (p.Hm / 4) * 2));
+      if (sp.nsplit > 8) hipLaunchKernelGGL(mla_combine<32>, cgrid, dim3(256), 0, st, p, sp.nsplit, ws_o, ws_ml);
+      else hipLaunchKernelGGL(mla_combine<8>, cgrid, dim3(256), 0, st, p, sp.nsplit, ws_o, ws_ml);
       if (n_launches) ++*n_launches;
     }
   } else {
