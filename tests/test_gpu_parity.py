@@ -45,6 +45,10 @@ INDEXER_CASES = {
     "fp8_decode_h64_t4": dict(B=1, T=4, S=1000, pos0=996, H=64, Hk=64, idx_dtype="fp8"),
     # between decode and prefill tiles
     "bf16_t8": dict(B=2, T=8, S=100, pos0=92),
+    # prefill over its own prefix with a square 3 x 3 grid of 128 x 128 tiles (walked lower
+    # triangle first) and a ragged last tile; fp8 as well (its own tile kernel)
+    "bf16_square_prefill": dict(B=2, T=300, S=300, pos0=0),
+    "fp8_square_prefill": dict(B=1, T=300, S=300, pos0=0, idx_dtype="fp8"),
 }
 
 
