@@ -24,7 +24,7 @@
 // select finishes; the output is written in order from the bitmaps.
 //
 // Few long rows (decode over a long prefix) would leave most compute units idle
-// with one workgroup per row, so there each row is cut into chunks of 4096 keys,
+// with one workgroup per row, so there each row is cut into chunks of 2048 keys,
 // one 256-thread workgroup per chunk, and the same radix select runs as a chain
 // of launches on the stream: the three digit histograms are summed per row in a
 // workspace with device-scope atomics, every later launch re-derives the digit
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(LG_THREADS) void topk_long(TopkParams p, int map_wo
 
 // ----------------------------------------------------------------- split rows
 constexpr int SP_THREADS = 256;
-constexpr int SP_PER = 16;                        // keys per thread
+constexpr int SP_PER = 8;                         // keys per thread
 constexpr int SP_CHUNK = SP_THREADS * SP_PER;     // keys per workgroup
 constexpr int SP_BINS = 2048;
 constexpr int64_t SP_MIN_KEYS = 2 * SP_CHUNK;     // shorter rows stay on one workgroup
