@@ -27,7 +27,8 @@ class Shape(C.Structure):
     _fields_ = [("B", C.c_int32), ("T", C.c_int32), ("s_cap", C.c_int64),
                 ("H", C.c_int32), ("D", C.c_int32), ("Hk", C.c_int32), ("topk", C.c_int32),
                 ("Hm", C.c_int32), ("Dc", C.c_int32), ("Dr", C.c_int32),
-                ("key_start", C.c_void_p), ("key_end", C.c_void_p)]
+                ("key_start", C.c_void_p), ("key_end", C.c_void_p),
+                ("key_start_host", C.c_void_p), ("key_end_host", C.c_void_p)]
 
 
 class TopkCache(C.Structure):
@@ -151,9 +152,21 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def make_shape(B, T, s_cap, *, H=0, D=0, Hk=0, topk=0, Hm=0, Dc=0, Dr=0, key_start=None, key_end=None) -> Shape:
-    shape = Shape(B, T, s_cap, H, D, Hk, topk, Hm, Dc, Dr, _dev_ptr(key_start), _dev_ptr(key_end))
-    shape._keep = (key_start, key_end)  # the struct holds raw pointers: keep their tensors alive
+def _host_i32(a):
+    if a is None:
+        return None
+    import numpy as np
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def make_shape(B, T, s_cap, *, H=0, D=0, Hk=0, topk=0, Hm=0, Dc=0, Dr=0, key_start=None, key_end=None,
+               key_start_host=None, key_end_host=None) -> Shape:
+    """dsa_shape.  key_start / key_end are device int32 tensors [B,T] (or None); their host copies
+    (numpy, optional) let dsa_group_forward fill the analytic counters."""
+    ksh, keh = _host_i32(key_start_host), _host_i32(key_end_host)
+    shape = Shape(B, T, s_cap, H, D, Hk, topk, Hm, Dc, Dr, _dev_ptr(key_start), _dev_ptr(key_end),
+                  None if ksh is None else ksh.ctypes.data, None if keh is None else keh.ctypes.data)
+    shape._keep = (key_start, key_end, ksh, keh)  # the struct holds raw pointers: keep their arrays alive
     return shape
 
 
@@ -258,7 +271,8 @@ class IndexCache:
 def group_forward(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale, cache: IndexCache, tag: int,
                   workspace, *, events=None, stream=None):
     """dsa_group_forward.  ``layers`` is a list of dicts with keys q, kv, out, lse and, on full
-    layers, index = dict(q, k, w, q_scale, k_scale).  Returns GroupStats."""
+    layers, index = dict(q, k, w, q_scale, k_scale).  Returns GroupStats, or None when the shape
+    has device key ranges without host copies (the counters cannot be formed then)."""
     n = len(indexer_types)
     types = (C.c_int * n)(*[FULL if t in ("full", FULL) else SHARED for t in indexer_types])
     idx_ios = []
@@ -275,10 +289,12 @@ def group_forward(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale,
     ev = None
     if events is not None:
         ev = (C.c_void_p * len(events))(*events)
-    stats = GroupStats()
+    want = (not shape.key_start or shape.key_start_host) and (not shape.key_end or shape.key_end_host)
+    stats = GroupStats() if want else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_group_forward(C.byref(shape), mla_dtype, n, types, arr, float(sm_scale), C.byref(cache.c),
-                                   tag, _dev_ptr(workspace), ws_bytes, ev, C.byref(stats), _stream(stream)))
+                                   tag, _dev_ptr(workspace), ws_bytes, ev,
+                                   C.byref(stats) if want else None, _stream(stream)))
     return stats
 
 

@@ -127,6 +127,42 @@ dsa::MlaParams mla_params(const dsa_shape* s, const void* q, const void* kv, con
   return dsa::MlaParams{s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, q, kv, idx, sm, out, lse};
 }
 
+// Analytic counters of a group call from host copies of the key ranges (NULL: 0 and
+// s_cap).  Candidate count n = clamped key_end - key_start, selected rows min(n, topk).
+void group_counters(const dsa_shape* s, dsa_dtype idx_dtype, dsa_dtype mla_dtype, int32_t n_layers,
+                    const dsa_layer_type* types, const int32_t* ks_h, const int32_t* ke_h, dsa_group_stats* out) {
+  const int64_t rows = rows_of(s);
+  double sum_n = 0, sum_j = 0, prefix = 0;
+  for (int b = 0; b < s->B; ++b) {
+    int64_t mx = 0;
+    for (int t = 0; t < s->T; ++t) {
+      const int64_t r = (int64_t)b * s->T + t;
+      int64_t a = ks_h ? ks_h[r] : 0, z = ke_h ? ke_h[r] : s->s_cap;
+      a = std::min<int64_t>(std::max<int64_t>(a, 0), s->s_cap);
+      z = std::min<int64_t>(std::max<int64_t>(z, a), s->s_cap);
+      sum_n += (double)(z - a);
+      sum_j += (double)std::min<int64_t>(z - a, s->topk);
+      mx = std::max(mx, z);
+    }
+    prefix += (double)mx;
+  }
+  int n_full = 0;
+  for (int l = 0; l < n_layers; ++l) n_full += types[l] == DSA_FULL;
+  const double ie = idx_dtype == DSA_F32 ? 4 : (idx_dtype == DSA_BF16 ? 2 : 1);
+  const double sc = idx_dtype == DSA_FP8_E4M3 ? 4 : 0;
+  const double me = mla_dtype == DSA_F32 ? 4 : 2;
+  const double R = s->Dc + s->Dr;
+  *out = dsa_group_stats{};
+  out->n_full = n_full;
+  out->n_shared = n_layers - n_full;
+  out->indexer_flops = n_full * 2.0 * s->H * s->D * sum_n;
+  out->indexer_bytes =
+      n_full * ((double)rows * s->H * (s->D * ie + 4 + sc) + prefix * s->Hk * (s->D * ie + sc) + 4.0 * sum_n);
+  out->topk_bytes = n_full * (4.0 * sum_n + 4.0 * (double)rows * s->topk);
+  out->attn_flops = n_layers * 2.0 * s->Hm * (2.0 * s->Dc + s->Dr) * sum_j;
+  out->attn_bytes = n_layers * (sum_j * R * me + (double)rows * s->Hm * R * me + (double)rows * s->Hm * s->Dc * me);
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,8 +287,6 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
   if (n_layers < 0) return fail(DSA_ERR_INVALID_ARG, "n_layers=%d", n_layers);
   if (n_layers > 0 && (!types || !layers)) return fail(DSA_ERR_INVALID_ARG, "indexer_types and layers must be non-NULL");
   if (!cache) return fail(DSA_ERR_INVALID_ARG, "cache handle is NULL");
-  int n_full = 0;
-  for (int l = 0; l < n_layers; ++l) n_full += types[l] == DSA_FULL;
   if (n_layers > 0) {
     st = check_mla_shape(s, mla_dtype);
     if (st != DSA_OK) return st;
@@ -285,6 +319,19 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
   const size_t sb = scores_bytes(s);
   if (ws_bytes < need || (need && !ws))
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "group workspace %zu < %zu", ws_bytes, need);
+  dsa_dtype idx_dtype = DSA_BF16;
+  for (int l = 0; l < n_layers; ++l)
+    if (types[l] == DSA_FULL) {
+      idx_dtype = layers[l].index->idx_dtype;
+      break;
+    }
+  if (stats) {
+    if ((s->key_start && !s->key_start_host) || (s->key_end && !s->key_end_host))
+      return fail(DSA_ERR_INVALID_ARG,
+                  "stats need host copies of the device key ranges (shape->key_start_host / key_end_host)");
+    group_counters(s, idx_dtype, mla_dtype, n_layers, types, s->key_start ? s->key_start_host : nullptr,
+                   s->key_end ? s->key_end_host : nullptr, stats);
+  }
 
   // ---- enqueue
   hipStream_t strm = (hipStream_t)stream;
@@ -292,6 +339,7 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
   void* kws = ws ? static_cast<char*>(ws) + sb : nullptr;
   const size_t kws_bytes = ws_bytes - std::min(ws_bytes, sb);
   int launches = 0;
+  int last_full = -1;           // last full layer whose top-k was enqueued
   auto rec = [&](int l, int slot) -> hipError_t {
     if (!events) return hipSuccess;
     hipEvent_t ev = static_cast<hipEvent_t>(events[6 * l + slot]);
@@ -308,15 +356,10 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
       if (e != hipSuccess) break;
       if ((e = rec(l, 1)) != hipSuccess) break;
       if ((e = rec(l, 2)) != hipSuccess) break;
+      last_full = l;  // from here on the indices buffer holds this call's data
       e = dsa::launch_topk(topk_params(s, scores, s->s_cap, cache->indices), kws, kws_bytes, strm, &launches);
       if (e != hipSuccess) break;
       if ((e = rec(l, 3)) != hipSuccess) break;
-      cache->B = s->B;
-      cache->T = s->T;
-      cache->topk = s->topk;
-      cache->valid = 1;
-      cache->donor_layer = l;
-      cache->tag = tag;
     }
     if ((e = rec(l, 4)) != hipSuccess) break;
     e = dsa::launch_sparse_mla(mla_params(s, L.q, L.kv, cache->indices, sm_scale, L.out, L.lse),
@@ -324,11 +367,17 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
     if (e != hipSuccess) break;
     e = rec(l, 5);
   }
-  if (stats) {
-    *stats = dsa_group_stats{};
-    stats->n_full = n_full;
-    stats->n_shared = n_layers - n_full;
-    stats->n_launches = launches;
+  if (stats) stats->n_launches = launches;
+  if (last_full >= 0) {
+    // the handle describes the indices buffer only once every launch was enqueued
+    cache->valid = e == hipSuccess ? 1 : 0;
+    if (e == hipSuccess) {
+      cache->B = s->B;
+      cache->T = s->T;
+      cache->topk = s->topk;
+      cache->donor_layer = last_full;
+      cache->tag = tag;
+    }
   }
   return e == hipSuccess ? DSA_OK : hip_fail(e, "group forward");
 }
@@ -340,36 +389,7 @@ dsa_status dsa_group_stats_compute(const dsa_shape* s, dsa_dtype idx_dtype, dsa_
   if (st != DSA_OK) return st;
   if (!out || (n_layers > 0 && !types)) return fail(DSA_ERR_INVALID_ARG, "stats and indexer_types must be non-NULL");
   if (!valid_dtype(idx_dtype) || !valid_dtype(mla_dtype)) return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
-  const int64_t rows = rows_of(s);
-  double sum_n = 0, sum_j = 0, prefix = 0;
-  for (int b = 0; b < s->B; ++b) {
-    int64_t mx = 0;
-    for (int t = 0; t < s->T; ++t) {
-      const int64_t r = (int64_t)b * s->T + t;
-      int64_t a = ks_h ? ks_h[r] : 0, z = ke_h ? ke_h[r] : s->s_cap;
-      a = std::min<int64_t>(std::max<int64_t>(a, 0), s->s_cap);
-      z = std::min<int64_t>(std::max<int64_t>(z, a), s->s_cap);
-      sum_n += (double)(z - a);
-      sum_j += (double)std::min<int64_t>(z - a, s->topk);
-      mx = std::max(mx, z);
-    }
-    prefix += (double)mx;
-  }
-  int n_full = 0;
-  for (int l = 0; l < n_layers; ++l) n_full += types[l] == DSA_FULL;
-  const double ie = idx_dtype == DSA_F32 ? 4 : (idx_dtype == DSA_BF16 ? 2 : 1);
-  const double sc = idx_dtype == DSA_FP8_E4M3 ? 4 : 0;
-  const double me = mla_dtype == DSA_F32 ? 4 : 2;
-  const double R = s->Dc + s->Dr;
-  *out = dsa_group_stats{};
-  out->n_full = n_full;
-  out->n_shared = n_layers - n_full;
-  out->indexer_flops = n_full * 2.0 * s->H * s->D * sum_n;
-  out->indexer_bytes =
-      n_full * ((double)rows * s->H * (s->D * ie + 4 + sc) + prefix * s->Hk * (s->D * ie + sc) + 4.0 * sum_n);
-  out->topk_bytes = n_full * (4.0 * sum_n + 4.0 * (double)rows * s->topk);
-  out->attn_flops = n_layers * 2.0 * s->Hm * (2.0 * s->Dc + s->Dr) * sum_j;
-  out->attn_bytes = n_layers * (sum_j * R * me + (double)rows * s->Hm * R * me + (double)rows * s->Hm * s->Dc * me);
+  group_counters(s, idx_dtype, mla_dtype, n_layers, types, ks_h, ke_h, out);
   return DSA_OK;
 }
 

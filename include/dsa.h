@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -61,6 +61,11 @@ typedef struct {
   int32_t Hm, Dc, Dr;    /* MLA heads, latent rank (value dims), rope dims; a latent row has Dc+Dr values */
   const int32_t* key_start; /* device int32 [B*T], or NULL for 0 */
   const int32_t* key_end;   /* device int32 [B*T] (exclusive), or NULL for s_cap */
+  /* Optional HOST copies of key_start / key_end (same layout, NULL = not given).  The
+   * kernels never read them; dsa_group_forward needs them only to fill the analytic
+   * counters of dsa_group_stats when the device ranges are given. */
+  const int32_t* key_start_host;
+  const int32_t* key_end_host;
 } dsa_shape;
 
 /*
@@ -159,10 +164,11 @@ typedef struct {
   float* lse;
 } dsa_layer_io;
 
-/* Analytic work of a group call (counts, not timings). */
+/* Analytic work of a group call (counts, not timings).  Candidate count n of a query =
+ * key_end - key_start after clamping to [0, s_cap]; selected rows |J| = min(n, topk). */
 typedef struct {
   int32_t n_full, n_shared;
-  int32_t n_launches;      /* kernels enqueued by the call */
+  int32_t n_launches;      /* kernels enqueued by the call (dsa_group_forward only) */
   double indexer_flops;    /* 2*H*D per (query, candidate) pair, per full layer */
   double indexer_bytes;    /* index q, w (+scales), index k of each item's prefix, fp32 scores written */
   double topk_bytes;       /* fp32 scores read + int32 indices written */
@@ -175,10 +181,14 @@ typedef struct {
  * pattern figure; the list comes from indexer_types as the page's config
  * evidence and implementation checklist ask, not from a fixed layer modulo).
  * For l in 0..n_layers-1:
- *   FULL:   indexer scores -> workspace, top-k -> cache->indices, and the cache
- *           is marked valid with donor_layer = l and the call's tag.
+ *   FULL:   indexer scores -> workspace, top-k -> cache->indices.
  *   SHARED: the cache's indices are used unchanged (no device work).
  *   both:   sparse MLA with layer l's own q and kv and the current indices.
+ * The handle's host fields change only when the call returns: after a successful
+ * enqueue of a list with full layers, valid = 1, donor_layer = the last full layer,
+ * tag = the call's tag and B, T, topk = the shape's.  If an enqueue fails after a full
+ * layer's top-k was enqueued (the indices buffer may then hold partial results),
+ * valid = 0; if it fails before that, the handle is left as it was.
  * Errors (checked for the whole list before anything is enqueued):
  *   DSA_ERR_INVALID_ARG  a full layer without `index`, null required pointers;
  *   DSA_ERR_NO_DONOR     the first layer is shared and cache->valid == 0 (a
@@ -192,7 +202,12 @@ typedef struct {
  *   events: NULL, or host array of 6*n_layers hipEvent_t; when given, for layer l
  *           events[6l+0/1] bracket the indexer, [6l+2/3] the top-k and [6l+4/5]
  *           the attention kernels (entries of shared layers' indexer/top-k unused).
- *   stats:  NULL or filled with n_full, n_shared and n_launches.
+ *   stats:  NULL, or filled with every field: the analytic counters (the same numbers as
+ *           dsa_group_stats_compute, computed before anything is enqueued, so they are
+ *           set even when an enqueue fails) and n_launches.  When the shape gives device
+ *           key ranges, the counters need their host copies (shape->key_start_host /
+ *           key_end_host): a call with stats, a device range and no host copy of it fails
+ *           with DSA_ERR_INVALID_ARG and enqueues nothing.
  *   workspace: ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_GROUP).
  */
 dsa_status dsa_group_forward(const dsa_shape* shape, dsa_dtype mla_dtype, int32_t n_layers,

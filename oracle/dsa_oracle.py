@@ -123,6 +123,24 @@ def index_scores_row(q_row: np.ndarray, k: np.ndarray, w_row: np.ndarray,
     return np.maximum(dots, 0.0) @ w_row
 
 
+def index_scores_rows(q_rows: np.ndarray, k: np.ndarray, w_rows: np.ndarray) -> np.ndarray:
+    """Index scores of several queries of one batch item against the same keys.
+
+    q_rows [R, H, D], k [n, Hk, D], w_rows [R, H] (float64) -> [R, n].  The same
+    definition as index_scores_row, summed head by head: for head h the dot
+    products of all R queries with all n keys of key head g(h), ReLU, times the
+    head weight of each query.
+    """
+    R, H, _ = q_rows.shape
+    Hk = k.shape[1]
+    out = np.zeros((R, k.shape[0]))
+    for h in range(H):
+        g = h if Hk == H else 0
+        dots = q_rows[:, h, :] @ k[:, g, :].T                   # [R, n]
+        out += w_rows[:, h][:, None] * np.maximum(dots, 0.0)
+    return out
+
+
 def index_scores(q: np.ndarray, k: np.ndarray, w: np.ndarray,
                  key_start: np.ndarray, key_end: np.ndarray) -> np.ndarray:
     """q [B,T,H,D], k [B,S,Hk,D], w [B,T,H] -> I [B,T,S], NaN outside each candidate range."""

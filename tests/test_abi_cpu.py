@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol(L):
     assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
-    assert L.dsa_abi_version() == 1
+    assert L.dsa_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -88,14 +88,14 @@ def test_sparse_mla_errors(L):
     assert f(C.byref(d), b.BF16, FAKE, FAKE, FAKE, 1.0, FAKE, None, FAKE, need - 1, None) == 5
 
 
-def _group(L, shape, types, layers, cache, tag=0, ws=FAKE, ws_bytes=None):
+def _group(L, shape, types, layers, cache, tag=0, ws=FAKE, ws_bytes=None, stats=None):
     n = len(types)
     tarr = (C.c_int * n)(*types)
     arr = (b.LayerIO * n)(*layers)
     if ws_bytes is None:
         ws_bytes = L.dsa_workspace_bytes(C.byref(shape), b.OP_GROUP)
     return L.dsa_group_forward(C.byref(shape), b.BF16, n, tarr, arr, 0.1, C.byref(cache), tag, ws, ws_bytes,
-                               None, None, None)
+                               None, None if stats is None else C.byref(stats), None)
 
 
 def _io(with_index):
@@ -222,3 +222,75 @@ def test_backward_validation(L):
     assert call(shape, dI=None) == 1
     assert call(shape, dt=b.FP8_E4M3) == 1
     assert call(_shape(topk=8, H=128, Hk=128)) == 2
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def test_group_stats_need_host_copies_of_device_ranges(L):
+    # a device range without its host copy: the counters cannot be formed, nothing is enqueued
+    s = _shape()
+    s.key_end = FAKE
+    fu, k1 = _io(True)
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    st = b.GroupStats()
+    assert _group(L, s, [b.FULL], [fu], cache, stats=st) == 1
+    assert "host copies" in b.last_error()
+    assert cache.valid == 0 and st.n_launches == 0
+
+
+# The next two tests need every kernel launch to fail, which only a host without a GPU
+# gives (the library then reports DSA_ERR_HIP at the first launch and nothing runs).
+# With a GPU visible the fake pointers would reach real kernels, so they are skipped.
+no_gpu_only = pytest.mark.skipif(_gpu_visible(), reason="relies on launches failing on a host without a GPU")
+
+
+@no_gpu_only
+@pytest.mark.parametrize("ranges", ["none", "host_copies"])
+def test_group_forward_fills_every_counter_before_enqueue(L, ranges):
+    T, S = 4, 16
+    ks_h = np.array([[0, 2, 5, 1]], np.int32)
+    ke_h = np.array([[3, 9, 16, 11]], np.int32)
+    s = _shape(T=T, s_cap=S)
+    if ranges == "host_copies":
+        s.key_start, s.key_end = FAKE, FAKE
+        s.key_start_host, s.key_end_host = ks_h.ctypes.data, ke_h.ctypes.data
+    fu, k1 = _io(True)
+    sh, k2 = _io(False)
+    types = [b.FULL, b.SHARED, b.SHARED, b.FULL]
+    st = b.GroupStats()
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    assert _group(L, s, types, [fu, sh, sh, fu], cache, stats=st) == 6       # DSA_ERR_HIP: no device
+    ref = b.group_stats_compute(_shape(T=T, s_cap=S), b.BF16, b.BF16, ["full", "shared", "shared", "full"],
+                                ks_h if ranges == "host_copies" else None, ke_h if ranges == "host_copies" else None)
+    assert (st.n_full, st.n_shared) == (2, 2)
+    for key in ("indexer_flops", "indexer_bytes", "topk_bytes", "attn_flops", "attn_bytes"):
+        assert getattr(st, key) == getattr(ref, key) and getattr(st, key) > 0, key
+    # closed forms on the hand-sized case: sum n over the rows, sum min(n, topk) with topk = 8
+    n = (ke_h - ks_h)[0] if ranges == "host_copies" else np.full(T, S)
+    assert st.indexer_flops == 2 * 2 * 4 * 32 * n.sum()
+    assert st.attn_flops == 4 * 2 * 8 * (2 * 64 + 16) * np.minimum(n, 8).sum()
+
+
+@no_gpu_only
+def test_group_forward_commits_the_cache_handle_only_after_a_whole_enqueue(L):
+    fu, k1 = _io(True)
+    sh, k2 = _io(False)
+    # a fresh handle: the first launch (the indexer) fails -> still empty
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    assert _group(L, _shape(), [b.FULL, b.SHARED], [fu, sh], cache, tag=9) == 6
+    assert (cache.valid, cache.donor_layer, cache.tag) == (0, -1, 0)
+    # a valid handle from an earlier call: a failure before any top-k leaves it as it was
+    cache = b.TopkCache(FAKE, 1, 4, 8, 1, 3, 5)
+    assert _group(L, _shape(), [b.FULL, b.SHARED], [fu, sh], cache, tag=9) == 6
+    assert (cache.valid, cache.donor_layer, cache.tag, cache.B, cache.T, cache.topk) == (1, 3, 5, 1, 4, 8)
+    # with an empty key capacity the indexer has nothing to do and the top-k launch is the
+    # first to fail: the indices buffer may hold partial data, so the handle is invalidated
+    cache = b.TopkCache(FAKE, 1, 4, 8, 1, 3, 5)
+    assert _group(L, _shape(s_cap=0), [b.FULL, b.SHARED], [fu, sh], cache, tag=9) == 6
+    assert cache.valid == 0 and cache.tag == 5

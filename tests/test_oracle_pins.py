@@ -57,6 +57,7 @@ def test_index_score_hand_example_per_head_keys():
     w = np.array(g["w"], float)[None]
     assert np.array_equal(O.index_scores_loop(q, k, w)[0], g["expected_per_head"])
     assert np.array_equal(O.index_scores_row(q[0], k, w[0], 0, 3), g["expected_per_head"])
+    assert np.array_equal(O.index_scores_rows(q, k, w)[0], g["expected_per_head"])
     # a sub-range returns the same positions' scores
     assert np.array_equal(O.index_scores_row(q[0], k, w[0], 1, 3), g["expected_per_head"][1:])
 
@@ -68,6 +69,7 @@ def test_index_score_hand_example_shared_key():
     w = np.array(g["w"], float)[None]
     assert np.array_equal(O.index_scores_loop(q, k, w)[0], g["expected_shared"])
     assert np.array_equal(O.index_scores_row(q[0], k, w[0], 0, 3), g["expected_shared"])
+    assert np.array_equal(O.index_scores_rows(q, k, w)[0], g["expected_shared"])
 
 
 def _rand_index(rng, T=5, S=7, H=3, D=4, Hk=None):
@@ -84,6 +86,7 @@ def test_index_score_loop_equals_vectorised(hk_one):
     ke = np.full((1, 5), 7, np.int32)
     got = O.index_scores(q[None], k[None], w[None], ks, ke)[0]
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O.index_scores_rows(q, k, w), ref, rtol=1e-12, atol=1e-14)
 
 
 def test_index_score_relu_identities_catch_sign_and_index_errors():
@@ -92,6 +95,8 @@ def test_index_score_relu_identities_catch_sign_and_index_errors():
     q, k, w = _rand_index(rng, T=3, S=6, H=4, D=5)
     pos = O.index_scores_loop(q, k, w)
     neg = O.index_scores_loop(-q, k, w)
+    for f in (O.index_scores_rows,):      # the batched form obeys the same identities
+        np.testing.assert_allclose(f(q, k, w) - f(-q, k, w), pos - neg, rtol=1e-12, atol=1e-12)
     dots = np.stack([q[:, h, :] @ k[:, h, :].T for h in range(4)], axis=-1)   # [T, S, H]
     np.testing.assert_allclose(pos - neg, (dots * w[:, None, :]).sum(-1), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(pos + neg, (np.abs(dots) * w[:, None, :]).sum(-1), rtol=1e-12, atol=1e-12)
@@ -185,6 +190,31 @@ def test_topk_invariant_under_increasing_transform_and_offset():
     b, _ = O.topk_row(np.exp(s) * 3 + 1, 10, 510, 64)
     assert np.array_equal(a, b)
     assert a.min() >= 10 and a.max() < 510
+
+
+def test_batched_topk_with_key_start_offsets_matches_brute_force():
+    # the batched call slices each row to [key_start, key_end) of absolute positions;
+    # every row is checked against brute force over that row's own candidates
+    rng = np.random.default_rng(25)
+    values = np.array([-1.0, -0.0, 0.0, 0.5, 1.0, 2.0])
+    B, T, S, k = 3, 7, 12, 4
+    sc = values[rng.integers(0, len(values), (B, T, S))]
+    ke = rng.integers(0, S + 1, (B, T)).astype(np.int32)
+    ks = np.minimum(rng.integers(0, 6, (B, T)), ke).astype(np.int32)
+    ks[0, 0], ke[0, 0] = 5, 12                 # n = 7 > k, candidates start at 5
+    ks[1, 2], ke[1, 2] = 9, 12                 # n = 3 < k: all kept, then -1
+    idx, tau = O.topk(sc, ks, ke, k)
+    for bb in range(B):
+        for t in range(T):
+            a, z = int(ks[bb, t]), int(ke[bb, t])
+            exp = _brute_topk(list(sc[bb, t, a:z]), a, k)
+            assert list(idx[bb, t, :len(exp)]) == exp, (bb, t)
+            assert (idx[bb, t, len(exp):] == -1).all()
+            if z - a > k:
+                assert tau[bb, t] == sorted(sc[bb, t, a:z], reverse=True)[k - 1]
+            else:
+                assert np.isnan(tau[bb, t])
+    assert list(idx[0, 0]) == _brute_topk(list(sc[0, 0, 5:12]), 5, k) and idx[0, 0].min() >= 5
 
 
 def test_topk_all_equal_takes_lowest_positions():
@@ -355,6 +385,24 @@ def test_group_stats_closed_forms_causal_prefill():
     assert st["attn_flops"] == 4 * 2 * 2 * (2 * 8 + 4) * sum_j
     assert st["topk_bytes"] == 4 * sum_n + 4 * T * k
     assert (st["n_full"], st["n_shared"]) == (1, 3)
+
+
+def test_group_stats_bytes_hand_counted():
+    # two items, two queries each; item 0 reads keys [0, 7), item 1 keys [0, 10)
+    ks = np.array([[0, 2], [1, 0]])
+    ke = np.array([[3, 7], [10, 5]])            # n = 3, 5, 9, 5: sum 22; min(n, 3) summed: 12
+    kw = dict(H=2, D=8, Hk=2, topk_k=3, Hm=2, Dc=4, Dr=2, S=10)
+    bf = O.group_stats(["full", "shared", "shared"], ks, ke, idx_bytes=2, idx_scaled=False, mla_bytes=2, **kw)
+    # index q 4 rows x 2 heads x 8 x 2 B = 128, w 4 x 2 x 4 B = 32, keys (7 + 10) x 2 x 8 x 2 B = 544,
+    # scores written 22 x 4 B = 88
+    assert bf["indexer_bytes"] == 128 + 32 + 544 + 88
+    # per layer: 12 gathered rows x 6 x 2 B = 144, q 4 x 2 x 6 x 2 B = 96, out 4 x 2 x 4 x 2 B = 64
+    assert bf["attn_bytes"] == 3 * (144 + 96 + 64)
+    assert bf["topk_bytes"] == 22 * 4 + 4 * 3 * 4
+    f8 = O.group_stats(["full", "full"], ks, ke, idx_bytes=1, idx_scaled=True, mla_bytes=4, **kw)
+    # fp8: q 64 B, w 32, q scales 4 x 2 x 4 = 32, keys 272, key scales 17 x 2 x 4 = 136, scores 88
+    assert f8["indexer_bytes"] == 2 * (64 + 32 + 32 + 272 + 136 + 88)
+    assert f8["attn_bytes"] == 2 * (12 * 6 * 4 + 4 * 2 * 6 * 4 + 4 * 2 * 4 * 4)
 
 
 # ------------------------------------------------------------------ decode-step preparation
