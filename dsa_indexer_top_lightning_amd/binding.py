@@ -71,6 +71,9 @@ _SIGS = {
     "dsa_group_forward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int32, C.c_void_p, C.POINTER(LayerIO),
                                     C.c_float, C.POINTER(TopkCache), C.c_uint64, C.c_void_p, C.c_size_t,
                                     C.c_void_p, C.POINTER(GroupStats), C.c_void_p]),
+    "dsa_group_forward_noalloc": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int32, C.c_void_p, C.POINTER(LayerIO),
+                                            C.c_float, C.POINTER(TopkCache), C.c_uint64, C.c_void_p,
+                                            C.POINTER(GroupStats), C.c_void_p]),
     "dsa_group_stats_compute": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_int, C.c_int32, C.c_void_p, C.c_void_p,
                                           C.c_void_p, C.POINTER(GroupStats)]),
     "dsa_index_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -269,7 +272,7 @@ class IndexCache:
 
 
 def group_forward(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale, cache: IndexCache, tag: int,
-                  workspace, *, events=None, stream=None):
+                  workspace, *, events=None, stream=None, _noalloc=False):
     """dsa_group_forward.  ``layers`` is a list of dicts with keys q, kv, out, lse and, on full
     layers, index = dict(q, k, w, q_scale, k_scale).  Returns GroupStats, or None when the shape
     has device key ranges without host copies (the counters cannot be formed then)."""
@@ -291,11 +294,30 @@ def group_forward(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale,
         ev = (C.c_void_p * len(events))(*events)
     want = (not shape.key_start or shape.key_start_host) and (not shape.key_end or shape.key_end_host)
     stats = GroupStats() if want else None
+    st = C.byref(stats) if want else None
+    if _noalloc:
+        _check(lib().dsa_group_forward_noalloc(C.byref(shape), mla_dtype, n, types, arr, float(sm_scale),
+                                               C.byref(cache.c), tag, ev, st, _stream(stream)))
+        return stats
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_group_forward(C.byref(shape), mla_dtype, n, types, arr, float(sm_scale), C.byref(cache.c),
-                                   tag, _dev_ptr(workspace), ws_bytes, ev,
-                                   C.byref(stats) if want else None, _stream(stream)))
+                                   tag, _dev_ptr(workspace), ws_bytes, ev, st, _stream(stream)))
     return stats
+
+
+def noalloc_scratch_bytes() -> int:
+    """DSA_NOALLOC_SCRATCH_BYTES as the header defines it."""
+    with open(HEADER) as f:
+        m = re.search(r"#define\s+DSA_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", f.read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def group_forward_noalloc(shape: Shape, mla_dtype: int, indexer_types, layers, sm_scale, cache: IndexCache,
+                          tag: int, *, events=None, stream=None):
+    """dsa_group_forward_noalloc: dsa_group_forward with the library's own device scratch instead of a
+    workspace (nothing is allocated).  Arguments and return value as for group_forward."""
+    return group_forward(shape, mla_dtype, indexer_types, layers, sm_scale, cache, tag, None, events=events,
+                         stream=stream, _noalloc=True)
 
 
 def group_stats_compute(shape: Shape, idx_dtype: int, mla_dtype: int, indexer_types, key_start_host=None,

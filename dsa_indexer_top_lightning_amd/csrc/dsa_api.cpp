@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/dsa.h"
@@ -161,6 +162,39 @@ void group_counters(const dsa_shape* s, dsa_dtype idx_dtype, dsa_dtype mla_dtype
   out->topk_bytes = n_full * (4.0 * sum_n + 4.0 * (double)rows * s->topk);
   out->attn_flops = n_layers * 2.0 * s->Hm * (2.0 * s->Dc + s->Dr) * sum_j;
   out->attn_bytes = n_layers * (sum_j * R * me + (double)rows * s->Hm * R * me + (double)rows * s->Hm * s->Dc * me);
+}
+
+// ---- allocation-free group call
+// Scratch of dsa_group_forward_noalloc: a file-scope device array, one copy per GPU,
+// held for the life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory, so its device address is looked up once per device (with that
+// device current) and only that address is handed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of the current device's scratch (looked up on the first call on it).
+dsa_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a NULL address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
 }
 
 }  // namespace
@@ -380,6 +414,24 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
     }
   }
   return e == hipSuccess ? DSA_OK : hip_fail(e, "group forward");
+}
+
+dsa_status dsa_group_forward_noalloc(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_layers,
+                                     const dsa_layer_type* types, const dsa_layer_io* layers, float sm_scale,
+                                     dsa_topk_cache* cache, uint64_t tag, void* const* events,
+                                     dsa_group_stats* stats, void* stream) {
+  dsa_status st = check_common(s);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_workspace_bytes(s, DSA_OP_GROUP);
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL,
+                "this group call needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                "(use dsa_group_forward with a workspace)",
+                need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && (st = current_scratch(&ws)) != DSA_OK) return st;
+  return dsa_group_forward(s, mla_dtype, n_layers, types, layers, sm_scale, cache, tag, ws,
+                           need > 0 ? (size_t)DSA_NOALLOC_SCRATCH_BYTES : 0, events, stats, stream);
 }
 
 dsa_status dsa_group_stats_compute(const dsa_shape* s, dsa_dtype idx_dtype, dsa_dtype mla_dtype, int32_t n_layers,

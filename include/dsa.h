@@ -217,6 +217,30 @@ dsa_status dsa_group_forward(const dsa_shape* shape, dsa_dtype mla_dtype, int32_
                              void* workspace, size_t ws_bytes,
                              void* const* events, dsa_group_stats* stats, void* stream);
 
+/*
+ * dsa_group_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, results and errors as dsa_group_forward; the
+ * scratch it needs (scores, top-k histograms, split-attention partials) lives in a
+ * device array of DSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends.  The call allocates nothing.
+ *   - A call whose dsa_workspace_bytes(shape, DSA_OP_GROUP) exceeds
+ *     DSA_NOALLOC_SCRATCH_BYTES fails with DSA_ERR_WORKSPACE_TOO_SMALL and enqueues
+ *     nothing (decode batches of the sizes served here need tens of MiB).
+ *   - The scratch is the current device's (hipGetDevice): make the device that owns
+ *     the stream and buffers current.  The first call on a device looks its address
+ *     up (hipGetSymbolAddress); make that call outside graph capture.
+ *   - Every call on one GPU shares that GPU's scratch and the scratch keeps the last
+ *     call's contents (no result depends on them).  Calls that overlap on one GPU
+ *     (other streams, other threads, or replays of graphs holding such calls) race:
+ *     order them on one stream.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dsa_status dsa_group_forward_noalloc(const dsa_shape* shape, dsa_dtype mla_dtype, int32_t n_layers,
+                                     const dsa_layer_type* indexer_types, const dsa_layer_io* layers,
+                                     float sm_scale, dsa_topk_cache* cache, uint64_t tag,
+                                     void* const* events, dsa_group_stats* stats, void* stream);
+
 /* Analytic counters of a group call from host copies of the key ranges (host
  * arrays [B*T]; key_start_host may be NULL for 0, key_end_host NULL for s_cap).
  * Pure host function. */

@@ -294,3 +294,19 @@ def test_group_forward_commits_the_cache_handle_only_after_a_whole_enqueue(L):
     cache = b.TopkCache(FAKE, 1, 4, 8, 1, 3, 5)
     assert _group(L, _shape(s_cap=0), [b.FULL, b.SHARED], [fu, sh], cache, tag=9) == 6
     assert cache.valid == 0 and cache.tag == 5
+
+
+def test_noalloc_group_rejects_calls_beyond_its_scratch_before_anything(L):
+    # the allocation-free group call holds DSA_NOALLOC_SCRATCH_BYTES of device scratch; a
+    # larger need is refused on the host, before any device is touched
+    big = _shape(B=1, T=4096, s_cap=8192, topk=2048, Hm=64, Dc=512, Dr=64)
+    assert L.dsa_workspace_bytes(C.byref(big), b.OP_GROUP) > b.noalloc_scratch_bytes()
+    fu, k1 = _io(True)
+    arr = (b.LayerIO * 1)(fu)
+    types = (C.c_int * 1)(b.FULL)
+    cache = b.TopkCache(FAKE, 0, 0, 0, 0, -1, 0)
+    assert L.dsa_group_forward_noalloc(C.byref(big), b.BF16, 1, types, arr, 0.1, C.byref(cache), 0, None, None,
+                                       None) == 5
+    assert "allocation-free" in b.last_error()
+    assert cache.valid == 0
+    assert b.noalloc_scratch_bytes() == 64 << 20
