@@ -277,6 +277,10 @@ __device__ __forceinline__ void tile_dma16(const void* base, uint32_t off, uint3
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
                : "memory", "m0");
 }
+__device__ __forceinline__ void tile_dma4_off(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void tile_dma4(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
@@ -615,6 +619,351 @@ void indexer_tile(IndexerParams p) {
     }
 }
 
+// ----------------------------------------------------------------- fp8 prefill kernel, specialised waves
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// fp8 index q/k with one key head per query head (D = 128).  A workgroup owns a 128-query x
+// 256-key tile and has 12 waves, three per SIMD:
+//  * 8 compute waves; wave w owns the 64 x 64 block [64 (w >> 2), +64) x [64 (w & 3), +64)
+//    (2 x 2 MFMA tiles of 32 x 32).  They form two groups (waves 0-3 and 4-7, one of each on
+//    every SIMD): in head h group 0 runs the MFMAs of head h and then its epilogue, group 1
+//    the epilogue of head h-1 and then the MFMAs of head h, so on each SIMD one wave feeds the
+//    matrix core while the other keeps the vector ALU busy.  They issue no global loads.
+//  * 4 copy waves (8-11, one per SIMD) issue every global-to-LDS copy: head h's Q and K rows
+//    (128 bytes each) form one 48 KiB LDS stage, three stages are in flight, and the copies
+//    run two heads ahead.  A copy waits in the memory pipeline until its data lands, which
+//    would stall a wave that also has MFMAs or vector work to issue; here only the copy waves
+//    wait.  They also form each head's w * q scale a head early.
+// One barrier per head: after it head h's stage and the per-row vectors of head h+1 are in
+// LDS, and the stage of head h-1 is free for head h+2's copies.
+//
+// A tile's key rows are shared by the workgroups of an XCD that own its query tiles (four on
+// the 128K-prefix chunk), and a copy that misses the L2 takes several heads to land; so one of
+// them, the one with the XCD's first query tile, also requests the key rows of head h + PF
+// into the L2 (a 4-byte global-to-LDS load per 64 bytes into a scratch word per lane).
+//
+// Epilogue, two vector operations per cell: the key scale of each column is pre-scaled by
+// 2^-E, where 2^E bounds the tile's largest key scale times 2^25, so every positive product
+// acc * ks 2^-E lies in (0, 1) (|acc| < 128 * 448^2 < 2^25 for e4m3 codes) and ReLU is the
+// clamp of one v_mul_f32; the weighted sum is one fma with w * q scale.  The tile's sums carry
+// the factor 2^-E, removed when the scores are written; all the powers of two are exact, so
+// each cell is the fp32 number sum over heads of w qs max(acc ks, 0).
+constexpr int G8_BM = 128;                           // queries per tile
+constexpr int G8_BN = 256;                           // keys per tile
+constexpr int G8_CW = 8;                             // compute waves
+constexpr int G8_DW = 4;                             // copy waves
+constexpr int G8_THREADS = 64 * (G8_CW + G8_DW);
+constexpr int G8_NST = 3;                            // tile stages in flight
+constexpr int G8_NV = 5;                             // per-row vector slots (heads h-1 .. h+3)
+constexpr int G8_PF = 6;                             // L2 requests run this many heads ahead
+constexpr int G8_QB = G8_BM * 128;                   // Q rows of one head
+constexpr int G8_STAGE = G8_QB + G8_BN * 128;        // + K rows: 48 KiB
+constexpr int G8_V_WQS = 0;                          // slot: per copy wave c, w then q scale of rows [32c, +32)
+constexpr int G8_V_KC = G8_V_WQS + 2 * G8_BM * 4;    //       k scale [BN]
+constexpr int G8_V_WQ = G8_V_KC + G8_BN * 4;         //       w * q scale [BM]
+constexpr int G8_VSLOT = G8_V_WQ + G8_BM * 4;
+constexpr int G8_VBASE = G8_NST * G8_STAGE;
+constexpr int G8_SINK = G8_VBASE + G8_NV * G8_VSLOT;  // 256 B that the L2 requests land in
+constexpr int G8_LDS = G8_SINK + 256;
+constexpr int G8_CPW = (G8_BM + G8_BN) / 8 / G8_DW;  // 1 KiB tile copies per copy wave per stage (12)
+constexpr int G8_VPW = 2;                            // per-row vector loads per copy wave per head
+constexpr int G8_L2N = 2;                            // L2 requests per copy wave per head (lead)
+static_assert(G8_CPW * 8 * G8_DW == G8_BM + G8_BN, "tile copies must split evenly over the copy waves");
+static_assert(G8_DW * G8_L2N * 64 * 64 == G8_BN * 128, "L2 requests cover the key rows in 64 B steps");
+
+// wait until at most n of this wave's global loads are in flight (n above 40 waits for all)
+__device__ __forceinline__ void g8_wait_loads(int n) {
+  switch (n) {
+#define G8W(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    G8W(0) G8W(1) G8W(2) G8W(3) G8W(4) G8W(5) G8W(6) G8W(7) G8W(8) G8W(9) G8W(10) G8W(11) G8W(12) G8W(13)
+    G8W(14) G8W(15) G8W(16) G8W(17) G8W(18) G8W(19) G8W(20) G8W(21) G8W(22) G8W(23) G8W(24) G8W(25) G8W(26)
+    G8W(27) G8W(28) G8W(29) G8W(30) G8W(31) G8W(32) G8W(33) G8W(34) G8W(35) G8W(36) G8W(37) G8W(38) G8W(39)
+    G8W(40)
+#undef G8W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+__device__ __forceinline__ void g8_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The copy waves' part.
+struct G8Copy {
+  const IndexerParams& p;
+  unsigned char* smem;
+  uint32_t smem_lds;
+  int lane, c, b, t0, H, T;
+  int64_t s0, S;
+  bool lead;                           // this workgroup requests the key rows into the L2
+  const unsigned char* cbase[G8_CPW];  // source of copy i for head 0 (uniform)
+  uint32_t coff[G8_CPW];               // per-lane byte offset from it
+  uint32_t cdst[G8_CPW];               // LDS offset inside a stage (uniform)
+  const float* wqsrc;                  // this lane's w (lanes 0-31) or q scale (32-63) of head 0
+  const float* kcbase;                 // k scale of key s0, head 0 (uniform)
+  uint32_t kcoff;                      // this lane's byte offset from it
+  const unsigned char* l2base;         // key row s0, head 0 (uniform)
+  uint32_t l2off[G8_L2N];              // per-lane 64 B steps of key rows [64c, +64)
+  int issued;                          // global loads issued so far
+  int mark_new, mark_old;              // `issued` after the newest / second-newest tile copies
+
+  __device__ __forceinline__ void setup() {
+    smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+    const unsigned char* qg = static_cast<const unsigned char*>(p.q);
+    const unsigned char* kg = static_cast<const unsigned char*>(p.k);
+    const int64_t row_bytes = (int64_t)H * HD;  // bytes per token of q and of k (fp8, Hk == H)
+#pragma unroll
+    for (int i = 0; i < G8_CPW; ++i) {
+      const int j = G8_CPW * c + i;  // copy j of the stage: 16 Q row octets, then 32 K row octets
+      const bool isk = j >= G8_BM / 8;
+      const int oct = isk ? j - G8_BM / 8 : j;
+      const int row = 8 * oct + (lane >> 3);
+      const int chunk = (lane & 7) ^ tperm(row);
+      // rows past T / S load a valid row; their results are never written
+      const int rr = isk ? (int)(min<int64_t>(s0 + row, S - 1) - s0) : min(t0 + row, T - 1) - t0;
+      cbase[i] = isk ? kg + ((int64_t)b * S + s0) * row_bytes : qg + ((int64_t)b * T + t0) * row_bytes;
+      coff[i] = (uint32_t)(rr * row_bytes + chunk * 16);
+      cdst[i] = (uint32_t)((isk ? G8_QB : 0) + oct * 1024);
+    }
+    // vectors: rows [32c, +32) of w (lanes 0-31) and q scale (lanes 32-63); columns [64c, +64) of k scale
+    {
+      const int r = min(t0 + 32 * c + (lane & 31), T - 1);  // w and q scale: separate tensors, full addresses
+      wqsrc = (lane < 32 ? p.w : p.q_scale) + ((int64_t)b * T + r) * H;
+      const int k = (int)(min<int64_t>(s0 + 64 * c + lane, S - 1) - s0);
+      kcbase = p.k_scale + ((int64_t)b * S + s0) * H;
+      kcoff = (uint32_t)(k * H * 4);
+    }
+    l2base = kg + ((int64_t)b * S + s0) * row_bytes;
+#pragma unroll
+    for (int n = 0; n < G8_L2N; ++n) {
+      const int u = 64 * n + lane;  // 0 .. 127: row 64c + u / 2, half u % 2
+      const int rr = (int)(min<int64_t>(s0 + 64 * c + (u >> 1), S - 1) - s0);
+      l2off[n] = (uint32_t)(rr * row_bytes + 64 * (u & 1));
+    }
+    issued = mark_new = mark_old = 0;
+  }
+
+  __device__ __forceinline__ void copy_vec(int h) {
+    const uint32_t slot = smem_lds + G8_VBASE + (uint32_t)(h % G8_NV) * G8_VSLOT;
+    tile_dma4(wqsrc + h, slot + G8_V_WQS + 256 * c);
+    tile_dma4_off(kcbase + h, kcoff, slot + G8_V_KC + 256 * c);
+    issued += G8_VPW;
+  }
+  __device__ __forceinline__ void copy_tiles(int h) {
+    const uint32_t st = smem_lds + (uint32_t)(h % G8_NST) * G8_STAGE;
+#pragma unroll
+    for (int i = 0; i < G8_CPW; ++i) tile_dma16(cbase[i] + (int64_t)h * HD, coff[i], st + cdst[i]);
+    issued += G8_CPW;
+    mark_old = mark_new;
+    mark_new = issued;
+  }
+  __device__ __forceinline__ void l2_request(int h) {
+#pragma unroll
+    for (int n = 0; n < G8_L2N; ++n) tile_dma4_off(l2base + (int64_t)h * HD, l2off[n], smem_lds + G8_SINK);
+    issued += G8_L2N;
+  }
+  // the copies issued so far are those of heads 0 .. min(h + 1, H - 1): head h's are the
+  // second-newest or, for the last head, the newest (loads complete in issue order)
+  __device__ __forceinline__ void wait_head(int h) const {
+    g8_wait_loads(issued - (h + 1 < H ? mark_old : mark_new));
+  }
+  // w * q scale of head h for rows [32c, +32) (this wave loaded both)
+  __device__ __forceinline__ void prep(int h) const {
+    float* v = reinterpret_cast<float*>(smem + G8_VBASE + (h % G8_NV) * G8_VSLOT);
+    if (lane < 32) v[G8_V_WQ / 4 + 32 * c + lane] = v[G8_V_WQS / 4 + 64 * c + lane] * v[G8_V_WQS / 4 + 64 * c + 32 + lane];
+  }
+
+  __device__ __forceinline__ void run() {
+    // prologue: vectors of heads 0..2 and tile copies of heads 0..1, each head's vectors ahead
+    // of the copies of the head before it, then L2 requests of heads 2 .. PF-1
+    copy_vec(0);
+    for (int h = 0; h < min(2, H); ++h) {
+      if (h + 1 < H) copy_vec(h + 1);
+      copy_tiles(h);
+    }
+    g8_wait_loads(issued - G8_VPW);  // head 0's vectors
+    prep(0);
+    if (lead)
+      for (int h = 2; h < min(G8_PF, H); ++h) l2_request(h);
+    for (int h = 0; h < H; ++h) {
+      wait_head(h);                  // head h's tile and head h+1's vectors (issued before it)
+      if (h + 1 < H) prep(h + 1);
+      g8_barrier();
+      if (h + 2 < H) {
+        if (h + 3 < H) copy_vec(h + 3);
+        copy_tiles(h + 2);
+        if (lead && h + G8_PF < H) l2_request(h + G8_PF);
+      }
+    }
+  }
+};
+
+// The compute waves' part.
+struct G8Math {
+  unsigned char* smem;
+  int lane, wv, grp, wm, wn, lr, lg, H;
+  uint32_t abase, bbase;               // fragment offsets (k-step 0) inside a stage
+  float down;                          // 2^-E of the tile
+  f32x16 acc[2][2], tot[2][2];
+
+  __device__ __forceinline__ void setup() {
+    const uint32_t sw = 16u * (uint32_t)((2 * lg) ^ tperm(lr));
+    abase = (uint32_t)(64 * wm + lr) * 128u + sw;
+    bbase = (uint32_t)G8_QB + (uint32_t)(64 * wn + lr) * 128u + sw;
+  }
+  // 32-byte fragment (k-step ks) of the row at `o` (k-step 0 offset) of a stage
+  __device__ __forceinline__ static i32x8 frag(const unsigned char* st, uint32_t o, int ks) {
+    const uint32_t x = o ^ (64u * (uint32_t)ks);
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(st + x);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(st + (x ^ 16u));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  // head h's contraction (stage h % NST) into acc
+  __device__ __forceinline__ void mfma(int h) {
+    const unsigned char* st = smem + (h % G8_NST) * G8_STAGE;
+    uint32_t ab = abase, bb_ = bbase;
+    asm volatile("" : "+v"(ab), "+v"(bb_));
+    const f32x16 zero = {};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const i32x8 b0 = frag(st, bb_, ks), b1 = frag(st, bb_ + 4096u, ks);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const i32x8 a = frag(st, ab + 4096u * i, ks);
+        acc[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b0, ks ? acc[i][0] : zero, 0, 0, 0, 127, 0, 127);
+        acc[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b1, ks ? acc[i][1] : zero, 0, 0, 0, 127, 0, 127);
+      }
+    }
+  }
+  // epilogue of head h: tot += (w qs) * clamp(acc * ks 2^-E); result row 8(r/4) + 4lg + r%4
+  __device__ __forceinline__ void epilogue(int h) {
+    const float* v = reinterpret_cast<const float*>(smem + G8_VBASE + (h % G8_NV) * G8_VSLOT);
+    float kc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) kc[j] = v[G8_V_KC / 4 + 64 * wn + 32 * j + lr] * down;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const float4 w4 = *reinterpret_cast<const float4*>(v + G8_V_WQ / 4 + 64 * wm + 32 * i + 8 * rq + 4 * lg);
+        const float wr[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            tot[i][j][r] = fmaf(wr[e], __builtin_amdgcn_fmed3f(acc[i][j][r] * kc[j], 0.f, 1.f), tot[i][j][r]);
+          }
+      }
+  }
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[i][j][r] = 0.f;
+    if (grp == 0) {
+      for (int h = 0; h < H; ++h) {
+        g8_barrier();
+        mfma(h);
+        epilogue(h);
+      }
+    } else {
+      for (int h = 0; h < H; ++h) {
+        g8_barrier();
+        if (h > 0) epilogue(h - 1);
+        mfma(h);
+      }
+      epilogue(H - 1);
+    }
+  }
+};
+
+template <int>
+__global__ __attribute__((amdgpu_flat_work_group_size(G8_THREADS, G8_THREADS), amdgpu_waves_per_eu(3, 3)))
+void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int32_t rks[G8_BM], rke[G8_BM];
+  __shared__ float wmax[G8_CW + G8_DW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y;
+  const int bid = blockIdx.x;
+  int qy, kx;
+  if (xcd_order) {
+    // Workgroups are dispatched to the 8 XCDs in turn (block i to XCD i % 8).  Each XCD owns
+    // nq / 8 query tiles and sweeps the key tiles in order, so its query tiles stay in its L2
+    // and the workgroups of an XCD that share a key tile read it at about the same time.
+    const int per = nq / 8, xcd = bid % 8, slot = bid / 8;
+    qy = xcd * per + slot % per;
+    kx = slot / per;
+  } else {
+    qy = bid % nq;
+    kx = bid / nq;
+  }
+  const int t0 = qy * G8_BM;
+  const int64_t s0 = (int64_t)kx * G8_BN;
+  const int T = p.T;
+  const int64_t S = p.s_cap;
+
+  int live = 0;
+  if (tid < G8_BM) {
+    const int t = t0 + tid;
+    int64_t ks = 0, ke = 0;
+    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, S, ks, ke);
+    rks[tid] = (int32_t)ks;
+    rke[tid] = (int32_t)ke;
+    live = (t < T) && (ks < s0 + G8_BN) && (ke > s0) && (ks < ke);
+  }
+  if (!__syncthreads_or(live)) return;
+
+  // 2^E bounds the tile's largest key scale (all heads) times 2^25
+  int tile_e;
+  {
+    const float* ksrc = p.k_scale + ((int64_t)b * S + s0) * p.H;
+    const int nks = (int)min<int64_t>(G8_BN, S - s0) * p.H;
+    float m = 0.f;
+    for (int i = tid; i < nks; i += G8_THREADS) m = fmaxf(m, ksrc[i]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    m = wmax[0];
+#pragma unroll
+    for (int i = 1; i < G8_CW + G8_DW; ++i) m = fmaxf(m, wmax[i]);
+    int x = 0;
+    (void)frexpf(m, &x);  // m < 2^x
+    tile_e = 25 + x;
+  }
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, so the role branches are too
+  if (wv >= G8_CW) {
+    G8Copy cw{p, smem, 0u, lane, wv - G8_CW, b, t0, p.H, T, s0, S, xcd_order && qy % (nq / 8) == 0};
+    cw.setup();
+    cw.run();
+    return;  // every load it issued has landed (the last head waits for all)
+  }
+  G8Math w{smem, lane, wv, wv >> 2, wv >> 2, wv & 3, lane & 31, lane >> 5, p.H};
+  w.down = ldexpf(1.f, -tile_e);
+  w.setup();
+  w.run();
+
+  // candidate cells of the wave's block: row 64wm + 32i + 8(r/4) + 4lg + r%4, column 64wn + 32j + lr;
+  // the sums carry 2^-E
+  const float up = ldexpf(1.f, tile_e);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int64_t s = s0 + 64 * w.wn + 32 * j + w.lr;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
+        const int t = t0 + m;
+        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = w.tot[i][j][r] * up;
+      }
+  }
+}
+#pragma clang diagnostic pop
+
 // ----------------------------------------------------------------- decode streaming kernel
 // Few queries per batch item (decode): the work is one pass over the item's index
 // keys, so this kernel streams them from HBM with whole-row 16-byte loads and does
@@ -721,6 +1070,20 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches) {
   if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;
   const bool mfma = (dt == BF16 || dt == FP8) && p.D == HD;
+  if (dt == FP8 && p.D == HD && p.Hk == p.H && p.T >= 64 && p.B <= 65535) {
+    const int nq = (p.T + G8_BM - 1) / G8_BM;
+    const int64_t nk = (p.s_cap + G8_BN - 1) / G8_BN;
+    if ((int64_t)nq * nk <= INT32_MAX) {
+      hipError_t e;
+      if ((e = DSA_ALLOW_LDS(indexer_fp8_groups<0>, G8_LDS)) != hipSuccess) return e;
+      // query tiles per XCD when they split evenly and the grid is not a causal square
+      const int xcd = (nq % 8 == 0) && (p.T != p.s_cap);
+      hipLaunchKernelGGL(indexer_fp8_groups<0>, dim3((unsigned)(nq * nk), (unsigned)p.B), dim3(G8_THREADS),
+                         G8_LDS, st, p, nq, (int)nk, xcd);
+      if (n_launches) ++*n_launches;
+      return hipGetLastError();
+    }
+  }
   if (mfma && p.T >= 32) {
     const size_t lds = (size_t)(dt == BF16 ? TileCfg<BF16>::LDS : TileCfg<FP8>::LDS);
     dim3 grid((unsigned)((p.s_cap + PK - 1) / PK), (unsigned)((p.T + PQ - 1) / PQ), (unsigned)p.B);
