@@ -4,14 +4,18 @@ A step is one dsa_group_forward over the workload's whole layer list (indexer
 scores -> top-k -> sparse MLA on full layers, sparse MLA with the cached indices
 on shared layers) for one batch of synthetic queries whose inputs are already
 resident in HBM.  Prints one JSON line:
-  value          query tokens/s per 4-layer group = B*T / (step time) * n_layers / 4
-  roofline       the dominant kernel (sparse MLA on a prefill workload): algorithmic
-                 FLOPs per launch / mean launch time (HIP events recorded by the
-                 library around each launch on the timed stream) vs bf16 MFMA peak
-  kernels        the same for every kernel family (indexer vs MFMA peak, top-k vs HBM)
-  cpu_baseline   the CPU oracle on a bounded sample of query rows of the same workload
+  value          query tokens/s per 4-layer group = B*T / (step time) * n_layers / 4, on the
+                 4096-query fp8 chunk over a 131,072-token prefix by default
+  roofline       the kernel with the largest share of the step: algorithmic FLOPs (or
+                 bytes) per launch / mean launch time (HIP events recorded by the library
+                 around each launch on the timed stream) vs the MFMA peak of its input
+                 type (or HBM)
+  kernels        the same for every kernel family
+  cpu_baseline   the CPU oracle on a time-bounded sample of query rows of the same workload
+  workloads      the same measurements for the 4096-token prefill and the two decodes
+                 (the decodes also as HIP-graph replays of one group call)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-sub]
 """
 from __future__ import annotations
 
@@ -28,16 +32,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "query tokens/s per 4-layer F/S group (indexer+top-k+sparse MLA); MFMA% & HBM GB/s"
+# the headline: the largest single-GPU workload by work per group (4096 queries over a 131,072-token
+# prefix, fp8 index keys); the others follow as sub-results
+HEADLINE = "chunk128k_fp8"
+SUB_WORKLOADS = ["prefill4k_bf16", "decode32k_b64_bf16", "decode1m_b4_fp8"]
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
-# HBM bytes per launch of the roofline kernel from rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE on
-# `bench.py --steps 2 --warmup 1 --no-cpu-baseline`, each scaled by the same counter's reading
-# on a plain copy of known size (`bench.py --copy-calibration`); keyed (workload, kernel) and
-# removed whenever that kernel changes (then reported as null).
-MEASURED_TRAFFIC_BYTES = {
-    ("decode32k_b64_bf16", "indexer_stream"): 8426542.5 * 1024 * 2.0 + 18968.1 * 1024 * 1.0,
-    ("prefill4k_bf16", "mla_mfma"): 314211.4 * 1024 * 2.0 + 263168.0 * 1024 * 1.0,
+# HBM bytes per launch of the roofline kernel from two rocprofv3 --pmc runs (FETCH_SIZE, then
+# WRITE_SIZE) of `bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-sub --workload <name>`, each
+# scaled by the same counter's reading on a plain copy of known size (`bench.py --copy-calibration`);
+# keyed (workload, kernel), with the profile summary it comes from, and removed whenever that kernel
+# changes (then reported as null).
+MEASURED_TRAFFIC = {
+    ("decode32k_b64_bf16", "indexer_stream"): {
+        "bytes": 8426542.5 * 1024 * 2.0 + 18968.1 * 1024 * 1.0,
+        "source": "profiles/indexer_stream_decode32k_b64_bf16_hbm_counters.md"},
 }
 
 
@@ -46,12 +56,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill4k_bf16")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="time budget of the CPU oracle baseline (rows evenly spaced over the workload, "
+                         "taken in a fixed order until the budget is spent)")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="time only --workload (by default the other workloads follow as sub-results)")
     ap.add_argument("--graph", action="store_true",
-                    help="also capture one group call as a HIP graph and time K replays (reported beside the "
-                         "eager figures)")
+                    help="also time HIP-graph replays of one group call for --workload (the sub-results "
+                         "of decode workloads always carry them)")
     ap.add_argument("--backward", action="store_true",
                     help="time layer 0's backward instead of the forward group: the sparse MLA backward (its "
                          "forward's indices, output and lse, a seeded output gradient) and the index-score "
@@ -124,51 +138,186 @@ def blas_threads():
         return 1
 
 
-def cpu_baseline(w, inputs, rows):
-    """The oracle, as it stands, on `rows` query rows spread over the workload (all layers)."""
+def sample_order(n):
+    """Row indices 0..n-1 in an order whose every prefix is spread over the whole range
+    (bit-reversal order of the next power of two), so a time-bounded sample stays even."""
+    m = 1 << max(0, (n - 1).bit_length())
+    bits = max(1, m.bit_length() - 1)
+    order = [int(format(i, f"0{bits}b")[::-1], 2) for i in range(m)] if m > 1 else [0]
+    return [i for i in order if i < n]
+
+
+def cpu_baseline(w, inputs, seconds, max_rows=None):
+    """The oracle, as it stands, on query rows spread over the workload (all layers), taken until
+    `seconds` of work are spent (at least two rows)."""
     import oracle as O
     blas = blas_threads()
     types = ["full" if c == "F" else "shared" for c in w.layers]
     ke, ks = w.key_end(), w.key_start()
     picks = [(b, t) for b in range(w.B) for t in range(w.T)]
-    sel = [picks[i] for i in np.linspace(0, len(picks) - 1, min(rows, len(picks))).astype(int)]
-    dec = [{} for _ in inputs]
-    t0 = time.perf_counter()
-    for l, L in enumerate(inputs):
-        dec[l]["kv"] = {}
-        if types[l] == "full":
-            dec[l]["k"] = {}
+    order = [picks[i] for i in sample_order(len(picks))]
+    if max_rows:
+        order = order[:max_rows]
+    dec = [{"kv": {}, "k": {}} for _ in inputs]
     done = 0
-    phase = {"score": 0.0, "sort": 0.0, "attention": 0.0}
-    for (b, t) in sel:
+    phase = {"decode": 0.0, "score": 0.0, "sort": 0.0, "attention": 0.0}
+    t0 = time.perf_counter()
+    for (b, t) in order:
         idx = None
         for l, L in enumerate(inputs):
+            p0 = time.perf_counter()
+            if types[l] == "full" and b not in dec[l]["k"]:
+                dec[l]["k"][b] = O.decode(L["idx_k"][b], w.idx_dtype,
+                                          L["idx_k_scale"][b] if "idx_k_scale" in L else None)
+            if b not in dec[l]["kv"]:
+                dec[l]["kv"][b] = O.decode(L["kv"][b], w.mla_dtype)
+            p1 = time.perf_counter()
+            phase["decode"] += p1 - p0
             if types[l] == "full":
-                if b not in dec[l]["k"]:
-                    dec[l]["k"][b] = O.decode(L["idx_k"][b], w.idx_dtype, L.get("idx_k_scale", [None] * w.B)[b]
-                                              if "idx_k_scale" in L else None)
                 qs = L["idx_q_scale"][b, t] if "idx_q_scale" in L else None
-                p0 = time.perf_counter()
                 q = O.decode(L["idx_q"][b, t], w.idx_dtype, qs)
                 row = O.index_scores_row(q, dec[l]["k"][b], L["w"][b, t].astype(np.float64),
                                          int(ks[b, t]), int(ke[b, t]))
-                p1 = time.perf_counter()
-                idx, _ = O.topk_row(row, int(ks[b, t]), int(ke[b, t]), w.topk)
                 p2 = time.perf_counter()
-                phase["score"] += p1 - p0
-                phase["sort"] += p2 - p1
-            if b not in dec[l]["kv"]:
-                dec[l]["kv"][b] = O.decode(L["kv"][b], w.mla_dtype)
-            p0 = time.perf_counter()
+                idx, _ = O.topk_row(row, int(ks[b, t]), int(ke[b, t]), w.topk)
+                p3 = time.perf_counter()
+                phase["score"] += p2 - p1
+                phase["sort"] += p3 - p2
+                p1 = p3
             O.sparse_mla_row(O.decode(L["mla_q"][b, t], w.mla_dtype), dec[l]["kv"][b], idx, w.sm_scale, w.Dc)
-            phase["attention"] += time.perf_counter() - p0
+            phase["attention"] += time.perf_counter() - p1
         done += 1
+        if done >= 2 and time.perf_counter() - t0 >= seconds:
+            break
     dt = time.perf_counter() - t0
     return {"value": done / dt * w.n_layers / 4.0, "unit": "query tokens/s", "cores": int(blas),
             "kind": "oracle",
-            "sample": f"{done} query rows evenly spaced over the {w.B}x{w.T} rows of {w.name}, all "
-                      f"{w.n_layers} layers, float64 NumPy, {dt:.1f} s (input decoding included)",
+            "sample": f"{done} of the {w.B}x{w.T} query rows of {w.name} (spread over the rows in bit-reversed "
+                      f"order, taken until {seconds:.0f} s were spent), all {w.n_layers} layers, float64 NumPy, "
+                      f"{dt:.1f} s including decoding of the inputs they read",
             "phase_s": {k: round(v, 2) for k, v in phase.items()}, "host": host_info()}
+
+
+def run_forward(w, dev, steps, warmup, graph, torch, B):
+    """Time `steps` group calls of workload w (inputs resident in HBM) after `warmup` untimed ones.
+    Per-kernel times come from HIP events the library records around each launch on the timed
+    stream.  Returns the measurement dict of the workload."""
+    ke_host, ks_host = w.key_end(), w.key_start()
+    ke = torch.from_numpy(ke_host).cuda()
+    ks = torch.from_numpy(ks_host).cuda() if ks_host.any() else None
+    types = ["full" if c == "F" else "shared" for c in w.layers]
+    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
+                         key_start=ks, key_end=ke, key_start_host=ks_host if ks is not None else None,
+                         key_end_host=ke_host)
+    ws = torch.empty(max(B.workspace_bytes(shape, B.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
+    cache = B.IndexCache(w.B, w.T, w.topk)
+    mdt = B.F32 if w.mla_dtype == "f32" else B.BF16
+    stream = torch.cuda.current_stream()
+    n = len(types)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6 * n)]
+        for e in evs:
+            e.record(stream)           # creates the HIP event; the library re-records it
+        return evs
+
+    stats = None
+    for _ in range(warmup):
+        stats = B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream)
+    events = [new_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(steps):
+        B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream,
+                        events=[e.cuda_event for e in events[s]])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    if stats is None:
+        idt = {"f32": B.F32, "bf16": B.BF16, "fp8": B.FP8_E4M3}[w.idx_dtype]
+        stats = B.group_stats_compute(shape, idt, mdt, types, ks_host, ke_host)
+
+    def mean_ms(slot, layers):
+        v = [events[s][6 * l + slot].elapsed_time(events[s][6 * l + slot + 1]) for s in range(steps) for l in layers]
+        return float(np.mean(v)) if v else None
+
+    full = [l for l in range(n) if types[l] == "full"]
+    nf = max(len(full), 1)
+    t_idx, t_topk, t_attn = mean_ms(0, full), mean_ms(2, full), mean_ms(4, range(n))
+    idx_flops = stats.indexer_flops / nf
+    idx_bytes = stats.indexer_bytes / nf
+    topk_bytes = stats.topk_bytes / nf
+    attn_flops, attn_bytes = stats.attn_flops / n, stats.attn_bytes / n
+    prefill = w.T > 1
+    idx_peak = PEAK_FP8_TFLOPS if w.idx_dtype == "fp8" else PEAK_BF16_TFLOPS
+    kernels = {
+        "indexer": {"ms": t_idx, "tflops": idx_flops / (t_idx * 1e-3) / 1e12 if t_idx else None,
+                    "gbs": idx_bytes / (t_idx * 1e-3) / 1e9 if t_idx else None},
+        "topk": {"ms": t_topk, "gbs": topk_bytes / (t_topk * 1e-3) / 1e9 if t_topk else None},
+        "sparse_mla": {"ms": t_attn, "tflops": attn_flops / (t_attn * 1e-3) / 1e12,
+                       # every selected row's bytes per query: mostly served by the caches on a prefill
+                       "gather_gbs_algorithmic": attn_bytes / (t_attn * 1e-3) / 1e9},
+    }
+    # roofline of the kernel family with the largest share of the step: prefill kernels are
+    # dense matrix-core work (bound: the MFMA peak of their input type), decode kernels and
+    # top-k stream memory (bound: HBM)
+    share = {"indexer": (t_idx or 0.0) * len(full), "topk": (t_topk or 0.0) * len(full), "sparse_mla": t_attn * n}
+    dom = max(share, key=share.get)
+    if dom == "indexer" and prefill:
+        kname = "indexer_tile<FP8>" if w.idx_dtype == "fp8" else "indexer_tile<BF16>"
+        roof = {"bound": "mfma", "achieved": kernels["indexer"]["tflops"], "peak": idx_peak, "unit": "TFLOP/s",
+                "kernel": kname, "algorithmic_per_launch": idx_flops, "launch_ms": t_idx}
+        if w.idx_dtype == "fp8":
+            roof["frac_of_bf16_peak"] = roof["achieved"] / PEAK_BF16_TFLOPS
+    elif dom == "indexer":
+        roof = {"bound": "hbm", "achieved": kernels["indexer"]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "indexer_stream", "algorithmic_per_launch": idx_bytes, "launch_ms": t_idx}
+    elif dom == "topk":
+        roof = {"bound": "hbm", "achieved": kernels["topk"]["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "topk", "algorithmic_per_launch": topk_bytes, "launch_ms": t_topk}
+    elif prefill:
+        roof = {"bound": "mfma", "achieved": kernels["sparse_mla"]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "kernel": "mla_mfma", "algorithmic_per_launch": attn_flops, "launch_ms": t_attn}
+    else:
+        ach = attn_bytes / (t_attn * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "kernel": "mla_mfma+mla_combine", "algorithmic_per_launch": attn_bytes, "launch_ms": t_attn}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr = MEASURED_TRAFFIC.get((w.name, roof["kernel"]))
+    roof["traffic"] = tr["bytes"] if tr else None
+    if tr:
+        roof["traffic_source"] = tr["source"]
+    step_dev = [events[s][0].elapsed_time(events[s][6 * n - 1]) for s in range(steps)]
+    tokens = w.B * w.T
+    res = {"value": tokens / (elapsed / steps) * n / 4.0, "ms_per_step": elapsed / steps * 1e3,
+           "roofline": roof, "kernels": kernels,
+           "step_device_ms": {f"p{q}": float(np.percentile(step_dev, q)) for q in (10, 50, 90)},
+           "graph": None, "_cache": cache, "_stream": stream}
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=side)
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        gel = time.perf_counter() - t0
+        res["graph"] = {"ms_per_step": gel / steps * 1e3, "value": tokens / (gel / steps) * n / 4.0,
+                        "replays": steps}
+        del g
+    return res
+
+
+def config_of(w):
+    return {"workload": w.name, "batch": w.B, "queries_per_item": w.T, "prefix": w.S, "layers": w.layers,
+            "index_heads": w.H, "index_dim": w.D, "index_key_heads": w.Hk, "index_dtype": w.idx_dtype,
+            "topk": w.topk, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"}
 
 
 def main():
@@ -191,151 +340,47 @@ def main():
     t0 = time.perf_counter()
     inputs = synth.build_inputs(w)
     dev = upload(w, inputs, torch)
-    ke_host, ks_host = w.key_end(), w.key_start()
-    ke = torch.from_numpy(ke_host).cuda()
-    ks = torch.from_numpy(ks_host).cuda() if ks_host.any() else None
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    types = ["full" if c == "F" else "shared" for c in w.layers]
-    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr,
-                         key_start=ks, key_end=ke)
-    ws = torch.empty(max(B.workspace_bytes(shape, B.OP_GROUP), 1), dtype=torch.uint8, device="cuda")
-    cache = B.IndexCache(w.B, w.T, w.topk)
-    mdt = B.F32 if w.mla_dtype == "f32" else B.BF16
-    idt = {"f32": B.F32, "bf16": B.BF16, "fp8": B.FP8_E4M3}[w.idx_dtype]
-    stats = B.group_stats_compute(shape, idt, mdt, types, ks_host, ke_host)
-    stream = torch.cuda.current_stream()
-
-    n = len(types)
-    steps = args.steps
-
-    def new_events():
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6 * n)]
-        for e in evs:
-            e.record(stream)           # creates the HIP event; the library re-records it
-        return evs
-
-    for _ in range(args.warmup):
-        B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream)
-    events = [new_events() for _ in range(steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(steps):
-        B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=stream,
-                        events=[e.cuda_event for e in events[s]])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
-    ms_step = elapsed / steps * 1e3
-
-    # per-kernel mean durations from the library's event records on the timed stream
-    def mean_ms(slot, layers):
-        v = [events[s][6 * l + slot].elapsed_time(events[s][6 * l + slot + 1]) for s in range(steps) for l in layers]
-        return float(np.mean(v)) if v else None
-
-    full_layers = [l for l in range(n) if types[l] == "full"]
-    t_idx = mean_ms(0, full_layers)
-    t_topk = mean_ms(2, full_layers)
-    t_attn = mean_ms(4, range(n))
-    idx_flops = stats.indexer_flops / max(len(full_layers), 1)
-    attn_flops = stats.attn_flops / n
-    attn_bytes = stats.attn_bytes / n
-    topk_bytes = stats.topk_bytes / max(len(full_layers), 1)
-    idx_peak = PEAK_FP8_TFLOPS if w.idx_dtype == "fp8" else PEAK_BF16_TFLOPS
-    kernels = {
-        "indexer": {"ms": t_idx, "tflops": idx_flops / (t_idx * 1e-3) / 1e12 if t_idx else None,
-                    "peak_tflops": idx_peak, "gbs": stats.indexer_bytes / max(len(full_layers), 1) / (t_idx * 1e-3) / 1e9
-                    if t_idx else None},
-        "topk": {"ms": t_topk, "gbs": topk_bytes / (t_topk * 1e-3) / 1e9 if t_topk else None,
-                 "peak_gbs": PEAK_HBM_GBS},
-        "sparse_mla": {"ms": t_attn, "tflops": attn_flops / (t_attn * 1e-3) / 1e12,
-                       "gbs": attn_bytes / (t_attn * 1e-3) / 1e9, "peak_tflops": PEAK_BF16_TFLOPS},
-    }
-    # roofline of the kernel that takes the largest share of the step; prefill kernels are
-    # dense matrix-core work (bound: MFMA peak of their input type), decode kernels and
-    # top-k stream memory (bound: HBM)
-    prefill = w.T > 1
-    nf = max(len(full_layers), 1)
-    cands = {
-        "indexer": (t_idx or 0.0) * len(full_layers),
-        "topk": (t_topk or 0.0) * len(full_layers),
-        "sparse_mla": t_attn * n,
-    }
-    dom = max(cands, key=cands.get)
-    if dom == "indexer" and prefill:
-        ach = idx_flops / (t_idx * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": idx_peak, "unit": "TFLOP/s",
-                "kernel": "indexer_tile", "algorithmic_per_launch": idx_flops}
-    elif dom == "indexer":
-        byt = stats.indexer_bytes / nf
-        ach = byt / (t_idx * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "kernel": "indexer_stream", "algorithmic_per_launch": byt}
-    elif dom == "topk":
-        ach = topk_bytes / (t_topk * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "kernel": "topk_rows", "algorithmic_per_launch": topk_bytes}
-    elif prefill:
-        ach = attn_flops / (t_attn * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "kernel": "mla_mfma", "algorithmic_per_launch": attn_flops}
-    else:
-        ach = attn_bytes / (t_attn * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "kernel": "mla_mfma", "algorithmic_per_launch": attn_bytes}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = MEASURED_TRAFFIC_BYTES.get((w.name, roof["kernel"])) if MEASURED_TRAFFIC_BYTES else None
-
-    # per-step device times from the library's first and last event records of each call
-    step_dev = [events[s][0].elapsed_time(events[s][6 * n - 1]) for s in range(steps)]
-    pct = {f"p{q}": float(np.percentile(step_dev, q)) for q in (10, 50, 90)}
-
-    tokens = w.B * w.T
-    graph = None
-    if args.graph:
-        g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                B.group_forward(shape, mdt, types, dev, w.sm_scale, cache, 1, ws, stream=side)
-        torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        gel = time.perf_counter() - t0
-        graph = {"ms_per_step": gel / steps * 1e3, "value": tokens / (gel / steps) * n / 4.0}
-    value = tokens / (elapsed / steps) * n / 4.0
-    res = {
-        "metric": METRIC, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16" if w.mla_dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "queries_per_item": w.T, "prefix": w.S, "layers": w.layers,
-                   "index_heads": w.H, "index_dim": w.D, "index_key_heads": w.Hk, "index_dtype": w.idx_dtype,
-                   "topk": w.topk, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}", "parallelism": "single GPU"},
-        "roofline": roof,
-        "kernels": kernels,
-        "step_device_ms": pct,
-        "graph": graph,
-    }
     if args.backward:
-        res = backward(args, w, inputs, dev, cache, torch, B, stream)
-    elif not args.no_cpu_baseline:
+        m = run_forward(w, dev, 1, 1, False, torch, B)
+        print(json.dumps(backward(args, w, inputs, dev, m["_cache"], torch, B, m["_stream"])))
+        return
+    m = run_forward(w, dev, args.steps, args.warmup, args.graph, torch, B)
+    print(f"[bench] {w.name}: {m['ms_per_step']:.3f} ms per group call", file=sys.stderr, flush=True)
+    res = {
+        "metric": METRIC, "value": m["value"], "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": m["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.mla_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": config_of(w), "roofline": m["roofline"], "kernels": m["kernels"],
+        "step_device_ms": m["step_device_ms"], "graph": m["graph"],
+    }
+    del dev
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_rows)
-        try:  # the same oracle on one thread, on a smaller sample
-            from threadpoolctl import threadpool_limits
-            with threadpool_limits(limits=1):
-                one = cpu_baseline(w, inputs, max(1, args.cpu_rows // 16))
-            res["cpu_baseline"]["one_core"] = {"value": one["value"], "sample": one["sample"],
-                                               "blas_threads": one["host"]["blas_threads"]}
-        except ImportError:
-            pass
+        res["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+    del inputs
+    if not args.no_sub:
+        res["workloads"] = {}
+        for name in SUB_WORKLOADS:
+            if name == w.name:
+                continue
+            sw = synth.WORKLOADS[name]
+            print(f"[bench] sub-result {name}: generating inputs", file=sys.stderr, flush=True)
+            t0 = time.perf_counter()
+            sdev = upload(sw, synth.build_inputs(sw), torch)
+            print(f"[bench] sub-result {name}: inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+                  flush=True)
+            sm = run_forward(sw, sdev, max(3, args.steps // 2), args.warmup, sw.T == 1, torch, B)
+            res["workloads"][name] = {"config": config_of(sw), "steps": max(3, args.steps // 2),
+                                      **{k: v for k, v in sm.items() if not k.startswith("_")}}
+            print(f"[bench] sub-result {name}: {sm['ms_per_step']:.3f} ms per group call", file=sys.stderr,
+                  flush=True)
+            del sdev, sm
+            torch.cuda.empty_cache()
     print(json.dumps(res))
 
 
@@ -412,7 +457,7 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
         dout_h = dout.to(torch.float64).cpu().numpy()
         q_h = O.decode(inputs[0]["mla_q"], w.mla_dtype)
         picks = [(b, t) for b in range(w.B) for t in range(w.T)]
-        n = min(len(picks), max(1, args.cpu_rows // 8))
+        n = min(len(picks), 256)
         sel = [picks[i] for i in np.linspace(0, len(picks) - 1, n).astype(int)]
         dI_h = dI.to(torch.float64).cpu().numpy()
         I0 = inputs[0]
