@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["indexer.hip", "topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip", "indexer_bwd.hip", "prep.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "indexer_topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip", "indexer_bwd.hip", "prep.hip", "dsa_api.cpp"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

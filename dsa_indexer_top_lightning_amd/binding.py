@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 FULL, SHARED = 0, 1
-OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP = 0, 1, 2, 3
+OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP, OP_INDEXER_TOPK = 0, 1, 2, 3, 4
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_NO_DONOR",
           4: "DSA_ERR_STALE_CACHE", 5: "DSA_ERR_WORKSPACE_TOO_SMALL", 6: "DSA_ERR_HIP"}
 
@@ -65,6 +65,8 @@ _SIGS = {
                                      C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]),
     "dsa_topk_select": (C.c_int, [C.POINTER(Shape), C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t,
                                   C.c_void_p]),
+    "dsa_indexer_topk": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "dsa_sparse_mla_attention": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                            C.c_float, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
                                            C.c_void_p]),
@@ -197,6 +199,20 @@ def topk_select(scores, out, s_cap, *, key_start=None, key_end=None, workspace=N
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_topk_select(C.byref(shape), _dev_ptr(scores), scores.shape[-1], _dev_ptr(out),
                                  _dev_ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def indexer_topk(q, k, w, out, *, q_scale=None, k_scale=None, key_start=None, key_end=None, sample_stride=0,
+                 workspace=None, stream=None):
+    """dsa_indexer_topk.  q [B,T,H,D], k [B,S,Hk,D], w [B,T,H], out [B,T,topk] int32 (written in place);
+    workspace: uint8 tensor of at least workspace_bytes(shape, OP_INDEXER_TOPK) bytes."""
+    B, T, H, D = q.shape
+    S, Hk = k.shape[1], k.shape[2]
+    shape = make_shape(B, T, S, H=H, D=D, Hk=Hk, topk=out.shape[-1], key_start=key_start, key_end=key_end)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().dsa_indexer_topk(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(q_scale), _dev_ptr(k),
+                                  _dev_ptr(k_scale), _dev_ptr(w), _dev_ptr(out), int(sample_stride),
+                                  _dev_ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 

@@ -115,11 +115,29 @@ size_t mla_ws(const dsa_shape* s, dsa_dtype dt) {
 }
 size_t scores_bytes(const dsa_shape* s) { return align_up((size_t)rows_of(s) * (size_t)s->s_cap * sizeof(float)); }
 
+// Full layers of a group over rows at least this long run the fused indexer -> top-k.
+constexpr int64_t kFuseMinKeys = 65536;
+
 dsa::IndexerParams indexer_params(const dsa_shape* s, const void* q, const float* qs, const void* k,
                                   const float* ksc, const float* w, float* scores, int64_t ld) {
   return dsa::IndexerParams{s->B, s->T, s->H, s->D, s->Hk, s->s_cap, s->key_start, s->key_end, q, qs, k, ksc, w,
                             scores, ld};
 }
+// Whether dsa_indexer_topk runs the shape without the score matrix (for this dtype / any dtype).
+bool fused_shape(const dsa_shape* s, dsa_dtype dt) {
+  return dsa::indexer_topk_fused(indexer_params(s, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s->s_cap),
+                                 (dsa::Dtype)dt, s->topk);
+}
+bool fused_any(const dsa_shape* s) { return fused_shape(s, DSA_BF16) || fused_shape(s, DSA_FP8_E4M3); }
+size_t indexer_topk_ws(const dsa_shape* s, bool fused) {
+  return dsa::indexer_topk_workspace_bytes(s->B, s->T, s->topk, s->s_cap, fused);
+}
+// Inside a group only prefill chunks fuse (fp8 tile kernel, T >= 64): for decode rows the score
+// round trip is small beside the key stream and the fused passes cost more than it.
+bool group_fuses(const dsa_shape* s, dsa_dtype dt) {
+  return s->s_cap >= kFuseMinKeys && s->T >= 64 && fused_shape(s, dt);
+}
+
 dsa::TopkParams topk_params(const dsa_shape* s, const float* scores, int64_t ld, int32_t* out) {
   return dsa::TopkParams{s->B, s->T, s->topk, s->s_cap, s->key_start, s->key_end, scores, ld, out};
 }
@@ -224,7 +242,12 @@ size_t dsa_workspace_bytes(const dsa_shape* s, dsa_op op) {
     case DSA_OP_INDEXER: return 0;
     case DSA_OP_TOPK: return topk_ws(s);
     case DSA_OP_SPARSE_MLA: return mla_ws(s, DSA_BF16);
-    case DSA_OP_GROUP: return scores_bytes(s) + align_up(std::max(topk_ws(s), mla_ws(s, DSA_BF16)));
+    case DSA_OP_GROUP: {
+      const size_t plain = scores_bytes(s) + align_up(std::max(topk_ws(s), mla_ws(s, DSA_BF16)));
+      const bool fuse = s->s_cap >= kFuseMinKeys && s->T >= 64 && fused_any(s);
+      return fuse ? std::max(plain, indexer_topk_ws(s, true)) : plain;
+    }
+    case DSA_OP_INDEXER_TOPK: return indexer_topk_ws(s, fused_any(s));
   }
   return 0;
 }
@@ -251,6 +274,25 @@ dsa_status dsa_topk_select(const dsa_shape* s, const float* scores, int64_t ld, 
     return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "top-k workspace %zu < %zu", ws_bytes, need);
   hipError_t e = dsa::launch_topk(topk_params(s, scores, ld, out), ws, ws_bytes, (hipStream_t)stream, nullptr);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "top-k launch");
+}
+
+dsa_status dsa_indexer_topk(const dsa_shape* s, dsa_dtype dt, const void* q, const float* qs, const void* k,
+                            const float* ksc, const float* w, int32_t* out, int32_t sample_stride, void* ws,
+                            size_t ws_bytes, void* stream) {
+  dsa_status st = check_indexer_shape(s, dt);
+  if (st == DSA_OK) st = check_topk_shape(s);
+  if (st == DSA_OK) st = check_indexer_ptrs(s, dt, q, qs, k, ksc, w);
+  if (st != DSA_OK) return st;
+  if (rows_of(s) > 0 && !out) return fail(DSA_ERR_INVALID_ARG, "topk_indices must be non-NULL");
+  if (!dsa::indexer_topk_stride_ok(sample_stride))
+    return fail(DSA_ERR_INVALID_ARG, "sample_stride %d: need 0 or 16 .. 1048576", sample_stride);
+  if (rows_of(s) == 0) return DSA_OK;
+  const size_t need = indexer_topk_ws(s, fused_shape(s, dt));
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "indexer top-k workspace %zu < %zu", ws_bytes, need);
+  hipError_t e = dsa::launch_indexer_topk(indexer_params(s, q, qs, k, ksc, w, nullptr, s->s_cap), (dsa::Dtype)dt,
+                                          s->topk, sample_stride, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
+  return e == hipSuccess ? DSA_OK : hip_fail(e, "indexer top-k launch");
 }
 
 dsa_status dsa_sparse_mla_attention(const dsa_shape* s, dsa_dtype dt, const void* q, const void* kv,
@@ -385,15 +427,25 @@ dsa_status dsa_group_forward(const dsa_shape* s, dsa_dtype mla_dtype, int32_t n_
     if (types[l] == DSA_FULL) {
       const dsa_index_io& I = *L.index;
       if ((e = rec(l, 0)) != hipSuccess) break;
-      e = dsa::launch_indexer(indexer_params(s, I.q, I.q_scale, I.k, I.k_scale, I.w, scores, s->s_cap),
-                              (dsa::Dtype)I.idx_dtype, strm, &launches);
-      if (e != hipSuccess) break;
-      if ((e = rec(l, 1)) != hipSuccess) break;
-      if ((e = rec(l, 2)) != hipSuccess) break;
-      last_full = l;  // from here on the indices buffer holds this call's data
-      e = dsa::launch_topk(topk_params(s, scores, s->s_cap, cache->indices), kws, kws_bytes, strm, &launches);
-      if (e != hipSuccess) break;
-      if ((e = rec(l, 3)) != hipSuccess) break;
+      const dsa::IndexerParams ip = indexer_params(s, I.q, I.q_scale, I.k, I.k_scale, I.w, scores, s->s_cap);
+      if (group_fuses(s, I.idx_dtype)) {
+        last_full = l;  // from here on the indices buffer holds this call's data
+        e = dsa::launch_indexer_topk(ip, (dsa::Dtype)I.idx_dtype, s->topk, 0, cache->indices, ws, ws_bytes, strm,
+                                     &launches);
+        if (e != hipSuccess) break;
+        if ((e = rec(l, 1)) != hipSuccess) break;
+        if ((e = rec(l, 2)) != hipSuccess) break;
+        if ((e = rec(l, 3)) != hipSuccess) break;
+      } else {
+        e = dsa::launch_indexer(ip, (dsa::Dtype)I.idx_dtype, strm, &launches);
+        if (e != hipSuccess) break;
+        if ((e = rec(l, 1)) != hipSuccess) break;
+        if ((e = rec(l, 2)) != hipSuccess) break;
+        last_full = l;  // from here on the indices buffer holds this call's data
+        e = dsa::launch_topk(topk_params(s, scores, s->s_cap, cache->indices), kws, kws_bytes, strm, &launches);
+        if (e != hipSuccess) break;
+        if ((e = rec(l, 3)) != hipSuccess) break;
+      }
     }
     if ((e = rec(l, 4)) != hipSuccess) break;
     e = dsa::launch_sparse_mla(mla_params(s, L.q, L.kv, cache->indices, sm_scale, L.out, L.lse),

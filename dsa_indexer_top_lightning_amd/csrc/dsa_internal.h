@@ -23,6 +23,22 @@ struct IndexerParams {
   const float* w;
   float* scores;
   int64_t ld;
+  // Rows with row_mask[row] == 0 are skipped (nothing written).  Nullable.
+  const int32_t* row_mask = nullptr;
+  // Launch hint: the mask leaves few rows live (the tile kernel then runs one block per key
+  // tile that walks the query tiles, instead of one block per tile).
+  int few_rows = 0;
+  // Sampling (kstride > 1): only keys s = kstride * i are scored, into scores[row * ld + i].
+  int64_t kstride = 1;
+  // Candidate mode (lkey != nullptr): no scores are written; every cell whose order key
+  // (order_key below) is >= lkey[row] is appended to its row's list: slot =
+  // atomicAdd(cand_cnt + row, 1), and if slot < cap, cand_pos[row * cap + slot] = key
+  // position, cand_val[row * cap + slot] = score.
+  const uint32_t* lkey = nullptr;
+  int32_t* cand_cnt = nullptr;
+  int32_t* cand_pos = nullptr;
+  float* cand_val = nullptr;
+  int32_t cap = 0;
 };
 
 struct TopkParams {
@@ -33,6 +49,7 @@ struct TopkParams {
   const float* scores;
   int64_t ld;
   int32_t* out;
+  const int32_t* row_mask = nullptr;  // rows with row_mask[row] == 0 are skipped (nullable)
 };
 
 struct MlaParams {
@@ -102,8 +119,19 @@ struct LatentAppendParams {
 
 // Each launcher assumes its arguments were validated by the host layer.
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches);
+// Whether the shape runs on a kernel with row masks, sampling and candidate mode (the fp8
+// tile kernel with one key head per query head, or the decode stream kernel).
+bool indexer_modes_supported(const IndexerParams& p, Dtype dt);
 size_t topk_workspace_bytes(int B, int T, int topk, int64_t s_cap);
 hipError_t launch_topk(const TopkParams& p, void* ws, size_t ws_bytes, hipStream_t st, int* n_launches);
+// Fused indexer -> top-k.  Workspace: [rows * s_cap fp32 scores][top-k workspace], then,
+// when `fused`, the sample, threshold and candidate buffers.  The scores region is only
+// written for rows that fall back (or by the unfused path of shapes that cannot fuse).
+bool indexer_topk_fused(const IndexerParams& p, Dtype dt, int topk);
+bool indexer_topk_stride_ok(int64_t stride);
+size_t indexer_topk_workspace_bytes(int B, int T, int topk, int64_t s_cap, bool fused);
+hipError_t launch_indexer_topk(const IndexerParams& p, Dtype dt, int topk, int64_t stride, int32_t* out, void* ws,
+                               size_t ws_bytes, hipStream_t st, int* n_launches);
 bool mla_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);
 size_t mla_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt);
 hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
@@ -130,6 +158,13 @@ inline hipError_t allow_dynamic_lds(const void* kernel, size_t bytes, std::atomi
   while (bytes > cur && !high.compare_exchange_weak(cur, bytes)) {
   }
   return hipSuccess;
+}
+
+// Scores -> uint32 keys that order like the floats (-0.0 folded onto +0.0).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Clamp a query's candidate range to [0, s_cap].

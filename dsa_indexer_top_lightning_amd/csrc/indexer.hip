@@ -692,7 +692,7 @@ struct G8Copy {
   unsigned char* smem;
   uint32_t smem_lds;
   int lane, c, b, t0, H, T;
-  int64_t s0, S;
+  int64_t s0, S, kst;                  // first key of the tile, key capacity, key stride (sampling)
   bool lead;                           // this workgroup requests the key rows into the L2
   const unsigned char* cbase[G8_CPW];  // source of copy i for head 0 (uniform)
   uint32_t coff[G8_CPW];               // per-lane byte offset from it
@@ -718,7 +718,7 @@ struct G8Copy {
       const int row = 8 * oct + (lane >> 3);
       const int chunk = (lane & 7) ^ tperm(row);
       // rows past T / S load a valid row; their results are never written
-      const int rr = isk ? (int)(min<int64_t>(s0 + row, S - 1) - s0) : min(t0 + row, T - 1) - t0;
+      const int rr = isk ? (int)(min<int64_t>(s0 + kst * row, S - 1) - s0) : min(t0 + row, T - 1) - t0;
       cbase[i] = isk ? kg + ((int64_t)b * S + s0) * row_bytes : qg + ((int64_t)b * T + t0) * row_bytes;
       coff[i] = (uint32_t)(rr * row_bytes + chunk * 16);
       cdst[i] = (uint32_t)((isk ? G8_QB : 0) + oct * 1024);
@@ -727,7 +727,7 @@ struct G8Copy {
     {
       const int r = min(t0 + 32 * c + (lane & 31), T - 1);  // w and q scale: separate tensors, full addresses
       wqsrc = (lane < 32 ? p.w : p.q_scale) + ((int64_t)b * T + r) * H;
-      const int k = (int)(min<int64_t>(s0 + 64 * c + lane, S - 1) - s0);
+      const int k = (int)(min<int64_t>(s0 + kst * (64 * c + lane), S - 1) - s0);
       kcbase = p.k_scale + ((int64_t)b * S + s0) * H;
       kcoff = (uint32_t)(k * H * 4);
     }
@@ -735,7 +735,7 @@ struct G8Copy {
 #pragma unroll
     for (int n = 0; n < G8_L2N; ++n) {
       const int u = 64 * n + lane;  // 0 .. 127: row 64c + u / 2, half u % 2
-      const int rr = (int)(min<int64_t>(s0 + 64 * c + (u >> 1), S - 1) - s0);
+      const int rr = (int)(min<int64_t>(s0 + kst * (64 * c + (u >> 1)), S - 1) - s0);
       l2off[n] = (uint32_t)(rr * row_bytes + 64 * (u & 1));
     }
     issued = mark_new = mark_old = 0;
@@ -878,65 +878,75 @@ struct G8Math {
   }
 };
 
-template <int>
-__global__ __attribute__((amdgpu_flat_work_group_size(G8_THREADS, G8_THREADS), amdgpu_waves_per_eu(3, 3)))
-void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ int32_t rks[G8_BM], rke[G8_BM];
-  __shared__ float wmax[G8_CW + G8_DW];
+// MODE: G8_SCORES (every key, scores stored), G8_SAMPLES (keys kstride * i, stored at column i),
+// G8_CANDIDATES (every key, cells reaching the row's threshold appended to its list)
+enum G8Mode : int { G8_SCORES = 0, G8_SAMPLES = 1, G8_CANDIDATES = 2 };
 
+struct G8Shared {
+  int32_t rks[G8_BM], rke[G8_BM];  // each row's key range (absolute; empty for masked rows)
+  int32_t clo[G8_BM], chi[G8_BM];  // candidate mode: the range as columns of the tile, in [0, 256]
+  uint32_t lkey[G8_BM];            // candidate mode: each row's threshold (see below)
+  float wmax[G8_CW + G8_DW];
+};
+
+// One tile: query tile qy (rows t0 = 128 qy ..), key tile kx, batch item b.  Every wave
+// returns from it (the copy waves once their loads have landed).
+template <int MODE>
+__device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* smem, G8Shared& sh, int b, int qy,
+                                        int kx, bool lead) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int b = blockIdx.y;
-  const int bid = blockIdx.x;
-  int qy, kx;
-  if (xcd_order) {
-    // Workgroups are dispatched to the 8 XCDs in turn (block i to XCD i % 8).  Each XCD owns
-    // nq / 8 query tiles and sweeps the key tiles in order, so its query tiles stay in its L2
-    // and the workgroups of an XCD that share a key tile read it at about the same time.
-    const int per = nq / 8, xcd = bid % 8, slot = bid / 8;
-    qy = xcd * per + slot % per;
-    kx = slot / per;
-  } else {
-    qy = bid % nq;
-    kx = bid / nq;
-  }
   const int t0 = qy * G8_BM;
-  const int64_t s0 = (int64_t)kx * G8_BN;
+  const int64_t kst = MODE == G8_SAMPLES ? p.kstride : 1;  // key stride
+  const int64_t s0 = (int64_t)kx * G8_BN * kst;  // first key of the tile; column i is key s0 + kst i
   const int T = p.T;
   const int64_t S = p.s_cap;
 
-  int live = 0;
+  int live = 0, inside = 1;
   if (tid < G8_BM) {
     const int t = t0 + tid;
     int64_t ks = 0, ke = 0;
-    if (t < T) clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, S, ks, ke);
-    rks[tid] = (int32_t)ks;
-    rke[tid] = (int32_t)ke;
-    live = (t < T) && (ks < s0 + G8_BN) && (ke > s0) && (ks < ke);
+    if (t < T && (!p.row_mask || p.row_mask[(int64_t)b * T + t]))
+      clamp_range(p.key_start, p.key_end, (int64_t)b * T + t, S, ks, ke);
+    sh.rks[tid] = (int32_t)ks;  // masked rows and rows past T get the empty range
+    sh.rke[tid] = (int32_t)ke;
+    live = (ks < s0 + G8_BN * kst) && (ke > s0) && (ks < ke);
+    if (MODE == G8_CANDIDATES) {
+      sh.clo[tid] = (int32_t)min<int64_t>(max<int64_t>(ks - s0, 0), G8_BN);
+      sh.chi[tid] = (int32_t)min<int64_t>(max<int64_t>(ke - s0, 0), G8_BN);
+      inside = ks <= s0 && ke >= s0 + G8_BN;
+      // The epilogue compares keys that do not fold -0.0 onto +0.0 (u ^ 0x80000000 or ~u); a
+      // threshold of +0.0's key is lowered by one, to -0.0's: the same cells pass as with folding.
+      const uint32_t lk = ks < ke ? p.lkey[(int64_t)b * T + t] : 0u;
+      sh.lkey[tid] = lk == 0x80000000u ? 0x7fffffffu : lk;
+    }
   }
   if (!__syncthreads_or(live)) return;
+  const bool all_in = MODE == G8_CANDIDATES && __syncthreads_and(inside);
 
   // 2^E bounds the tile's largest key scale (all heads) times 2^25
   int tile_e;
   {
     const float* ksrc = p.k_scale + ((int64_t)b * S + s0) * p.H;
-    const int nks = (int)min<int64_t>(G8_BN, S - s0) * p.H;
+    const int ncol = (int)min<int64_t>(G8_BN, (S - s0 + kst - 1) / kst);  // columns inside the prefix
     float m = 0.f;
-    for (int i = tid; i < nks; i += G8_THREADS) m = fmaxf(m, ksrc[i]);
+    if (MODE != G8_SAMPLES)
+      for (int i = tid; i < ncol * p.H; i += G8_THREADS) m = fmaxf(m, ksrc[i]);
+    else
+      for (int i = tid; i < ncol * p.H; i += G8_THREADS) m = fmaxf(m, ksrc[(i / p.H) * kst * p.H + i % p.H]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (lane == 0) wmax[wave] = m;
+    if (lane == 0) sh.wmax[wave] = m;
     __syncthreads();
-    m = wmax[0];
+    m = sh.wmax[0];
 #pragma unroll
-    for (int i = 1; i < G8_CW + G8_DW; ++i) m = fmaxf(m, wmax[i]);
+    for (int i = 1; i < G8_CW + G8_DW; ++i) m = fmaxf(m, sh.wmax[i]);
     int x = 0;
     (void)frexpf(m, &x);  // m < 2^x
     tile_e = 25 + x;
   }
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, so the role branches are too
   if (wv >= G8_CW) {
-    G8Copy cw{p, smem, 0u, lane, wv - G8_CW, b, t0, p.H, T, s0, S, xcd_order && qy % (nq / 8) == 0};
+    G8Copy cw{p, smem, 0u, lane, wv - G8_CW, b, t0, p.H, T, s0, S, kst, lead};
     cw.setup();
     cw.run();
     return;  // every load it issued has landed (the last head waits for all)
@@ -946,20 +956,134 @@ void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
   w.setup();
   w.run();
 
-  // candidate cells of the wave's block: row 64wm + 32i + 8(r/4) + 4lg + r%4, column 64wn + 32j + lr;
-  // the sums carry 2^-E
+  // candidate cells of the wave's block: row 64wm + 32i + 8(r/4) + 4lg + r%4, column 64wn + 32j + lr
+  // (key s0 + kst * column); the sums carry 2^-E
   const float up = ldexpf(1.f, tile_e);
+  if constexpr (MODE != G8_CANDIDATES) {
+    float* dst = p.scores + ((int64_t)b * T + t0) * p.ld + (int64_t)kx * G8_BN;  // row t0, column 0 of the tile
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t s = s0 + 64 * w.wn + 32 * j + w.lr;
+    for (int j = 0; j < 2; ++j) {
+      const int c = 64 * w.wn + 32 * j + w.lr;  // column of the tile: key s0 + kst * c
+      const int64_t s = s0 + kst * c;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
+          if (s >= sh.rks[m] && s < sh.rke[m]) dst[(int64_t)m * p.ld + c] = w.tot[i][j][r] * up;
+        }
+    }
+    return;
+  } else {
+    // Candidate mode.  Pass 1 marks the lane's candidate cells (bit 16 j + r of tb[i]) and
+    // counts them per row of the wave's 64-row block (lane l ends with row l's count); one
+    // atomic per lane reserves the slots of its row; pass 2 writes the cells to them.
+    const int own = 64 * w.wm;          // first row of the wave's block in the tile
+    uint32_t tb[2] = {0u, 0u}, mycnt = 0u;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
-        const int t = t0 + m;
-        if (t < T && s >= rks[m] && s < rke[m]) p.scores[((int64_t)b * T + t) * p.ld + s] = w.tot[i][j][r] * up;
+        const int m = own + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
+        bool take[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = 64 * w.wn + 32 * j + w.lr;
+          const uint32_t u = __float_as_uint(w.tot[i][j][r] * up);
+          const uint32_t key = u ^ (uint32_t)(((int32_t)u >> 31) | (int32_t)0x80000000);
+          take[j] = key >= sh.lkey[m] && (all_in || (c >= sh.clo[m] && c < sh.chi[m]));
+        }
+        tb[i] |= ((uint32_t)take[0] << r) | ((uint32_t)take[1] << (16 + r));
+        const uint64_t m0 = __ballot(take[0]), m1 = __ballot(take[1]);
+        const int l0 = 32 * i + 8 * (r >> 2) + (r & 3);  // the half-waves' rows: l0 and l0 + 4
+        const uint32_t clo = (uint32_t)(__popcll(m0 & 0xffffffffull) + __popcll(m1 & 0xffffffffull));
+        const uint32_t chi = (uint32_t)(__popcll(m0 >> 32) + __popcll(m1 >> 32));
+        mycnt = lane == l0 ? clo : (lane == l0 + 4 ? chi : mycnt);
       }
+    uint32_t base = 0u;
+    if (mycnt) base = (uint32_t)atomicAdd(p.cand_cnt + (int64_t)b * T + t0 + own + lane, (int32_t)mycnt);
+    const uint64_t half = w.lg ? ~0xffffffffull : 0xffffffffull;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool k0 = (tb[i] >> r) & 1u, k1 = (tb[i] >> (16 + r)) & 1u;
+        const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
+        if ((m0 | m1) == 0) continue;
+        const int l0 = 32 * i + 8 * (r >> 2) + (r & 3);
+        const uint32_t rb = w.lg ? __builtin_amdgcn_readlane(base, l0 + 4) : __builtin_amdgcn_readlane(base, l0);
+        const uint32_t c0 = (uint32_t)__popcll(m0 & half);
+        const int64_t row = (int64_t)b * T + t0 + own + l0 + 4 * w.lg;
+        int32_t* pos = p.cand_pos + row * p.cap;
+        float* val = p.cand_val + row * p.cap;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          if (!(j ? k1 : k0)) continue;
+          const uint64_t mj = (j ? m1 : m0) & half;
+          const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mj >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mj, 0u));
+          const uint32_t slot = rb + (j ? c0 : 0u) + below;
+          if (slot < (uint32_t)p.cap) {
+            pos[slot] = (int32_t)(s0 + 64 * w.wn + 32 * j + w.lr);
+            val[slot] = w.tot[i][j][r] * up;
+          }
+        }
+      }
+  }
+}
+
+constexpr int G8_QWORDS = 64;  // query-tile bits of the walking variant (up to 2048 query tiles)
+
+// grid (tiles, B).  QLOOP = false: block x is one tile (query-tile order as below).  QLOOP =
+// true: block x is key tile x and walks every query tile, skipping those without live rows
+// (for a row mask that leaves few rows: a tile-per-block grid would spend its time starting
+// and ending blocks).
+template <int MODE, bool QLOOP>
+__global__ __attribute__((amdgpu_flat_work_group_size(G8_THREADS, G8_THREADS), amdgpu_waves_per_eu(3, 3)))
+void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ G8Shared sh;
+  const int b = blockIdx.y;
+  const int bid = blockIdx.x;
+  if constexpr (QLOOP) {
+    // the query tiles that hold a row of the mask (one bit each; nq <= 32 G8_QWORDS)
+    __shared__ uint32_t qbits[G8_QWORDS];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < G8_QWORDS; i += G8_THREADS) qbits[i] = 0u;
+    __syncthreads();
+    const int32_t* mrow = p.row_mask + (int64_t)b * p.T;
+    for (int r0 = 0; r0 < p.T; r0 += 8 * G8_THREADS) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = r0 + u * G8_THREADS + tid;
+        v[u] = t < p.T ? mrow[t] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = (r0 + u * G8_THREADS + tid) / G8_BM;
+        if (v[u]) atomicOr(&qbits[q >> 5], 1u << (q & 31));
+      }
+    }
+    __syncthreads();
+    for (int qy = 0; qy < nq; ++qy) {
+      if (!((qbits[qy >> 5] >> (qy & 31)) & 1u)) continue;
+      g8_tile<MODE>(p, smem, sh, b, qy, bid, false);
+      __syncthreads();  // the next tile reuses every LDS buffer
+    }
+  } else {
+    int qy, kx;
+    if (xcd_order) {
+      // Workgroups are dispatched to the 8 XCDs in turn (block i to XCD i % 8).  Each XCD owns
+      // nq / 8 query tiles and sweeps the key tiles in order, so its query tiles stay in its L2
+      // and the workgroups of an XCD that share a key tile read it at about the same time.
+      const int per = nq / 8, xcd = bid % 8, slot = bid / 8;
+      qy = xcd * per + slot % per;
+      kx = slot / per;
+    } else {
+      qy = bid % nq;
+      kx = bid / nq;
+    }
+    g8_tile<MODE>(p, smem, sh, b, qy, kx, xcd_order && qy % (nq / 8) == 0);
   }
 }
 #pragma clang diagnostic pop
@@ -972,7 +1096,9 @@ void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
 // elements (l % LPH) * D/LPH .. +D/LPH of it (LPH = 64 / H lanes per head), the
 // query slice stays in registers, per-head dots are completed by lane shuffles,
 // then ReLU * weight and a shuffle reduction over the heads give the score.
-// grid: x = block of 64 keys, y = query row.  256 threads: wave w takes keys w, w+4, ...
+// grid: x = block of 64 keys (or samples), y = query row.  256 threads: wave w takes keys
+// w, w+4, ...  With sampling, column c of the row is key kstride * c; in candidate mode
+// lane 0 appends each key whose order key reaches the row's threshold.
 template <int DT, int LPH>
 __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
   constexpr int H = 64 / LPH;
@@ -985,10 +1111,13 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.y;
+  if (p.row_mask && !p.row_mask[row]) return;
   int64_t ks, ke;
   clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
-  const int64_t sblk = (int64_t)blockIdx.x * KPB;
-  if (sblk >= ke || sblk + KPB <= ks) return;
+  const int64_t kst = p.kstride;
+  const int64_t sblk = (int64_t)blockIdx.x * KPB;  // first column of the block
+  if (sblk * kst >= ke || (sblk + KPB - 1) * kst < ks) return;
+  const uint32_t lk = p.lkey ? p.lkey[row] : 0u;
   const int64_t b = row / p.T;
   const int Hk = p.Hk;
   const int h = lane / LPH, part = lane % LPH;
@@ -1018,7 +1147,8 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
   const int64_t krow = (int64_t)Hk * HD * ESZ;
 
   for (int j = wave; j < KPB; j += 4) {
-    const int64_t s = sblk + j;
+    const int64_t col = sblk + j;
+    const int64_t s = col * kst;
     if (s < ks || s >= ke) continue;  // the whole wave takes the same branch
     const unsigned char* src = kg + (b * p.s_cap + s) * krow + (int64_t)g * HD * ESZ + part * BYTES;
     i32x4 raw[LOADS];
@@ -1054,7 +1184,17 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
     float v = (part == 0) ? wh * fmaxf(dot, 0.f) : 0.f;
 #pragma unroll
     for (int off = LPH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) p.scores[row * p.ld + s] = v;
+    if (lane == 0) {
+      if (!p.lkey) {
+        p.scores[row * p.ld + col] = v;
+      } else if (order_key(v) >= lk) {
+        const int32_t slot = atomicAdd(p.cand_cnt + row, 1);
+        if (slot < p.cap) {
+          p.cand_pos[row * p.cap + slot] = (int32_t)s;
+          p.cand_val[row * p.cap + slot] = v;
+        }
+      }
+    }
   }
 }
 
@@ -1067,22 +1207,56 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
 
 }  // namespace
 
+namespace {
+// the fp8 tile kernel with one key head per query head (prefill)
+bool g8_path(const IndexerParams& p, Dtype dt) {
+  if (!(dt == FP8 && p.D == HD && p.Hk == p.H && p.T >= 64 && p.B <= 65535)) return false;
+  const int64_t nq = (p.T + G8_BM - 1) / G8_BM;
+  const int64_t nk = ((p.s_cap + p.kstride - 1) / p.kstride + G8_BN - 1) / G8_BN;
+  return nq * nk <= INT32_MAX;
+}
+// the decode stream kernel
+bool stream_path(const IndexerParams& p, Dtype dt) {
+  return (dt == BF16 || dt == FP8) && p.D == HD && p.T <= 4 && (int64_t)p.B * p.T <= 65535 &&
+         (p.H == 16 || p.H == 32 || p.H == 64) && (p.s_cap + p.kstride - 1) / p.kstride / 64 < INT32_MAX;
+}
+}  // namespace
+
+bool indexer_modes_supported(const IndexerParams& p, Dtype dt) { return g8_path(p, dt) || stream_path(p, dt); }
+
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches) {
   if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;
   const bool mfma = (dt == BF16 || dt == FP8) && p.D == HD;
-  if (dt == FP8 && p.D == HD && p.Hk == p.H && p.T >= 64 && p.B <= 65535) {
+  const bool modes = p.row_mask || p.kstride != 1 || p.lkey;
+  if (p.kstride < 1 || (p.lkey && p.kstride != 1) || (modes && !indexer_modes_supported(p, dt)))
+    return hipErrorInvalidValue;
+  const int64_t ncols = (p.s_cap + p.kstride - 1) / p.kstride;  // keys (or samples) per row
+  if (g8_path(p, dt)) {
     const int nq = (p.T + G8_BM - 1) / G8_BM;
-    const int64_t nk = (p.s_cap + G8_BN - 1) / G8_BN;
-    if ((int64_t)nq * nk <= INT32_MAX) {
-      hipError_t e;
-      if ((e = DSA_ALLOW_LDS(indexer_fp8_groups<0>, G8_LDS)) != hipSuccess) return e;
-      // query tiles per XCD when they split evenly and the grid is not a causal square
-      const int xcd = (nq % 8 == 0) && (p.T != p.s_cap);
-      hipLaunchKernelGGL(indexer_fp8_groups<0>, dim3((unsigned)(nq * nk), (unsigned)p.B), dim3(G8_THREADS),
-                         G8_LDS, st, p, nq, (int)nk, xcd);
-      if (n_launches) ++*n_launches;
-      return hipGetLastError();
+    const int64_t nk = (ncols + G8_BN - 1) / G8_BN;
+    hipError_t e;
+    // query tiles per XCD when they split evenly and the grid is not a causal square
+    const int xcd = (nq % 8 == 0) && (p.T != p.s_cap);
+    const dim3 grid((unsigned)(nq * nk), (unsigned)p.B);
+    if (p.lkey) {
+      if ((e = DSA_ALLOW_LDS((indexer_fp8_groups<G8_CANDIDATES, false>), G8_LDS)) != hipSuccess) return e;
+      hipLaunchKernelGGL((indexer_fp8_groups<G8_CANDIDATES, false>), grid, dim3(G8_THREADS), G8_LDS, st, p, nq,
+                         (int)nk, xcd);
+    } else if (p.kstride != 1) {
+      if ((e = DSA_ALLOW_LDS((indexer_fp8_groups<G8_SAMPLES, false>), G8_LDS)) != hipSuccess) return e;
+      hipLaunchKernelGGL((indexer_fp8_groups<G8_SAMPLES, false>), grid, dim3(G8_THREADS), G8_LDS, st, p, nq,
+                         (int)nk, xcd);
+    } else if (p.few_rows && p.row_mask && nq <= 32 * G8_QWORDS) {
+      if ((e = DSA_ALLOW_LDS((indexer_fp8_groups<G8_SCORES, true>), G8_LDS)) != hipSuccess) return e;
+      hipLaunchKernelGGL((indexer_fp8_groups<G8_SCORES, true>), dim3((unsigned)nk, (unsigned)p.B), dim3(G8_THREADS),
+                         G8_LDS, st, p, nq, (int)nk, 0);
+    } else {
+      if ((e = DSA_ALLOW_LDS((indexer_fp8_groups<G8_SCORES, false>), G8_LDS)) != hipSuccess) return e;
+      hipLaunchKernelGGL((indexer_fp8_groups<G8_SCORES, false>), grid, dim3(G8_THREADS), G8_LDS, st, p, nq,
+                         (int)nk, xcd);
     }
+    if (n_launches) ++*n_launches;
+    return hipGetLastError();
   }
   if (mfma && p.T >= 32) {
     const size_t lds = (size_t)(dt == BF16 ? TileCfg<BF16>::LDS : TileCfg<FP8>::LDS);
@@ -1095,9 +1269,9 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
       if ((e = DSA_ALLOW_LDS(indexer_tile<FP8>, lds)) != hipSuccess) return e;
       hipLaunchKernelGGL(indexer_tile<FP8>, grid, dim3(TILE_THREADS), lds, st, p);
     }
-  } else if (mfma && p.T <= 4 && (int64_t)p.B * p.T <= 65535 && (p.H == 16 || p.H == 32 || p.H == 64)) {
+  } else if (stream_path(p, dt)) {
     // decode: stream the keys once per query row
-    dim3 grid((unsigned)((p.s_cap + 63) / 64), (unsigned)((int64_t)p.B * p.T));
+    dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)((int64_t)p.B * p.T));
     if (dt == BF16) {
       if (p.H == 16) hipLaunchKernelGGL((indexer_stream<BF16, 4>), grid, dim3(256), 0, st, p);
       else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<BF16, 2>), grid, dim3(256), 0, st, p);

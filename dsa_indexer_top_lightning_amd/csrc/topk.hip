@@ -32,6 +32,7 @@
 // chunk's number of keys > tau and == tau, and the emitting launch writes each
 // chunk's kept positions after those of the chunks before it.
 #include "dsa_internal.h"
+#include "select.h"
 
 namespace dsa {
 namespace {
@@ -39,51 +40,6 @@ namespace {
 constexpr int TK_THREADS = 512;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int64_t TK_CACHE_KEYS = 32768;  // 128 KiB of LDS
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint32_t lane_prefix(uint64_t mask, int lane) {
-  return (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-}
-
-// Wave 0: in the 2048-bin histogram `hist` (digits of the candidates that match the
-// prefix so far), find the digit holding the rem-th largest candidate and that
-// candidate's rank among the keys with this digit (written to *digit, *rank).  The total
-// count must be >= rem.  Callers synchronise before and after.
-__device__ __forceinline__ void hist_find(const uint32_t* hist, uint32_t rem, uint32_t* digit, uint32_t* rank) {
-  const int lane = threadIdx.x & 63;
-  // lane L owns digits [32L, 32L+32) and sums them starting at bin L % 32 of its range, so
-  // that the 64 lanes of each read hit different LDS banks; then suffix sums over lanes
-  uint32_t c = 0;
-  for (int d = 0; d < 32; ++d) c += hist[32 * lane + ((d + lane) & 31)];
-  uint32_t x = c;
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t v = __shfl_down(x, off, 64);
-    if (lane + off < 64) x += v;
-  }
-  // x = number of candidates with digit >= 32*lane; non-increasing in lane
-  const uint64_t ge = __ballot(x >= rem);
-  const int L = __popcll(ge) - 1;  // last lane whose suffix reaches rem (>= 0: total >= rem)
-  const uint32_t above = __shfl(x - c, L, 64);  // candidates with a digit above lane L's range
-  // inside lane L's range: lane i < 32 takes digit 32L + i; s = candidates with a digit in
-  // [32L + i, 32L + 32); the digit is the highest i with above + s >= rem
-  const uint32_t h = lane < 32 ? hist[32 * L + lane] : 0u;
-  uint32_t sfx = h;
-  for (int off = 1; off < 32; off <<= 1) {
-    const uint32_t v = __shfl_down(sfx, off, 64);
-    if (lane + off < 32) sfx += v;
-  }
-  const uint64_t hit = __ballot(lane < 32 && above + sfx >= rem);
-  const int i = hit ? 63 - __clzll(hit) : 0;
-  if (lane == i) {
-    *digit = (uint32_t)(32 * L + i);
-    *rank = rem - (above + sfx - h);
-  }
-}
 
 struct SelectLds {
   uint32_t* hist;                  // [2048]
@@ -162,6 +118,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
 
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
+  if (p.row_mask && !p.row_mask[row]) return;
   int64_t ks, ke;
   clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
   const int64_t n = ke - ks;
@@ -247,23 +204,6 @@ __device__ __forceinline__ void for_each_key(const float* src, int64_t n, F&& f)
   if (t < n) f(t, order_key(src[t]));
 }
 
-// exclusive prefix sum of v over the workgroup (wsum: LG_WAVES words of LDS)
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  uint32_t before = x - v;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  __syncthreads();
-  return before;
-}
-
 // the == tau positions of bitmap word x that are kept, given e_before of them earlier in the row
 __device__ __forceinline__ uint32_t take_equal(uint32_t x, uint32_t e_before, uint32_t rem) {
   if (e_before >= rem) return 0u;
@@ -291,6 +231,7 @@ __global__ __launch_bounds__(LG_THREADS) void topk_long(TopkParams p, int map_wo
 
   const int tid = threadIdx.x, wave = tid >> 6;
   const int64_t row = blockIdx.x;
+  if (p.row_mask && !p.row_mask[row]) return;
   int64_t ks, ke;
   clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
   const int64_t n = ke - ks;
@@ -427,7 +368,7 @@ constexpr int SP_THREADS = 256;
 constexpr int SP_PER = 8;                         // keys per thread
 constexpr int SP_CHUNK = SP_THREADS * SP_PER;     // keys per workgroup
 constexpr int SP_BINS = 2048;
-constexpr int64_t SP_MIN_KEYS = 2 * SP_CHUNK;     // shorter rows stay on one workgroup
+constexpr int64_t SP_MIN_KEYS = 8192;             // shorter rows stay on one workgroup (one launch)
 constexpr int64_t SP_MAX_ROWS = 512;              // more rows fill the chip by themselves
 
 __host__ __device__ constexpr int sp_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
@@ -497,7 +438,7 @@ __device__ void sp_prefix(const uint32_t* gh, int passes, uint32_t K, uint32_t& 
 
 struct SpRow {
   int64_t ks, ke, lo, hi;
-  bool skip;
+  bool masked, skip;
 };
 
 __device__ __forceinline__ SpRow sp_row(const TopkParams& p) {
@@ -505,7 +446,8 @@ __device__ __forceinline__ SpRow sp_row(const TopkParams& p) {
   clamp_range(p.key_start, p.key_end, blockIdx.y, p.s_cap, r.ks, r.ke);
   r.lo = r.ks + (int64_t)blockIdx.x * SP_CHUNK;
   r.hi = min(r.ke, r.lo + SP_CHUNK);
-  r.skip = (r.ke - r.ks <= p.topk) || r.lo >= r.ke;
+  r.masked = p.row_mask && !p.row_mask[blockIdx.y];
+  r.skip = r.masked || (r.ke - r.ks <= p.topk) || r.lo >= r.ke;
   return r;
 }
 
@@ -589,6 +531,7 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_emit(TopkParams p, Spli
   const int K = p.topk;
   int32_t* out = p.out + row * (int64_t)K;
   SpRow r = sp_row(p);
+  if (r.masked) return;
   if (r.ke - r.ks <= K) {
     if (blockIdx.x == 0)
       for (int i = tid; i < K; i += SP_THREADS) out[i] = (i < r.ke - r.ks) ? (int32_t)(r.ks + i) : -1;
@@ -609,7 +552,7 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_emit(TopkParams p, Spli
   const uint32_t my_gt = c[2 * blockIdx.x], my_eq = c[2 * blockIdx.x + 1];
   if (my_gt == 0 && (my_eq == 0 || eqb >= rem)) return;  // nothing kept here (uniform)
 
-  // stage the chunk's keys; thread t then walks positions lo + 32t .. lo + 32t + 31
+  // stage the chunk's keys; thread t then walks positions lo + SP_PER t .. lo + SP_PER (t + 1) - 1
   const float* src = p.scores + row * p.ld;
   const int len = (int)(r.hi - r.lo);
   for (int i = tid; i < len; i += SP_THREADS) keys[i + i / SP_PER] = order_key(src[r.lo + i]);

@@ -302,18 +302,20 @@ def _blocks(n):
     return [(r, min(n, r + BLOCK_ROWS)) for r in range(0, n, BLOCK_ROWS)]
 
 
-def build_layer_inputs(w: Workload, layer: int, with_index: bool):
+def build_layer_inputs(w: Workload, layer: int, with_index: bool, with_mla: bool = True):
     """Stored (host) inputs of one layer for all batch items.
 
-    Returns a dict with 'mla_q' [B,T,Hm,row], 'kv' [B,S,row] and, for layers
-    that carry an indexer, 'idx_q' [B,T,H,D], 'idx_k' [B,S,Hk,D], 'w' [B,T,H]
-    and fp8 scales 'idx_q_scale' [B,T,H], 'idx_k_scale' [B,S,Hk].
-    Storage arrays: float32, uint16 (bf16 bits) or uint8 (e4m3fn codes).
+    Returns a dict with 'mla_q' [B,T,Hm,row], 'kv' [B,S,row] (unless with_mla is
+    False) and, for layers that carry an indexer, 'idx_q' [B,T,H,D], 'idx_k'
+    [B,S,Hk,D], 'w' [B,T,H] and fp8 scales 'idx_q_scale' [B,T,H], 'idx_k_scale'
+    [B,S,Hk].  Storage arrays: float32, uint16 (bf16 bits) or uint8 (e4m3fn codes).
     """
     mdt = np.float32 if w.mla_dtype == "f32" else np.uint16
-    out = {"mla_q": np.empty((w.B, w.T, w.Hm, w.row), mdt),
-           "kv": np.empty((w.B, w.S, w.row), mdt)}
+    out = {}
     jobs = []
+    if with_mla:
+        out["mla_q"] = np.empty((w.B, w.T, w.Hm, w.row), mdt)
+        out["kv"] = np.empty((w.B, w.S, w.row), mdt)
 
     def fill_mq(b, t0, t1):
         out["mla_q"][b, t0:t1] = store(mla_q_rows(w, layer, b, t0, t1), w.mla_dtype)[0]
@@ -321,7 +323,7 @@ def build_layer_inputs(w: Workload, layer: int, with_index: bool):
     def fill_kv(b, s0, s1):
         out["kv"][b, s0:s1] = store(mla_kv_rows(w, layer, b, s0, s1), w.mla_dtype)[0]
 
-    for b in range(w.B):
+    for b in range(w.B if with_mla else 0):
         jobs += [(fill_mq, b, r0, r1) for r0, r1 in _blocks(w.T)]
         jobs += [(fill_kv, b, r0, r1) for r0, r1 in _blocks(w.S)]
     if with_index:

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
   DSA_OK = 0,
@@ -50,7 +50,13 @@ typedef enum {
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 /* OCP e4m3fn */ } dsa_dtype;
 typedef enum { DSA_FULL = 0, DSA_SHARED = 1 } dsa_layer_type;
-typedef enum { DSA_OP_INDEXER = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA = 2, DSA_OP_GROUP = 3 } dsa_op;
+typedef enum {
+  DSA_OP_INDEXER = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA = 2,
+  DSA_OP_GROUP = 3,
+  DSA_OP_INDEXER_TOPK = 4
+} dsa_op;
 
 /* Problem shape (host struct).  Fields a call does not use are ignored. */
 typedef struct {
@@ -104,6 +110,40 @@ dsa_status dsa_indexer_scores(const dsa_shape* shape, dsa_dtype idx_dtype,
 dsa_status dsa_topk_select(const dsa_shape* shape, const float* scores, int64_t ld_scores,
                            int32_t* topk_indices, void* workspace, size_t ws_bytes,
                            void* stream);
+
+/*
+ * Lightning indexer and top-k in one call (section 1 of the IndexShare page: the
+ * indexer scores the prefix and only the top-k positions go on; the DeepSeek-V3.2
+ * material names this scan and selection as the long-context cost).  The result is
+ * bit-identical to dsa_indexer_scores followed by dsa_topk_select on the same inputs;
+ * the arguments are those two calls' (without scores), and topk_indices is written in
+ * the same way.
+ * Where the shape runs on a kernel with sampling and candidate modes (fp8 with
+ * Hk == H, D == 128 and T >= 64; or decode rows, T <= 4, D == 128, H in {16,32,64},
+ * bf16 or fp8) and topk <= 4096, the fp32 score matrix is not written:
+ *   1. every sample_stride-th key of each row is scored;
+ *   2. each row's threshold is the r-th largest of its samples, r = ceil(k/R + y) with
+ *      y^2 = 36 (k/R + y) (R = sample_stride, k = topk): about R r keys reach it, six
+ *      standard deviations of that count above k;
+ *   3. every key is scored again and those at or above the threshold are kept, with
+ *      their positions, in a list of up to 12288 per row;
+ *   4. a row whose list holds c keys with topk <= c <= 12288 holds every key at or above
+ *      its topk-th largest score, and selects from the list (same order and ties);
+ *   5. any other row is scored in full into the workspace and selected as by
+ *      dsa_topk_select.
+ * Other shapes run the two calls back to back through the workspace.
+ *   sample_stride  0 for the default (64), else 16 .. 1048576 (DSA_ERR_INVALID_ARG
+ *                  otherwise); it changes the time taken, never the result
+ *   workspace      ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_INDEXER_TOPK).  Its
+ *                  first B*T*s_cap*4 bytes are the [B*T, s_cap] fp32 score buffer of
+ *                  step 5: the candidate cells of the rows that fell back are written
+ *                  there and nothing else is (so a caller can tell which rows did).
+ */
+dsa_status dsa_indexer_topk(const dsa_shape* shape, dsa_dtype idx_dtype,
+                            const void* q, const float* q_scale,
+                            const void* k, const float* k_scale,
+                            const float* w, int32_t* topk_indices, int32_t sample_stride,
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Sparse MLA attention over the selected latent rows (section 1 of the IndexShare
@@ -181,7 +221,9 @@ typedef struct {
  * pattern figure; the list comes from indexer_types as the page's config
  * evidence and implementation checklist ask, not from a fixed layer modulo).
  * For l in 0..n_layers-1:
- *   FULL:   indexer scores -> workspace, top-k -> cache->indices.
+ *   FULL:   indexer scores -> workspace, top-k -> cache->indices; with s_cap >= 65536
+ *           and T >= 64, on shapes that dsa_indexer_topk runs without the score matrix,
+ *           as that call does (same indices).
  *   SHARED: the cache's indices are used unchanged (no device work).
  *   both:   sparse MLA with layer l's own q and kv and the current indices.
  * The handle's host fields change only when the call returns: after a successful
@@ -201,7 +243,9 @@ typedef struct {
  *                        guard).
  *   events: NULL, or host array of 6*n_layers hipEvent_t; when given, for layer l
  *           events[6l+0/1] bracket the indexer, [6l+2/3] the top-k and [6l+4/5]
- *           the attention kernels (entries of shared layers' indexer/top-k unused).
+ *           the attention kernels (entries of shared layers' indexer/top-k unused;
+ *           on a layer that runs as dsa_indexer_topk, [6l+0/1] bracket the whole
+ *           indexer -> top-k and [6l+2/3] are recorded together after it).
  *   stats:  NULL, or filled with every field: the analytic counters (the same numbers as
  *           dsa_group_stats_compute, computed before anything is enqueued, so they are
  *           set even when an enqueue fails) and n_launches.  When the shape gives device

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol(L):
     assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
-    assert L.dsa_abi_version() == 2
+    assert L.dsa_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -152,6 +152,44 @@ def test_topk_workspace_only_for_few_long_rows(L):
     # many rows, or short rows, take one workgroup per row and no workspace
     assert L.dsa_workspace_bytes(C.byref(_shape(B=1, T=4096, s_cap=4096, topk=2048)), b.OP_TOPK) == 0
     assert L.dsa_workspace_bytes(C.byref(_shape(B=1, T=512, s_cap=1 << 17, topk=2048)), b.OP_TOPK) == 0
+
+
+def _itk(L, shape, dt=b.BF16, out=FAKE, stride=0, ws=FAKE, ws_bytes=1 << 40, qs=None, ks=None):
+    return L.dsa_indexer_topk(C.byref(shape), dt, FAKE, qs, FAKE, ks, FAKE, out, stride, ws, ws_bytes, None)
+
+
+def test_indexer_topk_errors(L):
+    assert _itk(L, _shape(topk=0)) == 1
+    assert _itk(L, _shape(D=24)) == 2
+    assert _itk(L, _shape(), dt=b.FP8_E4M3) == 1            # fp8 without scales
+    assert _itk(L, _shape(), out=None) == 1
+    for bad in (-1, 1, 15, (1 << 20) + 1):
+        assert _itk(L, _shape(), stride=bad) == 1
+        assert "sample_stride" in b.last_error()
+    s = _shape()
+    need = L.dsa_workspace_bytes(C.byref(s), b.OP_INDEXER_TOPK)
+    assert need > 0
+    assert _itk(L, s, ws_bytes=need - 1) == 5
+    assert _itk(L, s, ws=None, ws_bytes=need) == 5
+    assert L.dsa_indexer_topk(C.byref(_shape(B=0)), b.BF16, None, None, None, None, None, None, 0, None, 0, None) == 0
+
+
+def test_indexer_topk_workspace_layout(L):
+    # a 4096-query chunk over a 131072-key prefix (fp8 and one key head per query head can fuse):
+    # score buffer for fall-back rows, no top-k histograms (many rows), samples sized for
+    # stride 16, four per-row words, 12288 candidate positions and values per row
+    rows, S = 4096, 131072
+    s = _shape(B=1, T=rows, s_cap=S, H=32, D=128, Hk=32, topk=2048, Hm=64, Dc=512, Dr=64)
+    want = rows * S * 4 + rows * (S // 16) * 4 + 4 * rows * 4 + 2 * rows * 12288 * 4
+    assert L.dsa_workspace_bytes(C.byref(s), b.OP_INDEXER_TOPK) == want
+    # a group over rows this long runs the fused call in the same workspace
+    assert L.dsa_workspace_bytes(C.byref(s), b.OP_GROUP) >= want
+    # D = 64 has no sampling kernel: the unfused pair (scores + top-k workspace) only
+    s64 = _shape(B=1, T=rows, s_cap=S, H=32, D=64, Hk=32, topk=2048)
+    assert L.dsa_workspace_bytes(C.byref(s64), b.OP_INDEXER_TOPK) == rows * S * 4
+    # shorter prefixes do not fuse inside a group: its workspace is the unfused one
+    sh = _shape(B=1, T=4096, s_cap=4096, H=32, D=128, Hk=32, topk=2048, Hm=64, Dc=512, Dr=64)
+    assert L.dsa_workspace_bytes(C.byref(sh), b.OP_GROUP) < L.dsa_workspace_bytes(C.byref(sh), b.OP_INDEXER_TOPK)
 
 
 def test_workspace_sizes(L):
