@@ -249,9 +249,13 @@ def run_forward(w, dev, steps, warmup, graph, torch, B):
     attn_flops, attn_bytes = stats.attn_flops / n, stats.attn_bytes / n
     prefill = w.T > 1
     idx_peak = PEAK_FP8_TFLOPS if w.idx_dtype == "fp8" else PEAK_BF16_TFLOPS
+    fused = stats.n_fused > 0   # full layers run as the fused indexer -> top-k: one span, no score matrix
+    if fused:
+        t_topk = None
     kernels = {
         "indexer": {"ms": t_idx, "tflops": idx_flops / (t_idx * 1e-3) / 1e12 if t_idx else None,
-                    "gbs": idx_bytes / (t_idx * 1e-3) / 1e9 if t_idx else None},
+                    "gbs": idx_bytes / (t_idx * 1e-3) / 1e9 if t_idx else None,
+                    "includes_topk": fused},
         "topk": {"ms": t_topk, "gbs": topk_bytes / (t_topk * 1e-3) / 1e9 if t_topk else None},
         "sparse_mla": {"ms": t_attn, "tflops": attn_flops / (t_attn * 1e-3) / 1e12,
                        # every selected row's bytes per query: mostly served by the caches on a prefill
@@ -263,7 +267,8 @@ def run_forward(w, dev, steps, warmup, graph, torch, B):
     share = {"indexer": (t_idx or 0.0) * len(full), "topk": (t_topk or 0.0) * len(full), "sparse_mla": t_attn * n}
     dom = max(share, key=share.get)
     if dom == "indexer" and prefill:
-        kname = "indexer_tile<FP8>" if w.idx_dtype == "fp8" else "indexer_tile<BF16>"
+        kname = ("indexer_fp8_groups+fused_select" if fused else "indexer_fp8_groups") if w.idx_dtype == "fp8" \
+            else "indexer_tile<BF16>"
         roof = {"bound": "mfma", "achieved": kernels["indexer"]["tflops"], "peak": idx_peak, "unit": "TFLOP/s",
                 "kernel": kname, "algorithmic_per_launch": idx_flops, "launch_ms": t_idx}
         if w.idx_dtype == "fp8":

@@ -47,7 +47,7 @@ class LayerIO(C.Structure):
 
 
 class GroupStats(C.Structure):
-    _fields_ = [("n_full", C.c_int32), ("n_shared", C.c_int32), ("n_launches", C.c_int32),
+    _fields_ = [("n_full", C.c_int32), ("n_shared", C.c_int32), ("n_launches", C.c_int32), ("n_fused", C.c_int32),
                 ("indexer_flops", C.c_double), ("indexer_bytes", C.c_double), ("topk_bytes", C.c_double),
                 ("attn_flops", C.c_double), ("attn_bytes", C.c_double)]
 

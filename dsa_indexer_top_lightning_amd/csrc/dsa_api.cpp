@@ -174,6 +174,7 @@ void group_counters(const dsa_shape* s, dsa_dtype idx_dtype, dsa_dtype mla_dtype
   *out = dsa_group_stats{};
   out->n_full = n_full;
   out->n_shared = n_layers - n_full;
+  out->n_fused = group_fuses(s, idx_dtype) ? n_full : 0;
   out->indexer_flops = n_full * 2.0 * s->H * s->D * sum_n;
   out->indexer_bytes =
       n_full * ((double)rows * s->H * (s->D * ie + 4 + sc) + prefix * s->Hk * (s->D * ie + sc) + 4.0 * sum_n);

@@ -209,6 +209,8 @@ typedef struct {
 typedef struct {
   int32_t n_full, n_shared;
   int32_t n_launches;      /* kernels enqueued by the call (dsa_group_forward only) */
+  int32_t n_fused;         /* full layers run as dsa_indexer_topk runs (no score matrix); the
+                            * byte counters below still count the score matrix's write and read */
   double indexer_flops;    /* 2*H*D per (query, candidate) pair, per full layer */
   double indexer_bytes;    /* index q, w (+scales), index k of each item's prefix, fp32 scores written */
   double topk_bytes;       /* fp32 scores read + int32 indices written */

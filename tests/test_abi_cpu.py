@@ -192,6 +192,19 @@ def test_indexer_topk_workspace_layout(L):
     assert L.dsa_workspace_bytes(C.byref(sh), b.OP_GROUP) < L.dsa_workspace_bytes(C.byref(sh), b.OP_INDEXER_TOPK)
 
 
+def test_group_stats_count_the_fused_full_layers(L):
+    # prefill chunks over >= 65536 keys on the fp8 tile kernel run fused; bf16 prefill, short
+    # prefixes and decode rows do not
+    types = (C.c_int * 4)(b.FULL, b.SHARED, b.FULL, b.SHARED)
+    chunk = _shape(B=1, T=4096, s_cap=131072, H=32, D=128, Hk=32, topk=2048, Hm=64, Dc=512, Dr=64)
+    for shape, dt, want in [(chunk, b.FP8_E4M3, 2), (chunk, b.BF16, 0),
+                            (_shape(B=1, T=4096, s_cap=4096, H=32, D=128, Hk=32, topk=2048), b.FP8_E4M3, 0),
+                            (_shape(B=4, T=1, s_cap=1 << 20, H=32, D=128, Hk=32, topk=2048), b.FP8_E4M3, 0)]:
+        st = b.GroupStats()
+        assert L.dsa_group_stats_compute(C.byref(shape), dt, b.BF16, 4, types, None, None, C.byref(st)) == 0
+        assert (st.n_full, st.n_fused) == (2, want)
+
+
 def test_workspace_sizes(L):
     s = _shape(B=1, T=4096, s_cap=4096, topk=2048, Hm=64, Dc=512, Dr=64)
     assert L.dsa_workspace_bytes(C.byref(s), b.OP_GROUP) >= 4096 * 4096 * 4
