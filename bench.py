@@ -71,20 +71,95 @@ def parse():
                          "forward's indices, output and lse, a seeded output gradient) and the index-score "
                          "backward at the selected positions (a seeded score gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain device-to-device copy of BYTES (3 times) and exit: the reference "
-                         "kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
+                    help="only run the calibration library's copy kernel over BYTES (3 times) and exit: the "
+                         "reference kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only measure achievable peaks with the calibration library's own kernels and exit: a "
+                         "4 GiB copy, the sparse attention's row gather over the 128K chunk's and the 4K "
+                         "prefill's key ranges, and bf16 / fp8 matrix-core loops")
     return ap.parse_args()
+
+
+def calib_lib():
+    import ctypes as C
+    L = C.CDLL(os.path.join(ROOT, "dsa_indexer_top_lightning_amd", "libdsa_calib.so"))
+    L.calib_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
+    L.calib_read.argtypes = [C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p]
+    L.calib_gather.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    L.calib_mfma.argtypes = [C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    return L
+
+
+def _ok(rc):
+    if rc != 0:
+        raise RuntimeError(f"calibration kernel launch failed (HIP error {rc})")
 
 
 def copy_calibration(nbytes):
     import torch
+    L = calib_lib()
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    st = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
     for _ in range(3):
-        dst.copy_(src)
+        _ok(L.calib_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, st))
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 3}))
+    print(json.dumps({"kernel": "copy16", "copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+
+
+def calibrate():
+    """Achievable peaks from the calibration library's kernels (HIP events on the launch stream)."""
+    import torch
+    L = calib_lib()
+    stream = torch.cuda.current_stream()
+    st = stream.cuda_stream
+
+    def timed(f, n):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    nbytes = 4 << 30
+    src = torch.arange(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: _ok(L.calib_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, st)), 5)
+    assert torch.equal(dst, src), "copy kernel result differs from its source"
+    out["copy"] = {"bytes_moved": 2 * nbytes, "ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}
+    del dst
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    ms = timed(lambda: _ok(L.calib_read(src.data_ptr(), nbytes // 16, sink.data_ptr(), st)), 5)
+    out["read"] = {"bytes_read": nbytes, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9}
+    del src, sink
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    nq, k, row_bytes = 4096, 2048, 1152
+    for name, S in (("chunk128k_rows", 131072), ("prefill4k_rows", 4096)):
+        rows = torch.randint(0, 256, (S * row_bytes,), dtype=torch.uint8, device="cuda", generator=g)
+        idx = torch.empty((nq, k), dtype=torch.int32, device="cuda")
+        for q0 in range(0, nq, 256):   # k distinct random rows per query, ascending
+            r = torch.rand((256, S), device="cuda", generator=g).argsort(dim=1)[:, :k]
+            idx[q0:q0 + 256] = r.sort(dim=1).values.to(torch.int32)
+        sink = torch.zeros(nq, dtype=torch.int32, device="cuda")
+        ms = timed(lambda: _ok(L.calib_gather(rows.data_ptr(), idx.data_ptr(), nq, k, row_bytes, sink.data_ptr(),
+                                              st)), 10)
+        out[f"gather_{name}"] = {"rows": S, "queries": nq, "rows_per_query": k, "row_bytes": row_bytes, "ms": ms,
+                                 "TBps": nq * k * row_bytes / (ms * 1e-3) / 1e12}
+        del rows, idx
+    blocks, iters = 256 * 8, 4000
+    res = torch.empty(blocks * 256, device="cuda")
+    for fp8, name, flop in ((0, "mfma_bf16_32x32x16", 32 * 32 * 16 * 2), (1, "mfma_fp8_32x32x64", 32 * 32 * 64 * 2)):
+        ms = timed(lambda: _ok(L.calib_mfma(fp8, blocks, iters, res.data_ptr(), st)), 5)
+        total = blocks * 4 * iters * 4 * flop
+        out[name] = {"ms": ms, "TFLOPs": total / (ms * 1e-3) / 1e12}
+    print(json.dumps(out))
 
 
 def upload(w, inputs, torch):
@@ -329,6 +404,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.calibrate:
+        calibrate()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "

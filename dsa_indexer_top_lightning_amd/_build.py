@@ -11,6 +11,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
+# measurement kernels of the benchmark's calibration mode, a library of their own
+CALIB_LIB = os.path.join(PKG, "libdsa_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 SOURCES = ["indexer.hip", "topk.hip", "indexer_topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip", "indexer_bwd.hip", "prep.hip", "dsa_api.cpp"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
@@ -36,20 +39,25 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link libdsa.so in the package directory."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = ["hipcc", "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libdsa.so (and libdsa_calib.so) in the package directory."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], CALIB_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CALIB_LIB}")
     return LIB
 
 
