@@ -45,6 +45,9 @@ PEAK_HBM_GBS = 8000.0
 # keyed (workload, kernel), with the profile summary it comes from, and removed whenever that kernel
 # changes (then reported as null).
 MEASURED_TRAFFIC = {
+    ("chunk128k_fp8", "mla_mfma"): {
+        "bytes": 3913289.2 * 1024 * 2.0 + 263168.0 * 1024 * 1.0,
+        "source": "profiles/mla_mfma_chunk128k_fp8_hbm_counters.md"},
     ("decode32k_b64_bf16", "indexer_stream"): {
         "bytes": 8426542.5 * 1024 * 2.0 + 18968.1 * 1024 * 1.0,
         "source": "profiles/indexer_stream_decode32k_b64_bf16_hbm_counters.md"},
@@ -73,6 +76,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run the calibration library's copy kernel over BYTES (3 times) and exit: the "
                          "reference kernel whose FETCH_SIZE / WRITE_SIZE counters scale the HBM traffic figures")
+    ap.add_argument("--ab-indexer-topk", action="store_true",
+                    help="only time layer 0's indexer -> top-k both ways on --workload and exit: "
+                         "dsa_indexer_scores + dsa_topk_select, and dsa_indexer_topk (default sample stride), "
+                         "with a check that both give the same indices")
     ap.add_argument("--calibrate", action="store_true",
                     help="only measure achievable peaks with the calibration library's own kernels and exit: a "
                          "4 GiB copy, the sparse attention's row gather over the 128K chunk's and the 4K "
@@ -106,6 +113,53 @@ def copy_calibration(nbytes):
         _ok(L.calib_copy(src.data_ptr(), dst.data_ptr(), nbytes // 16, st))
     torch.cuda.synchronize()
     print(json.dumps({"kernel": "copy16", "copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "launches": 3}))
+
+
+def ab_indexer_topk(w, steps, warmup):
+    """Layer 0's indexer -> top-k of workload w, unfused and fused, HIP-event timed (mean of `steps`)."""
+    import torch
+
+    from dsa_indexer_top_lightning_amd import binding as B
+    from dsa_indexer_top_lightning_amd import synth
+    L = synth.build_layer_inputs(w, 0, True, with_mla=False)
+    dt = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[w.idx_dtype]
+    q = torch.from_numpy(L["idx_q"].view(np.int16) if w.idx_dtype == "bf16" else L["idx_q"]).cuda().view(dt)
+    k = torch.from_numpy(L["idx_k"].view(np.int16) if w.idx_dtype == "bf16" else L["idx_k"]).cuda().view(dt)
+    wt = torch.from_numpy(L["w"]).cuda()
+    qs = torch.from_numpy(L["idx_q_scale"]).cuda() if "idx_q_scale" in L else None
+    ks = torch.from_numpy(L["idx_k_scale"]).cuda() if "idx_k_scale" in L else None
+    del L
+    ke = torch.from_numpy(w.key_end()).cuda()
+    shape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk, key_end=ke)
+    ws = torch.empty((B.workspace_bytes(shape, B.OP_INDEXER_TOPK),), dtype=torch.uint8, device="cuda")
+    scores = ws[:w.B * w.T * w.S * 4].view(torch.float32).view(w.B, w.T, w.S)
+    tws = torch.empty((max(1, B.workspace_bytes(shape, B.OP_TOPK)),), dtype=torch.uint8, device="cuda")
+    a = torch.empty((w.B, w.T, w.topk), dtype=torch.int32, device="cuda")
+    f = torch.empty_like(a)
+    ex = dict(q_scale=qs, k_scale=ks, key_end=ke)
+
+    def unfused():
+        B.indexer_scores(q, k, wt, scores, **ex)
+        B.topk_select(scores, a, w.S, key_end=ke, workspace=tws)
+
+    def fused():
+        B.indexer_topk(q, k, wt, f, workspace=ws, **ex)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    t_u, t_f = timed(unfused), timed(fused)
+    same = bool(torch.equal(a, f))
+    print(json.dumps({"workload": w.name, "unfused_ms": t_u, "fused_ms": t_f, "indices_identical": same,
+                      "steps": steps, "warmup": warmup}))
 
 
 def calibrate():
@@ -407,6 +461,10 @@ def main():
         return
     if args.calibrate:
         calibrate()
+        return
+    if args.ab_indexer_topk:
+        from dsa_indexer_top_lightning_amd import synth
+        ab_indexer_topk(synth.WORKLOADS[args.workload], args.steps, args.warmup)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
