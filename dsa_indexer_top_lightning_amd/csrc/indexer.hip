@@ -1099,7 +1099,7 @@ void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
 // grid: x = block of 64 keys (or samples), y = query row.  256 threads: wave w takes keys
 // w, w+4, ...  With sampling, column c of the row is key kstride * c; in candidate mode
 // lane 0 appends each key whose order key reaches the row's threshold.
-template <int DT, int LPH>
+template <int DT, int LPH, int MODE>
 __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
   constexpr int H = 64 / LPH;
   constexpr int EPL = HD / LPH;                 // elements per lane
@@ -1114,10 +1114,10 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
   if (p.row_mask && !p.row_mask[row]) return;
   int64_t ks, ke;
   clamp_range(p.key_start, p.key_end, row, p.s_cap, ks, ke);
-  const int64_t kst = p.kstride;
+  const int64_t kst = MODE == G8_SAMPLES ? p.kstride : 1;
   const int64_t sblk = (int64_t)blockIdx.x * KPB;  // first column of the block
   if (sblk * kst >= ke || (sblk + KPB - 1) * kst < ks) return;
-  const uint32_t lk = p.lkey ? p.lkey[row] : 0u;
+  const uint32_t lk = MODE == G8_CANDIDATES ? p.lkey[row] : 0u;
   const int64_t b = row / p.T;
   const int Hk = p.Hk;
   const int h = lane / LPH, part = lane % LPH;
@@ -1185,7 +1185,7 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
 #pragma unroll
     for (int off = LPH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
     if (lane == 0) {
-      if (!p.lkey) {
+      if constexpr (MODE != G8_CANDIDATES) {
         p.scores[row * p.ld + col] = v;
       } else if (order_key(v) >= lk) {
         const int32_t slot = atomicAdd(p.cand_cnt + row, 1);
@@ -1214,6 +1214,22 @@ bool g8_path(const IndexerParams& p, Dtype dt) {
   const int64_t nq = (p.T + G8_BM - 1) / G8_BM;
   const int64_t nk = ((p.s_cap + p.kstride - 1) / p.kstride + G8_BN - 1) / G8_BN;
   return nq * nk <= INT32_MAX;
+}
+template <int DT, int MODE>
+void launch_stream_dm(const IndexerParams& p, dim3 grid, hipStream_t st) {
+  if (p.H == 16) hipLaunchKernelGGL((indexer_stream<DT, 4, MODE>), grid, dim3(256), 0, st, p);
+  else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<DT, 2, MODE>), grid, dim3(256), 0, st, p);
+  else hipLaunchKernelGGL((indexer_stream<DT, 1, MODE>), grid, dim3(256), 0, st, p);
+}
+template <int DT>
+void launch_stream_d(const IndexerParams& p, int mode, dim3 grid, hipStream_t st) {
+  if (mode == G8_CANDIDATES) launch_stream_dm<DT, G8_CANDIDATES>(p, grid, st);
+  else if (mode == G8_SAMPLES) launch_stream_dm<DT, G8_SAMPLES>(p, grid, st);
+  else launch_stream_dm<DT, G8_SCORES>(p, grid, st);
+}
+void launch_stream(const IndexerParams& p, Dtype dt, int mode, dim3 grid, hipStream_t st) {
+  if (dt == BF16) launch_stream_d<BF16>(p, mode, grid, st);
+  else launch_stream_d<FP8>(p, mode, grid, st);
 }
 // the decode stream kernel
 bool stream_path(const IndexerParams& p, Dtype dt) {
@@ -1272,15 +1288,8 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
   } else if (stream_path(p, dt)) {
     // decode: stream the keys once per query row
     dim3 grid((unsigned)((ncols + 63) / 64), (unsigned)((int64_t)p.B * p.T));
-    if (dt == BF16) {
-      if (p.H == 16) hipLaunchKernelGGL((indexer_stream<BF16, 4>), grid, dim3(256), 0, st, p);
-      else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<BF16, 2>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((indexer_stream<BF16, 1>), grid, dim3(256), 0, st, p);
-    } else {
-      if (p.H == 16) hipLaunchKernelGGL((indexer_stream<FP8, 4>), grid, dim3(256), 0, st, p);
-      else if (p.H == 32) hipLaunchKernelGGL((indexer_stream<FP8, 2>), grid, dim3(256), 0, st, p);
-      else hipLaunchKernelGGL((indexer_stream<FP8, 1>), grid, dim3(256), 0, st, p);
-    }
+    const int mode = p.lkey ? G8_CANDIDATES : (p.kstride != 1 ? G8_SAMPLES : G8_SCORES);
+    launch_stream(p, dt, mode, grid, st);
   } else if (mfma) {
     const int rs = (dt == BF16) ? MfmaCfg<BF16>::RS : MfmaCfg<FP8>::RS;
     const size_t lds = (size_t)(TM + TN) * rs + (size_t)p.H * TM * 4 + (dt == FP8 ? (size_t)p.Hk * TN * 4 : 0);
