@@ -544,12 +544,15 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
     dki = torch.empty(w.B, w.S, w.Hk, w.D, device="cuda")
     dwi = torch.empty(w.B, w.T, w.H, device="cuda")
     idx = cache.indices
+    bshape = B.make_shape(w.B, w.T, w.S, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr)
+    nbws = B.workspace_bytes(bshape, B.OP_SPARSE_MLA_BWD)
+    bws = torch.empty((nbws,), dtype=torch.uint8, device="cuda") if nbws else None
 
     def call(ev=None):
         if ev:
             ev[0].record(stream)
         B.sparse_mla_backward(L["q"], L["kv"], idx, w.sm_scale, L["out"], L["lse"], dout, dq, dkv, Dc=w.Dc,
-                              stream=stream)
+                              workspace=bws, stream=stream)
         if ev:
             ev[1].record(stream)
         B.index_backward(I["q"], I["k"], I["w"], idx, dI, dqi, dki, dwi, q_scale=I.get("q_scale"),

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 FULL, SHARED = 0, 1
-OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP, OP_INDEXER_TOPK = 0, 1, 2, 3, 4
+OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP, OP_INDEXER_TOPK, OP_SPARSE_MLA_BWD = 0, 1, 2, 3, 4, 5
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_NO_DONOR",
           4: "DSA_ERR_STALE_CACHE", 5: "DSA_ERR_WORKSPACE_TOO_SMALL", 6: "DSA_ERR_HIP"}
 
@@ -82,7 +82,8 @@ _SIGS = {
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p]),
     "dsa_sparse_mla_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float,
-                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                          C.c_size_t, C.c_void_p]),
     "dsa_index_prep": (C.c_int, [C.c_int32, C.c_int32, C.c_int32, C.c_float, C.c_int, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dsa_latent_append": (C.c_int, [C.c_int32, C.c_int32, C.c_int, C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p,
@@ -240,15 +241,18 @@ def index_backward(q, k, w, topk_indices, dI, dq, dk, dw, *, q_scale=None, k_sca
     return dq, dk, dw
 
 
-def sparse_mla_backward(q, kv, topk_indices, sm_scale, out, lse, dout, dq, dkv, *, Dc, stream=None):
+def sparse_mla_backward(q, kv, topk_indices, sm_scale, out, lse, dout, dq, dkv, *, Dc, workspace=None, stream=None):
     """dsa_sparse_mla_backward.  Forward inputs and results (out, lse), dout [B,T,Hm,Dc];
-    dq [B,T,Hm,Dc+Dr] and dkv [B,S,Dc+Dr] fp32 are written in place."""
+    dq [B,T,Hm,Dc+Dr] and dkv [B,S,Dc+Dr] fp32 are written in place; workspace: uint8 tensor
+    of at least workspace_bytes(shape, OP_SPARSE_MLA_BWD) bytes (None when that is 0)."""
     B, T, Hm, R = q.shape
     S = kv.shape[1]
     shape = make_shape(B, T, S, topk=topk_indices.shape[-1], Hm=Hm, Dc=Dc, Dr=R - Dc)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_sparse_mla_backward(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(kv),
                                          _dev_ptr(topk_indices), float(sm_scale), _dev_ptr(out), _dev_ptr(lse),
-                                         _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dkv), _stream(stream)))
+                                         _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dkv), _dev_ptr(workspace), ws_bytes,
+                                         _stream(stream)))
     return dq, dkv
 
 

@@ -113,6 +113,9 @@ size_t topk_ws(const dsa_shape* s) { return dsa::topk_workspace_bytes(s->B, s->T
 size_t mla_ws(const dsa_shape* s, dsa_dtype dt) {
   return dsa::mla_workspace_bytes(s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, (dsa::Dtype)dt);
 }
+size_t mla_bwd_ws(const dsa_shape* s, dsa_dtype dt) {
+  return dsa::mla_bwd_workspace_bytes(s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, (dsa::Dtype)dt);
+}
 size_t scores_bytes(const dsa_shape* s) { return align_up((size_t)rows_of(s) * (size_t)s->s_cap * sizeof(float)); }
 
 // Full layers of a group over rows at least this long run the fused indexer -> top-k.
@@ -249,6 +252,7 @@ size_t dsa_workspace_bytes(const dsa_shape* s, dsa_op op) {
       return fuse ? std::max(plain, indexer_topk_ws(s, true)) : plain;
     }
     case DSA_OP_INDEXER_TOPK: return indexer_topk_ws(s, fused_any(s));
+    case DSA_OP_SPARSE_MLA_BWD: return mla_bwd_ws(s, DSA_BF16);
   }
   return 0;
 }
@@ -314,19 +318,26 @@ dsa_status dsa_sparse_mla_attention(const dsa_shape* s, dsa_dtype dt, const void
 
 dsa_status dsa_sparse_mla_backward(const dsa_shape* s, dsa_dtype dt, const void* q, const void* kv,
                                    const int32_t* idx, float sm_scale, const void* out, const float* lse,
-                                   const void* dout, float* dq, float* dkv, void* stream) {
+                                   const void* dout, float* dq, float* dkv, void* ws, size_t ws_bytes,
+                                   void* stream) {
   dsa_status st = check_mla_shape(s, dt);
   if (st == DSA_OK) st = check_sm_scale(sm_scale);
   if (st != DSA_OK) return st;
-  if (!dsa::mla_bwd_supported(s->Hm, s->Dc, s->Dr, (dsa::Dtype)dt))
-    return fail(DSA_ERR_UNSUPPORTED, "sparse MLA backward: Hm=%d Dc=%d Dr=%d need Hm <= 64, Dc <= 512, Dc+Dr <= 640",
+  const bool mfma = dsa::mla_bwd_uses_mfma(s->Hm, s->Dc, s->Dr, s->s_cap, (dsa::Dtype)dt);
+  if (!mfma && !dsa::mla_bwd_supported(s->Hm, s->Dc, s->Dr, (dsa::Dtype)dt))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "sparse MLA backward: Hm=%d Dc=%d Dr=%d need Hm <= 64, Dc <= 512, Dc+Dr <= 640 (or bf16 with "
+                "Dc=512, Dr=64 and Hm a multiple of 64)",
                 s->Hm, s->Dc, s->Dr);
   if (s->s_cap > 0 && (!kv || !dkv)) return fail(DSA_ERR_INVALID_ARG, "kv and dkv must be non-NULL");
   if (rows_of(s) > 0 && (!q || !idx || !out || !lse || !dout || !dq))
     return fail(DSA_ERR_INVALID_ARG, "q, topk_indices, out, lse, dout and dq must be non-NULL");
+  const size_t need = mla_bwd_ws(s, dt);
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "sparse MLA backward workspace %zu < %zu", ws_bytes, need);
   const dsa::MlaBwdParams p{s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, q, kv, idx, sm_scale,
                             out, lse, dout, dq, dkv};
-  hipError_t e = dsa::launch_sparse_mla_bwd(p, (dsa::Dtype)dt, (hipStream_t)stream, nullptr);
+  hipError_t e = dsa::launch_sparse_mla_bwd(p, (dsa::Dtype)dt, ws, ws_bytes, (hipStream_t)stream, nullptr);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "sparse MLA backward launch");
 }
 

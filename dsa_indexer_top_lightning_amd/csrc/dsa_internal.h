@@ -138,7 +138,14 @@ hipError_t launch_sparse_mla(const MlaParams& p, Dtype dt, void* ws, size_t ws_b
                              int* n_launches);
 size_t mla_bwd_lds_bytes(int Hm, int Dc, int Dr, Dtype dt);
 bool mla_bwd_supported(int Hm, int Dc, int Dr, Dtype dt);
-hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
+// bf16 with 512 + 64 latent rows and heads in groups of 64 runs on the matrix cores (its
+// workspace holds P and sm_scale * dz per selected slot); other shapes on the vector kernel
+bool mla_bwd_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);
+size_t mla_bwd_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt);
+hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws_bytes, hipStream_t st,
+                                      int* n_launches);
+hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                                 int* n_launches);
 bool index_bwd_supported(int H, int D, int Hk);
 hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
 hipError_t launch_index_prep(const PrepParams& p, hipStream_t st);

@@ -237,7 +237,9 @@ bool mla_bwd_supported(int Hm, int Dc, int Dr, Dtype dt) {
          Dc + Dr <= 64 * BW_RI && (dt == F32 || dt == BF16) && mla_bwd_lds_bytes(Hm, Dc, Dr, dt) <= 150 * 1024;
 }
 
-hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, hipStream_t st, int* n_launches) {
+hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                                 int* n_launches) {
+  if (mla_bwd_uses_mfma(p.Hm, p.Dc, p.Dr, p.s_cap, dt)) return launch_sparse_mla_bwd_mfma(p, ws, ws_bytes, st, n_launches);
   const int64_t rows = (int64_t)p.B * p.T;
   const int64_t nkv = (int64_t)p.B * p.s_cap * (p.Dc + p.Dr);
   // few query tokens (decode): split each selection so that >= 1024 workgroups run

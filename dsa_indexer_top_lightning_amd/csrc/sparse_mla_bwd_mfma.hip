@@ -1,0 +1,605 @@
+// Backward of the sparse MLA attention on the matrix cores (bf16, 576/512 latent rows,
+// heads in groups of 64).  The math is the vector kernel's (sparse_mla_bwd.hip):
+//
+//   P_j  = exp(z_j - lse),  z_j = sm_scale q . c_j        dP_j = dout . c_j[:512]
+//   dz_j = P_j (dP_j - D),  D = dout . o                   dz'_j = sm_scale dz_j
+//   dq   = sum_j dz'_j c_j                                  dc_j += sum_h dz'_j q + [P_j dout, 0]
+//
+// as four launches, so that no kernel holds more than one head-major operand set:
+//   mla_bwd_delta  D = dout . o per (query, head), fp32, into the workspace;
+//   mla_bwd_pz     per (query, split, head group): the forward's 64-row tiles gathered into
+//                  LDS; S^T = C Q^T and dP^T = C dO^T on v_mfma_f32_32x32x16_bf16 (query and
+//                  output-gradient fragments held in registers), then P and dz' as bf16 into
+//                  the workspace: [query][slot][head] and, for dq, [query][head][slot];
+//   mla_bwd_dc     per (query, split, head group): the query's 64 head rows and output
+//                  gradients in LDS; per tile dC = dz'^T Q + P^T [dO, 0] (K = heads), added to
+//                  the selected latent rows with fp32 atomics;
+//   mla_bwd_dq     per (query, split, head group): the tiles gathered again, dq^T += C^T dz'^T.
+// Slots past the last valid entry of a row are never touched; invalid slots inside that
+// range get P = dz' = 0, so the later kernels read whole tiles without masks.
+//
+// Fragment order along the contraction: the transposing LDS reads (ds_read_b64_tr_b16) of
+// a 16-row block starting at rb give lane group lg the rows rb + 8 (i / 4) + 4 lg + i % 4
+// (i = 0..7), the order in which a 32 x 32 accumulator holds its rows; every fragment
+// paired with such a read (global loads of dz' and P) follows the same order.
+#include <algorithm>
+
+#include "dsa_internal.h"
+#include "mla_tile.h"
+
+namespace dsa {
+namespace {
+using namespace mla;
+
+constexpr float BM_LOG2E = 1.4426950408889634f;
+
+// workspace arrays (bf16 bits); Tp = topk rounded up to whole 64-row tiles
+struct BwWs {
+  float* delta;   // [rows][Hm]
+  uint16_t* p;    // [rows][Tp][Hm]
+  uint16_t* dz;   // [rows][Tp][Hm]   sm_scale * dz
+  uint16_t* dzt;  // [rows][Hm][Tp]   the same, slot-contiguous per head
+  int Tp;
+};
+
+__device__ __forceinline__ bool bm_valid(int32_t v, int64_t s_cap) { return v >= 0 && (int64_t)v < s_cap; }
+
+// the last slot of the row whose entry is valid (-1: none), from every wave's scan
+__device__ int bm_last_valid(const int32_t* gidx, int topk, int64_t s_cap, int* xs) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int emax = -1;
+  for (int e0 = 64 * wave; e0 < topk; e0 += 8 * 256) {
+    int32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + 256 * u + lane;
+      v[u] = e < topk ? gidx[e] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (bm_valid(v[u], s_cap)) emax = e0 + 256 * u + lane;
+  }
+  for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+  if (lane == 0) xs[wave] = emax;
+  __syncthreads();
+  emax = max(max(xs[0], xs[1]), max(xs[2], xs[3]));
+  __syncthreads();
+  return emax;
+}
+
+// Transposing read of a 16-row block of a tile-layout buffer: dims [32 nb, +32) (segment
+// nb / 2), rows [rb, rb + 16) (rb a multiple of 16, so perm(row) = perm(row - rb)).
+struct TrOff {
+  int o[2][2];  // [read][dim-block parity]
+  __device__ __forceinline__ TrOff(int lane) {
+    const int lr = lane & 31, lg = lane >> 5;
+    const int blk = lr >> 4, li = lr & 15, x = (li & 3) >> 1;
+    const int vrow = 4 * lg + (li >> 2);
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+      for (int dp = 0; dp < 2; ++dp)
+        o[rd][dp] = (vrow + 8 * rd) * SEG + 16 * ((4 * dp + 2 * blk + x) ^ perm(vrow + 8 * rd)) + ((li & 1) << 3);
+  }
+  __device__ __forceinline__ bf16x8 read(const unsigned char* buf, int nb, int rb) const {
+    const int off = (nb >> 1) * GROUP_BYTES + rb * SEG;
+    union {
+      i16x4 h[2];
+      bf16x8 b;
+    } a;
+    const bool odd = nb & 1;  // a select, not an index: nb may vary per wave
+    a.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(buf + (odd ? o[0][1] : o[0][0]) + off));
+    a.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)(buf + (odd ? o[1][1] : o[1][0]) + off));
+    return a.b;
+  }
+};
+
+// 8 bf16 at p[0..3] and p[8..11] (the two halves of a permuted fragment), 8-byte loads
+__device__ __forceinline__ bf16x8 ld_split8(const uint16_t* p) {
+  const uint2 lo = *reinterpret_cast<const uint2*>(p);
+  const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
+  const i32x4 v = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------- D = dout . o
+// grid = rows; wave w takes heads w, w + 4, ...; 8 values per lane
+__global__ __launch_bounds__(256) void mla_bwd_delta(MlaBwdParams p, float* __restrict__ delta) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t tok = blockIdx.x;
+  for (int h = wave; h < p.Hm; h += 4) {
+    const int64_t o = ((tok * p.Hm + h) * MDC + 8 * lane);
+    const i32x4 g = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.dout) + o);
+    const i32x4 y = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.out) + o);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t a = (uint32_t)g[e], c = (uint32_t)y[e];
+      d = fmaf(__uint_as_float(a << 16), __uint_as_float(c << 16), d);
+      d = fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(c & 0xffff0000u), d);
+    }
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off, 64);
+    if (lane == 0) delta[tok * p.Hm + h] = d;
+  }
+}
+
+// ---------------------------------------------------------------- P and dz'
+constexpr int PZ_RING = 4 * 4 * MT * 4;                  // per-wave ring of 4 tiles' entries
+constexpr int PZ_LDS = 2 * TILE_BYTES + PZ_RING + 64;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_bwd_pz(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* xs = reinterpret_cast<int*>(smem + 2 * TILE_BYTES + PZ_RING);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int hh = wave & 1, vv = wave >> 1;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int64_t rows = (int64_t)p.B * p.T;
+  const int64_t tok = rows - 1 - (int64_t)blockIdx.x / nsplit;
+  const int split = (int)((int64_t)blockIdx.x % nsplit);
+  const int hg = blockIdx.y;
+  const int64_t b = tok / p.T;
+  const int64_t s_cap = p.s_cap;
+  const int topk = p.topk, Tp = w.Tp;
+  const int32_t* gidx = p.idx + tok * (int64_t)topk;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  auto tile_dst = [&](int bf) -> uint32_t { return smem_lds + bf * TILE_BYTES + wv * (16 * SEG); };
+
+  // tiles of this split, up to the row's last valid entry (the same range for every split
+  // and for the later kernels)
+  const int emax = bm_last_valid(gidx, topk, s_cap, xs);
+  const int t_row = emax < 0 ? 0 : emax / MT + 1;
+  const int t0 = split * tiles_per_split;
+  const int ntiles = max(0, min(t_row, t0 + tiles_per_split) - t0);
+  if (ntiles == 0) return;
+
+  const int32_t* ering = reinterpret_cast<const int32_t*>(smem + 2 * TILE_BYTES) + wv * 4 * MT;
+  const uint32_t ering_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int32_t*)ering;
+  auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
+  auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
+  auto in_range = [&](int t) -> bool { return (t0 + t) * MT + lane < topk; };
+  const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
+  auto tile_src = [&](int32_t ent) -> GatherSrc {
+    return gather_src(kvg, MRB, bm_valid(ent, s_cap) ? ent : 0, wave, lane);
+  };
+
+  // prologue: entries of tiles 0 and 1, the query's 64 head rows into buffer 1 and their
+  // output gradients (1024-byte rows) into buffer 0, all in flight together
+  fetch_entries(0);
+  fetch_entries(1);
+  {
+    const unsigned char* qrows = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + hg * MHG) * MRB;
+    gather_tile(tile_dst(1), gather_src(qrows, MRB, lane, wave, lane));
+    const unsigned char* grows = static_cast<const unsigned char*>(p.dout) + (tok * p.Hm + hg * MHG) * (MDC * 2);
+    gather_tile<8>(tile_dst(0), gather_src(grows, MDC * 2, lane, wave, lane));
+  }
+  const int myhead = hg * MHG + 32 * hh + lr;
+  const float Dh = w.delta[tok * p.Hm + myhead];
+  const float lse2 = p.lse[tok * p.Hm + myhead] * BM_LOG2E;
+  wait_vmem();
+  lds_barrier();
+
+  // query and output-gradient fragments of head 32hh + lr, dims 16 st + 8 lg .. +7
+  bf16x8 qf[MROW / 16], gf[MDC / 16];
+  {
+    const int qr = 32 * hh + lr;
+    const unsigned char* qt = smem + TILE_BYTES + qr * SEG;
+    const unsigned char* gt = smem + qr * SEG;
+#pragma unroll
+    for (int st = 0; st < MROW / 16; ++st)
+      qf[st] = *reinterpret_cast<const bf16x8*>(qt + (st >> 2) * GROUP_BYTES + 16 * ((2 * (st & 3) + lg) ^ perm(qr)));
+#pragma unroll
+    for (int st = 0; st < MDC / 16; ++st)
+      gf[st] = *reinterpret_cast<const bf16x8*>(gt + (st >> 2) * GROUP_BYTES + 16 * ((2 * (st & 3) + lg) ^ perm(qr)));
+  }
+#pragma unroll
+  for (int st = 0; st < MDC / 16; ++st) asm volatile("" : "+a"(qf[st]), "+a"(gf[st]));
+#pragma unroll
+  for (int st = MDC / 16; st < MROW / 16; ++st) asm volatile("" : "+v"(qf[st]));
+  lds_barrier();  // every wave has read buffer 0 before the first gather overwrites it
+
+  uint64_t vmask_nxt;
+  {
+    const int32_t e0 = read_entry(0);
+    vmask_nxt = __ballot(bm_valid(e0, s_cap) && in_range(0));
+    gather_tile(tile_dst(0), tile_src(e0));
+  }
+  fetch_entries(2);
+
+  const float c1 = p.sm_scale * BM_LOG2E;
+  const int mk = 32 * vv + lr;
+  int koff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) koff[u] = mk * SEG + 16 * ((2 * u + lg) ^ perm(mk));
+  uint16_t* wp = w.p + (tok * Tp) * p.Hm + myhead;
+  uint16_t* wz = w.dz + (tok * Tp) * p.Hm + myhead;
+  uint16_t* wzt = w.dzt + (tok * p.Hm + myhead) * (int64_t)Tp;
+  // P and dz' of a tile as bf16 pairs (rows r, r + 1 of the accumulator), stored after the
+  // next tile barrier: stores count in vmcnt, and stored right away they would hold up that
+  // barrier's wait for the gather
+  uint32_t pp[8], pz[8];
+  auto store_tile = [&](int t) {
+    const int e0 = (t0 + t) * MT + 32 * vv;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t e = e0 + 8 * (r >> 2) + 4 * lg + (r & 3);
+      wp[e * p.Hm] = (uint16_t)((r & 1) ? pp[r >> 1] >> 16 : pp[r >> 1]);
+      wz[e * p.Hm] = (uint16_t)((r & 1) ? pz[r >> 1] >> 16 : pz[r >> 1]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(wzt + e0 + 8 * q + 4 * lg) = make_uint2(pz[2 * q], pz[2 * q + 1]);
+  };
+
+  for (int i = 0; i < ntiles; ++i) {
+    const int bf = i & 1;
+    tile_barrier();
+    if (i > 0) store_tile(i - 1);
+    const uint64_t vmask = vmask_nxt;
+    const bool more = i + 1 < ntiles;
+    GatherSrc gnext;
+    if (more) {
+      const int32_t e_next = read_entry(i + 1);
+      vmask_nxt = __ballot(bm_valid(e_next, s_cap) && in_range(i + 1));
+      gnext = tile_src(e_next);
+    }
+    const unsigned char* tb = smem + bf * TILE_BYTES;
+    f32x16 s, g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = 0.f;
+      g[r] = 0.f;
+    }
+    {
+      constexpr int KG = 4;
+      auto kfrag = [&](int st) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(tb + koff[st & 3] + (st >> 2) * GROUP_BYTES);
+      };
+      constexpr int NG = MROW / 16 / KG;
+      bf16x8 kf[3][KG];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int u = 0; u < KG; ++u) kf[gg][u] = kfrag(KG * gg + u);
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        if (gg + 2 < NG) {
+#pragma unroll
+          for (int u = 0; u < KG; ++u) kf[(gg + 2) % 3][u] = kfrag(KG * (gg + 2) + u);
+        }
+#pragma unroll
+        for (int u = 0; u < KG; ++u) {
+          const int st = KG * gg + u;
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[gg % 3][u], qf[st], s, 0, 0, 0);
+          if (st < MDC / 16) g = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[gg % 3][u], gf[st], g, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (gg < 6 && more) {
+          gather_part(gg, tile_dst(bf ^ 1), gnext);
+          if (gg == 5) fetch_entries(i + 3);
+        }
+      }
+    }
+    // P, dz' of rows 32vv + 8(r/4) + 4lg + r%4 of the tile, head myhead
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float pv[2], zv[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int m = 32 * vv + 8 * ((r + u) >> 2) + 4 * lg + ((r + u) & 3);
+        const bool ok = (vmask >> m) & 1ull;
+        const float P = ok ? __builtin_amdgcn_exp2f(fmaf(s[r + u], c1, -lse2)) : 0.f;
+        pv[u] = P;
+        zv[u] = ok ? p.sm_scale * P * (g[r + u] - Dh) : 0.f;
+      }
+      pp[r >> 1] = (uint32_t)f32_to_bf16_bits(pv[0]) | ((uint32_t)f32_to_bf16_bits(pv[1]) << 16);
+      pz[r >> 1] = (uint32_t)f32_to_bf16_bits(zv[0]) | ((uint32_t)f32_to_bf16_bits(zv[1]) << 16);
+    }
+  }
+  store_tile(ntiles - 1);
+}
+
+// ---------------------------------------------------------------- dC
+// Dim blocks of wave w: (row block mb, dim block nb) for mb in {0, 1}, nb in [4w, 4w + 4),
+// and the rope block (mb = w & 1, nb = 16 + w / 2): 9 accumulators.
+constexpr int DC_LDS = TILE_BYTES + 8 * GROUP_BYTES + MT * 4 + 64;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* qbuf = smem;                       // the query's 64 head rows, tile layout
+  unsigned char* gbuf = smem + TILE_BYTES;          // their output gradients, 8 segments
+  int32_t* sidx = reinterpret_cast<int32_t*>(smem + TILE_BYTES + 8 * GROUP_BYTES);
+  int* xs = reinterpret_cast<int*>(sidx + MT);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int64_t rows = (int64_t)p.B * p.T;
+  const int64_t tok = rows - 1 - (int64_t)blockIdx.x / nsplit;
+  const int split = (int)((int64_t)blockIdx.x % nsplit);
+  const int hg = blockIdx.y;
+  const int64_t b = tok / p.T;
+  const int64_t s_cap = p.s_cap;
+  const int topk = p.topk, Tp = w.Tp;
+  const int32_t* gidx = p.idx + tok * (int64_t)topk;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  const int emax = bm_last_valid(gidx, topk, s_cap, xs);
+  const int t_row = emax < 0 ? 0 : emax / MT + 1;
+  const int t0 = split * tiles_per_split;
+  const int ntiles = max(0, min(t_row, t0 + tiles_per_split) - t0);
+  if (ntiles == 0) return;
+  {
+    const unsigned char* qrows = static_cast<const unsigned char*>(p.q) + (tok * p.Hm + hg * MHG) * MRB;
+    gather_tile(smem_lds + wv * (16 * SEG), gather_src(qrows, MRB, lane, wave, lane));
+    const unsigned char* grows = static_cast<const unsigned char*>(p.dout) + (tok * p.Hm + hg * MHG) * (MDC * 2);
+    gather_tile<8>(smem_lds + TILE_BYTES + wv * (16 * SEG), gather_src(grows, MDC * 2, lane, wave, lane));
+  }
+
+  const TrOff tr(lane);
+  const int rope_mb = wv & 1, rope_nb = 16 + (wv >> 1);
+  f32x16 acc[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  // A fragments of a tile (dz'^T and P^T, rows 32mb + lr, heads of k-step ks in the permuted
+  // order): two 8-byte loads each from the [slot][head] arrays
+  const int64_t hoff = hg * MHG + 4 * lg;
+  auto load_a = [&](int t, bf16x8 (&az)[2][4], bf16x8 (&ap)[2][4]) {
+    const int64_t e0 = (int64_t)(t0 + t) * MT;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t o = ((tok * Tp + e0 + 32 * mb + lr) * p.Hm) + hoff + 16 * ks;
+        az[mb][ks] = ld_split8(w.dz + o);
+        ap[mb][ks] = ld_split8(w.p + o);
+      }
+  };
+  bf16x8 az0[2][4], ap0[2][4], az1[2][4], ap1[2][4];
+  load_a(0, az0, ap0);
+  wait_vmem();
+  __syncthreads();  // the query and gradient copies are in LDS
+
+  float* dkv = p.dkv + b * s_cap * MROW;
+  // one tile: its row indices into LDS, the next tile's A fragments requested, 68 products,
+  // then the row gradients added to the latent rows
+  auto step = [&](int i, const bf16x8 (&az)[2][4], const bf16x8 (&ap)[2][4], bf16x8 (&nz)[2][4],
+                  bf16x8 (&np)[2][4]) {
+    if (tid < MT) {
+      const int e = (t0 + i) * MT + tid;
+      const int32_t v = e < topk ? gidx[e] : -1;
+      sidx[tid] = bm_valid(v, s_cap) ? v : -1;
+    }
+    if (i + 1 < ntiles) load_a(i + 1, nz, np);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int rb = 16 * ks;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int nb = 4 * wv + j;
+        const bf16x8 bq = tr.read(qbuf, nb, rb), bg = tr.read(gbuf, nb, rb);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(az[mb][ks], bq, acc[4 * mb + j], 0, 0, 0);
+          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[mb][ks], bg, acc[4 * mb + j], 0, 0, 0);
+        }
+      }
+      const bf16x8 bq = tr.read(qbuf, rope_nb, rb);
+      acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(az[rope_mb][ks], bq, acc[8], 0, 0, 0);
+    }
+    lds_barrier();  // sidx of this tile is in place (no wait for the atomics or the prefetch)
+    // accumulator (mb, nb) holds dim 32nb + lr of rows 32mb + 8(r/4) + 4lg + r%4
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+      const int mb = j < 8 ? (j >> 2) : rope_mb;
+      const int nb = j < 8 ? 4 * wv + (j & 3) : rope_nb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t ri = sidx[32 * mb + 8 * (r >> 2) + 4 * lg + (r & 3)];
+        if (ri >= 0) unsafeAtomicAdd(dkv + (int64_t)ri * MROW + 32 * nb + lr, acc[j][r]);
+        acc[j][r] = 0.f;
+      }
+    }
+    lds_barrier();  // sidx is read before the next tile rewrites it
+  };
+  for (int i = 0; i < ntiles; i += 2) {
+    step(i, az0, ap0, az1, ap1);
+    if (i + 1 < ntiles) step(i + 1, az1, ap1, az0, ap0);
+  }
+}
+
+// ---------------------------------------------------------------- dq
+// Accumulators of wave w: dq^T blocks (dims 32nb, heads 32hb) for nb in [4w, 4w + 4), hb in
+// {0, 1}, and the rope block (nb = 16 + w / 2, hb = w & 1).
+constexpr int DQ_LDS = 2 * TILE_BYTES + PZ_RING + 64;
+
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* xs = reinterpret_cast<int*>(smem + 2 * TILE_BYTES + PZ_RING);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane & 31, lg = lane >> 5;
+  const int64_t rows = (int64_t)p.B * p.T;
+  const int64_t tok = rows - 1 - (int64_t)blockIdx.x / nsplit;
+  const int split = (int)((int64_t)blockIdx.x % nsplit);
+  const int hg = blockIdx.y;
+  const int64_t b = tok / p.T;
+  const int64_t s_cap = p.s_cap;
+  const int topk = p.topk, Tp = w.Tp;
+  const int32_t* gidx = p.idx + tok * (int64_t)topk;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+  auto tile_dst = [&](int bf) -> uint32_t { return smem_lds + bf * TILE_BYTES + wv * (16 * SEG); };
+
+  const int emax = bm_last_valid(gidx, topk, s_cap, xs);
+  const int t_row = emax < 0 ? 0 : emax / MT + 1;
+  const int t0 = split * tiles_per_split;
+  const int ntiles = max(0, min(t_row, t0 + tiles_per_split) - t0);
+  const int rope_hb = wv & 1, rope_nb = 16 + (wv >> 1);
+  f32x16 acc[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+
+  if (ntiles > 0) {
+    const int32_t* ering = reinterpret_cast<const int32_t*>(smem + 2 * TILE_BYTES) + wv * 4 * MT;
+    const uint32_t ering_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const int32_t*)ering;
+    auto fetch_entries = [&](int t) { dma4(gidx + min((t0 + t) * MT + lane, topk - 1), ering_lds + (t & 3) * MT * 4); };
+    auto read_entry = [&](int t) -> int32_t { return ering[(t & 3) * MT + lane]; };
+    const unsigned char* kvg = static_cast<const unsigned char*>(p.kv) + b * s_cap * MRB;
+    // invalid slots gather row 0 (in bounds); their dz' is 0
+    auto tile_src = [&](int32_t ent) -> GatherSrc {
+      return gather_src(kvg, MRB, bm_valid(ent, s_cap) ? ent : 0, wave, lane);
+    };
+    // B fragments of a tile (dz'^T: heads 32hb + lr, slots of k-step ks in the permuted order)
+    auto load_b = [&](int t, bf16x8 (&bz)[2][4]) {
+      const int64_t e0 = (int64_t)(t0 + t) * MT + 4 * lg;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          bz[hb][ks] = ld_split8(w.dzt + (tok * p.Hm + hg * MHG + 32 * hb + lr) * (int64_t)Tp + e0 + 16 * ks);
+    };
+    fetch_entries(0);
+    fetch_entries(1);
+    wait_vmem();
+    lds_barrier();
+    gather_tile(tile_dst(0), tile_src(read_entry(0)));
+    fetch_entries(2);
+    bf16x8 bz0[2][4], bz1[2][4];
+    load_b(0, bz0);
+    const TrOff tr(lane);
+    // one tile: wait for its gather and B fragments, request the next tile's, 36 products
+    auto step = [&](int i, const bf16x8 (&bz)[2][4], bf16x8 (&nz)[2][4]) {
+      const int bf = i & 1;
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // tile i and its B fragments landed
+      if (i + 1 < ntiles) {
+        gather_tile(tile_dst(bf ^ 1), tile_src(read_entry(i + 1)));
+        fetch_entries(i + 3);
+        load_b(i + 1, nz);
+      }
+      const unsigned char* tb = smem + bf * TILE_BYTES;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int rb = 16 * ks;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8 a = tr.read(tb, 4 * wv + j, rb);
+          acc[2 * j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[0][ks], acc[2 * j], 0, 0, 0);
+          acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[1][ks], acc[2 * j + 1], 0, 0, 0);
+        }
+        const bf16x8 a = tr.read(tb, rope_nb, rb);
+        acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[rope_hb][ks], acc[8], 0, 0, 0);
+      }
+    };
+    for (int i = 0; i < ntiles; i += 2) {
+      step(i, bz0, bz1);
+      if (i + 1 < ntiles) step(i + 1, bz1, bz0);
+    }
+  }
+  // accumulator (nb, hb) holds, for head 32hb + lr, dims 32nb + 8(r/4) + 4lg + r%4
+#pragma unroll
+  for (int j = 0; j < 9; ++j) {
+    const int nb = j < 8 ? 4 * wv + (j >> 1) : rope_nb;
+    const int hb = j < 8 ? (j & 1) : rope_hb;
+    float* dq = p.dq + (tok * p.Hm + hg * MHG + 32 * hb + lr) * MROW + 32 * nb + 4 * lg;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (nsplit == 1) {
+        *reinterpret_cast<float4*>(dq + 8 * q) = make_float4(acc[j][4 * q], acc[j][4 * q + 1], acc[j][4 * q + 2], acc[j][4 * q + 3]);
+      } else if (ntiles > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) unsafeAtomicAdd(dq + 8 * q + e, acc[j][4 * q + e]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void bm_zero(float* x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) x[i] = 0.f;
+}
+
+struct BmPlan {
+  int nsplit, tiles_per_split;
+};
+// few query tokens: split each selection so that about 1024 workgroups run
+BmPlan bm_plan(int64_t rows, int groups, int topk) {
+  const int tiles = (topk + MT - 1) / MT;
+  int nsplit = 1;
+  const int64_t items = rows * groups;
+  if (items > 0 && items < 1024) nsplit = (int)std::min<int64_t>(tiles, (1024 + items - 1) / items);
+  const int per = (tiles + nsplit - 1) / nsplit;
+  return BmPlan{per > 0 ? (tiles + per - 1) / per : 1, per};
+}
+
+size_t bm_al(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+bool mla_bwd_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt) {
+  return dt == BF16 && Dc == MDC && Dr == MROW - MDC && Hm % MHG == 0 && s_cap * (int64_t)MRB < (int64_t(1) << 32);
+}
+
+size_t mla_bwd_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt) {
+  if (!mla_bwd_uses_mfma(Hm, Dc, Dr, s_cap, dt)) return 0;
+  const size_t rows = (size_t)B * T, Tp = (size_t)(topk + MT - 1) / MT * MT;
+  return bm_al(rows * Hm * 4) + 3 * bm_al(rows * Tp * Hm * 2);
+}
+
+hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws_bytes, hipStream_t st,
+                                      int* n_launches) {
+  const int64_t rows = (int64_t)p.B * p.T;
+  const int Tp = (p.topk + MT - 1) / MT * MT;
+  if (ws_bytes < mla_bwd_workspace_bytes(p.B, p.T, p.Hm, p.Dc, p.Dr, p.topk, p.s_cap, BF16) || (rows > 0 && !ws))
+    return hipErrorInvalidValue;
+  const int64_t nkv = (int64_t)p.B * p.s_cap * MROW;
+  if (nkv > 0) {
+    hipLaunchKernelGGL(bm_zero, dim3((unsigned)std::min<int64_t>((nkv + 255) / 256, 4096)), dim3(256), 0, st, p.dkv, nkv);
+    if (n_launches) ++*n_launches;
+  }
+  if (rows == 0) return hipGetLastError();
+  char* base = static_cast<char*>(ws);
+  BwWs w;
+  w.delta = reinterpret_cast<float*>(base);
+  base += bm_al((size_t)rows * p.Hm * 4);
+  const size_t arr = bm_al((size_t)rows * Tp * p.Hm * 2);
+  w.p = reinterpret_cast<uint16_t*>(base);
+  w.dz = reinterpret_cast<uint16_t*>(base + arr);
+  w.dzt = reinterpret_cast<uint16_t*>(base + 2 * arr);
+  w.Tp = Tp;
+  const int groups = p.Hm / MHG;
+  const BmPlan pl = bm_plan(rows, groups, p.topk);
+  const int64_t nq = rows * p.Hm * MROW;
+  if (pl.nsplit > 1 && nq > 0) {
+    hipLaunchKernelGGL(bm_zero, dim3((unsigned)std::min<int64_t>((nq + 255) / 256, 4096)), dim3(256), 0, st, p.dq, nq);
+    if (n_launches) ++*n_launches;
+  }
+  hipLaunchKernelGGL(mla_bwd_delta, dim3((unsigned)rows), dim3(256), 0, st, p, w.delta);
+  const dim3 grid((unsigned)(rows * pl.nsplit), (unsigned)groups);
+  hipError_t e;
+  {
+    static std::atomic<size_t> high{0};
+    if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_pz), PZ_LDS, high)) != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_bwd_pz, grid, dim3(256), PZ_LDS, st, p, pl.nsplit, pl.tiles_per_split, w);
+  }
+  {
+    static std::atomic<size_t> high{0};
+    if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dc), DC_LDS, high)) != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_bwd_dc, grid, dim3(256), DC_LDS, st, p, pl.nsplit, pl.tiles_per_split, w);
+  }
+  {
+    static std::atomic<size_t> high{0};
+    if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dq), DQ_LDS, high)) != hipSuccess) return e;
+    hipLaunchKernelGGL(mla_bwd_dq, grid, dim3(256), DQ_LDS, st, p, pl.nsplit, pl.tiles_per_split, w);
+  }
+  if (n_launches) *n_launches += 4;
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -55,7 +55,8 @@ typedef enum {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA = 2,
   DSA_OP_GROUP = 3,
-  DSA_OP_INDEXER_TOPK = 4
+  DSA_OP_INDEXER_TOPK = 4,
+  DSA_OP_SPARSE_MLA_BWD = 5
 } dsa_op;
 
 /* Problem shape (host struct).  Fields a call does not use are ignored. */
@@ -312,12 +313,18 @@ dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
  *   dkv [B,S,Dc+Dr] fp32, overwritten: zeroed by the call, then every selected row
  *       collects its contributions with fp32 atomics (their order is not fixed, so dkv
  *       is reproducible to fp32 rounding, not bit for bit)
- * Requires Hm <= 64, Dc <= 512, Dc + Dr <= 640 (DSA_ERR_UNSUPPORTED otherwise);
- * DSA_ERR_INVALID_ARG on NULL pointers or a bad sm_scale.  No workspace.
+ *   workspace  ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_SPARSE_MLA_BWD): nonzero only
+ *       for bf16 with Dc = 512, Dr = 64 and Hm a multiple of 64, which runs on the matrix
+ *       cores; the workspace then holds D per (query, head) and P and sm_scale dz per
+ *       (query, selected slot, head) in bf16 (6 bytes per (query, slot, head))
+ * Requires Hm <= 64, Dc <= 512, Dc + Dr <= 640, or the matrix-core shape above
+ * (DSA_ERR_UNSUPPORTED otherwise); DSA_ERR_INVALID_ARG on NULL pointers or a bad sm_scale;
+ * DSA_ERR_WORKSPACE_TOO_SMALL.
  */
 dsa_status dsa_sparse_mla_backward(const dsa_shape* shape, dsa_dtype mla_dtype, const void* q, const void* kv,
                                    const int32_t* topk_indices, float sm_scale, const void* out,
-                                   const float* lse, const void* dout, float* dq, float* dkv, void* stream);
+                                   const float* lse, const void* dout, float* dq, float* dkv, void* workspace,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * Backward of the index score at the selected positions (training the indexer: a loss

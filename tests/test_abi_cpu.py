@@ -262,10 +262,19 @@ def test_backward_validation(L):
     shape = _shape(topk=8)
     # sparse MLA backward: bad scale, unsupported head count, NULL pointers
     f = L.dsa_sparse_mla_backward
-    args = lambda sh, sc=0.1, dq=FAKE: f(C.byref(sh), b.BF16, FAKE, FAKE, FAKE, sc, FAKE, FAKE, FAKE, dq, FAKE, None)
+    args = lambda sh, sc=0.1, dq=FAKE, ws=None, nws=0: f(C.byref(sh), b.BF16, FAKE, FAKE, FAKE, sc, FAKE, FAKE, FAKE,
+                                                         dq, FAKE, ws, nws, None)
     assert args(shape, sc=0.0) == 1
     assert args(shape, dq=None) == 1
-    assert args(_shape(topk=8, Hm=128)) == 2
+    assert args(_shape(topk=8, Hm=96)) == 2             # more than 64 heads, not in groups of 64
+    # the matrix-core shape (bf16, 512 + 64, heads in groups of 64) needs its workspace: D per
+    # (query, head), then P, dz' and dz' transposed per (query, slot rounded up to 64, head)
+    mma = _shape(B=2, T=3, topk=100, Hm=128, Dc=512, Dr=64, s_cap=1000)
+    need = L.dsa_workspace_bytes(C.byref(mma), b.OP_SPARSE_MLA_BWD)
+    assert need == 6 * 128 * 4 + 3 * (6 * 128 * 128 * 2)   # both multiples of 256; slots 100 -> 128
+    assert args(mma) == 5
+    assert args(mma, ws=FAKE, nws=need - 1) == 5
+    assert L.dsa_workspace_bytes(C.byref(_shape(topk=8)), b.OP_SPARSE_MLA_BWD) == 0   # vector kernel
     # index backward: unsupported heads, NULL pointers, fp8 without scales
     g = L.dsa_index_backward
     call = lambda sh, dt=b.BF16, qs=None, dI=FAKE: g(C.byref(sh), dt, FAKE, qs, FAKE, FAKE, FAKE, FAKE, dI, FAKE,

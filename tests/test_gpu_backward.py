@@ -54,7 +54,9 @@ def _run(q, kv, dout, idx, Dc, scale, dtype):
     b.sparse_mla_attention(qd, kvd, idd, scale, out, lse, Dc=Dc, workspace=ws)
     dq = torch.full((B, T, Hm, R), float("nan"), device="cuda")
     dkv = torch.full((B, S, R), float("nan"), device="cuda")   # the call must clear it
-    b.sparse_mla_backward(qd, kvd, idd, scale, out, lse, dd, dq, dkv, Dc=Dc)
+    nws = b.workspace_bytes(shape, b.OP_SPARSE_MLA_BWD)
+    bws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda") if nws else None  # stale contents
+    b.sparse_mla_backward(qd, kvd, idd, scale, out, lse, dd, dq, dkv, Dc=Dc, workspace=bws)
     torch.cuda.synchronize()
     return dq.cpu().numpy().astype(np.float64), dkv.cpu().numpy().astype(np.float64)
 
@@ -63,8 +65,16 @@ CASES = {
     # name: (B, T, S, Hm, Dc, Dr, k, dtype, tol)
     "fp32_small": (2, 5, 40, 8, 64, 16, 12, "f32", 1e-5),
     "fp32_odd_heads": (1, 4, 30, 3, 40, 8, 9, "f32", 1e-5),
+    # bf16 with 512 + 64 dims and heads in groups of 64: the matrix-core kernels
     "bf16_mla_dims": (1, 24, 300, 64, 512, 64, 64, "bf16", 2e-2),
     "bf16_decode": (3, 1, 5000, 64, 512, 64, 2048, "bf16", 2e-2),
+    # two head groups, a partial last tile (200 = 3 x 64 + 8 slots), 40 queries
+    "bf16_two_head_groups": (2, 20, 3000, 128, 512, 64, 200, "bf16", 2e-2),
+    # 512 query rows: each workgroup walks 2 tiles of its selection (with fewer rows the
+    # selection is split to one tile per workgroup)
+    "bf16_two_tiles_per_workgroup": (1, 512, 2000, 64, 512, 64, 256, "bf16", 2e-2),
+    # 32 heads: the vector kernel
+    "bf16_32_heads": (1, 8, 300, 32, 512, 64, 64, "bf16", 2e-2),
 }
 
 
@@ -85,12 +95,14 @@ def test_sparse_mla_backward_matches_oracle(name):
     assert np.all(dkv[untouched] == 0.0)     # rows nobody selected: exactly zero
 
 
-def test_sparse_mla_backward_empty_selections():
-    B, T, S, Hm, Dc, Dr = 1, 3, 16, 8, 64, 16
+@pytest.mark.parametrize("B,T,S,Hm,Dc,Dr,k,dtype", [(1, 3, 16, 8, 64, 16, 4, "f32"),
+                                                      (1, 3, 100, 64, 512, 64, 64, "bf16"),      # matrix cores
+                                                      (2, 1, 3000, 64, 512, 64, 2048, "bf16")])  # ... split
+def test_sparse_mla_backward_empty_selections(B, T, S, Hm, Dc, Dr, k, dtype):
     rng = np.random.default_rng(5)
-    q, kv, dout, idx, _ = _inputs(rng, B, T, S, Hm, Dc, Dr, 4, "f32")
+    q, kv, dout, idx, _ = _inputs(rng, B, T, S, Hm, Dc, Dr, k, dtype)
     idx[:] = -1
-    dq, dkv = _run(q, kv, dout, idx, Dc, 0.1, "f32")
+    dq, dkv = _run(q, kv, dout, idx, Dc, 0.1, dtype)
     assert np.all(dq == 0) and np.all(dkv == 0)
 
 
