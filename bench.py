@@ -547,6 +547,9 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
     bshape = B.make_shape(w.B, w.T, w.S, topk=w.topk, Hm=w.Hm, Dc=w.Dc, Dr=w.Dr)
     nbws = B.workspace_bytes(bshape, B.OP_SPARSE_MLA_BWD)
     bws = torch.empty((nbws,), dtype=torch.uint8, device="cuda") if nbws else None
+    ishape = B.make_shape(w.B, w.T, w.S, H=w.H, D=w.D, Hk=w.Hk, topk=w.topk)
+    niws = B.workspace_bytes(ishape, B.OP_INDEX_BWD)
+    iws = torch.empty((niws,), dtype=torch.uint8, device="cuda") if niws else None
 
     def call(ev=None):
         if ev:
@@ -556,7 +559,7 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
         if ev:
             ev[1].record(stream)
         B.index_backward(I["q"], I["k"], I["w"], idx, dI, dqi, dki, dwi, q_scale=I.get("q_scale"),
-                         k_scale=I.get("k_scale"), stream=stream)
+                         k_scale=I.get("k_scale"), workspace=iws, stream=stream)
         if ev:
             ev[2].record(stream)
 

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libdsa.so")
 # measurement kernels of the benchmark's calibration mode, a library of their own
 CALIB_LIB = os.path.join(PKG, "libdsa_calib.so")
 CALIB_SOURCES = ["calib.hip"]
-SOURCES = ["indexer.hip", "topk.hip", "indexer_topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip", "sparse_mla_bwd_mfma.hip", "indexer_bwd.hip", "prep.hip", "dsa_api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "indexer_topk.hip", "sparse_mla.hip", "sparse_mla_bwd.hip", "sparse_mla_bwd_mfma.hip", "indexer_bwd.hip", "indexer_bwd_dense.hip", "prep.hip", "dsa_api.cpp"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 FULL, SHARED = 0, 1
-OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP, OP_INDEXER_TOPK, OP_SPARSE_MLA_BWD = 0, 1, 2, 3, 4, 5
+OP_INDEXER, OP_TOPK, OP_SPARSE_MLA, OP_GROUP, OP_INDEXER_TOPK, OP_SPARSE_MLA_BWD, OP_INDEX_BWD = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_NO_DONOR",
           4: "DSA_ERR_STALE_CACHE", 5: "DSA_ERR_WORKSPACE_TOO_SMALL", 6: "DSA_ERR_HIP"}
 
@@ -80,7 +80,7 @@ _SIGS = {
                                           C.c_void_p, C.POINTER(GroupStats)]),
     "dsa_index_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
-                                     C.c_void_p]),
+                                     C.c_void_p, C.c_size_t, C.c_void_p]),
     "dsa_sparse_mla_backward": (C.c_int, [C.POINTER(Shape), C.c_int, C.c_void_p, C.c_void_p, C.c_void_p, C.c_float,
                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                           C.c_size_t, C.c_void_p]),
@@ -229,15 +229,19 @@ def sparse_mla_attention(q, kv, topk_indices, sm_scale, out, lse=None, *, Dc, wo
     return out
 
 
-def index_backward(q, k, w, topk_indices, dI, dq, dk, dw, *, q_scale=None, k_scale=None, stream=None):
+def index_backward(q, k, w, topk_indices, dI, dq, dk, dw, *, q_scale=None, k_scale=None, workspace=None,
+                   stream=None):
     """dsa_index_backward.  Index inputs as for indexer_scores, topk_indices and dI [B,T,topk];
-    dq [B,T,H,D], dk [B,S,Hk,D] and dw [B,T,H] fp32 are written in place."""
+    dq [B,T,H,D], dk [B,S,Hk,D] and dw [B,T,H] fp32 are written in place; workspace: uint8 tensor
+    of at least workspace_bytes(shape, OP_INDEX_BWD) bytes (None when that is 0)."""
     B, T, H, D = q.shape
     S, Hk = k.shape[1], k.shape[2]
     shape = make_shape(B, T, S, H=H, D=D, Hk=Hk, topk=topk_indices.shape[-1])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().dsa_index_backward(C.byref(shape), dtype_code(q), _dev_ptr(q), _dev_ptr(q_scale), _dev_ptr(k),
                                     _dev_ptr(k_scale), _dev_ptr(w), _dev_ptr(topk_indices), _dev_ptr(dI),
-                                    _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dw), _stream(stream)))
+                                    _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dw), _dev_ptr(workspace), ws_bytes,
+                                    _stream(stream)))
     return dq, dk, dw
 
 

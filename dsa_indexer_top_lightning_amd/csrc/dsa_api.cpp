@@ -116,6 +116,9 @@ size_t mla_ws(const dsa_shape* s, dsa_dtype dt) {
 size_t mla_bwd_ws(const dsa_shape* s, dsa_dtype dt) {
   return dsa::mla_bwd_workspace_bytes(s->B, s->T, s->Hm, s->Dc, s->Dr, s->topk, s->s_cap, (dsa::Dtype)dt);
 }
+size_t index_bwd_ws(const dsa_shape* s, dsa_dtype dt) {
+  return dsa::index_bwd_workspace_bytes(s->B, s->T, s->H, s->D, s->Hk, s->topk, s->s_cap, (dsa::Dtype)dt);
+}
 size_t scores_bytes(const dsa_shape* s) { return align_up((size_t)rows_of(s) * (size_t)s->s_cap * sizeof(float)); }
 
 // Full layers of a group over rows at least this long run the fused indexer -> top-k.
@@ -253,6 +256,7 @@ size_t dsa_workspace_bytes(const dsa_shape* s, dsa_op op) {
     }
     case DSA_OP_INDEXER_TOPK: return indexer_topk_ws(s, fused_any(s));
     case DSA_OP_SPARSE_MLA_BWD: return mla_bwd_ws(s, DSA_BF16);
+    case DSA_OP_INDEX_BWD: return std::max(index_bwd_ws(s, DSA_BF16), index_bwd_ws(s, DSA_FP8_E4M3));
   }
   return 0;
 }
@@ -343,7 +347,7 @@ dsa_status dsa_sparse_mla_backward(const dsa_shape* s, dsa_dtype dt, const void*
 
 dsa_status dsa_index_backward(const dsa_shape* s, dsa_dtype dt, const void* q, const float* qs, const void* k,
                               const float* ksc, const float* w, const int32_t* idx, const float* dI, float* dq,
-                              float* dk, float* dw, void* stream) {
+                              float* dk, float* dw, void* ws, size_t ws_bytes, void* stream) {
   dsa_status st = check_indexer_shape(s, dt);
   if (st == DSA_OK) st = check_topk_shape(s);
   if (st != DSA_OK) return st;
@@ -358,9 +362,12 @@ dsa_status dsa_index_backward(const dsa_shape* s, dsa_dtype dt, const void* q, c
     if (!k || !dk) return fail(DSA_ERR_INVALID_ARG, "k and dk must be non-NULL");
     if (dt == DSA_FP8_E4M3 && !ksc) return fail(DSA_ERR_INVALID_ARG, "fp8 inputs need q_scale and k_scale");
   }
+  const size_t need = index_bwd_ws(s, dt);
+  if (ws_bytes < need || (need && !ws))
+    return fail(DSA_ERR_WORKSPACE_TOO_SMALL, "index backward workspace %zu < %zu", ws_bytes, need);
   const dsa::IndexBwdParams p{s->B, s->T, s->H, s->D, s->Hk, s->topk, s->s_cap, q, qs, k, ksc, w, idx, dI,
                               dq, dk, dw};
-  hipError_t e = dsa::launch_index_bwd(p, (dsa::Dtype)dt, (hipStream_t)stream, nullptr);
+  hipError_t e = dsa::launch_index_bwd(p, (dsa::Dtype)dt, ws, ws_bytes, (hipStream_t)stream, nullptr);
   return e == hipSuccess ? DSA_OK : hip_fail(e, "index backward launch");
 }
 

@@ -147,7 +147,13 @@ hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws
 hipError_t launch_sparse_mla_bwd(const MlaBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
                                  int* n_launches);
 bool index_bwd_supported(int H, int D, int Hk);
-hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, hipStream_t st, int* n_launches);
+// dense-selection path of the index backward (matrix cores; needs a workspace)
+bool index_bwd_dense(int B, int T, int H, int D, int Hk, int topk, int64_t s_cap, Dtype dt);
+size_t index_bwd_workspace_bytes(int B, int T, int H, int D, int Hk, int topk, int64_t s_cap, Dtype dt);
+hipError_t launch_index_bwd_dense(const IndexBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                                  int* n_launches);
+hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                            int* n_launches);
 hipError_t launch_index_prep(const PrepParams& p, hipStream_t st);
 hipError_t launch_latent_append(const LatentAppendParams& p, hipStream_t st);
 

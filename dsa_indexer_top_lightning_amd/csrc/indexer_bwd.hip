@@ -156,7 +156,10 @@ bool index_bwd_supported(int H, int D, int Hk) {
   return H >= 1 && H <= IB_WAVES * IB_HPW && D >= 1 && D <= 64 * IB_DI && (Hk == H || Hk == 1);
 }
 
-hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, hipStream_t st, int* n_launches) {
+hipError_t launch_index_bwd(const IndexBwdParams& p, Dtype dt, void* ws, size_t ws_bytes, hipStream_t st,
+                            int* n_launches) {
+  if (index_bwd_dense(p.B, p.T, p.H, p.D, p.Hk, p.topk, p.s_cap, dt))
+    return launch_index_bwd_dense(p, dt, ws, ws_bytes, st, n_launches);
   const int64_t rows = (int64_t)p.B * p.T;
   int nsplit = 1;
   if (rows > 0 && rows < 1024) nsplit = (int)std::min<int64_t>(p.topk, (1024 + rows - 1) / rows);

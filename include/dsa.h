@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 typedef enum {
   DSA_OK = 0,
@@ -56,7 +56,8 @@ typedef enum {
   DSA_OP_SPARSE_MLA = 2,
   DSA_OP_GROUP = 3,
   DSA_OP_INDEXER_TOPK = 4,
-  DSA_OP_SPARSE_MLA_BWD = 5
+  DSA_OP_SPARSE_MLA_BWD = 5,
+  DSA_OP_INDEX_BWD = 6
 } dsa_op;
 
 /* Problem shape (host struct).  Fields a call does not use are ignored. */
@@ -337,15 +338,25 @@ dsa_status dsa_sparse_mla_backward(const dsa_shape* shape, dsa_dtype mla_dtype, 
  *   q, q_scale, k, k_scale, w: as for dsa_indexer_scores (shape->H, D, Hk, s_cap)
  *   topk_indices [B,T,topk] int32 (slots outside [0, s_cap) are ignored)
  *   dI  [B,T,topk] fp32, the gradient at each slot's position
- *   dq  [B,T,H,D] fp32, dk [B,S,Hk,D] fp32, dw [B,T,H] fp32, all overwritten (dk is zeroed
- *       by the call and collects contributions with fp32 atomics; for fewer than 1024
- *       query tokens dq and dw do too: reproducible to fp32 rounding only)
+ *   dq  [B,T,H,D] fp32, dk [B,S,Hk,D] fp32, dw [B,T,H] fp32, all overwritten.
+ *   workspace  ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_INDEX_BWD), device memory the
+ *       call may overwrite; may be NULL when that is 0.
+ * Two paths, chosen from the shape alone:
+ *   - dense selections (bf16 or fp8, D == 128, 8 * topk >= s_cap, B*T*s_cap*4 <= 4 GiB):
+ *     dI is scattered into a dense [B*T][s_cap] fp32 matrix in the workspace (slots naming
+ *     one key add up) and the sums over keys and queries run as matrix-core tile products
+ *     (G = dI w [s > 0] entering them as two bf16 terms, so fp32-level rounding); every row
+ *     of dq, dk and dw is written once, deterministically;
+ *   - otherwise (no workspace): dk is zeroed by the call and collects contributions with
+ *     fp32 atomics; for fewer than 1024 query tokens dq and dw do too (reproducible to
+ *     fp32 rounding only).
  * Requires H <= 64 (DSA_ERR_UNSUPPORTED otherwise) and the indexer's shape rules;
- * DSA_ERR_INVALID_ARG on NULL pointers.  No workspace.
+ * DSA_ERR_INVALID_ARG on NULL pointers; DSA_ERR_WORKSPACE_TOO_SMALL.
  */
 dsa_status dsa_index_backward(const dsa_shape* shape, dsa_dtype idx_dtype, const void* q, const float* q_scale,
                               const void* k, const float* k_scale, const float* w, const int32_t* topk_indices,
-                              const float* dI, float* dq, float* dk, float* dw, void* stream);
+                              const float* dI, float* dq, float* dk, float* dw, void* workspace,
+                              size_t ws_bytes, void* stream);
 
 /*
  * Decode-step preparation of new index vectors (the Megatron-Bridge pull request's

@@ -20,7 +20,7 @@ def test_library_exports_every_declared_symbol(L):
     assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
-    assert L.dsa_abi_version() == 3
+    assert L.dsa_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -277,11 +277,22 @@ def test_backward_validation(L):
     assert L.dsa_workspace_bytes(C.byref(_shape(topk=8)), b.OP_SPARSE_MLA_BWD) == 0   # vector kernel
     # index backward: unsupported heads, NULL pointers, fp8 without scales
     g = L.dsa_index_backward
-    call = lambda sh, dt=b.BF16, qs=None, dI=FAKE: g(C.byref(sh), dt, FAKE, qs, FAKE, FAKE, FAKE, FAKE, dI, FAKE,
-                                                       FAKE, FAKE, None)
+    call = lambda sh, dt=b.BF16, qs=None, dI=FAKE, ws=None, nws=0: g(C.byref(sh), dt, FAKE, qs, FAKE, FAKE, FAKE,
+                                                                     FAKE, dI, FAKE, FAKE, FAKE, ws, nws, None)
     assert call(shape, dI=None) == 1
     assert call(shape, dt=b.FP8_E4M3) == 1
     assert call(_shape(topk=8, H=128, Hk=128)) == 2
+    # dense selections (D = 128, 8 topk >= s_cap): the workspace holds dI as a [row][key] fp32
+    # matrix with rows of s_cap rounded up to 64 keys, then a byte per 64 x 64 block
+    dense = _shape(B=2, T=3, topk=100, H=8, D=128, Hk=8, s_cap=700)
+    need = L.dsa_workspace_bytes(C.byref(dense), b.OP_INDEX_BWD)
+    assert need == (6 * 704 * 4 + 255) // 256 * 256 + 256      # 2 x 1 x 11 = 22 occupancy bytes
+    assert call(dense) == 5
+    assert call(dense, ws=FAKE, nws=need - 1) == 5
+    assert L.dsa_workspace_bytes(C.byref(_shape(B=2, T=3, topk=100, H=8, D=128, Hk=8, s_cap=801)),
+                                 b.OP_INDEX_BWD) == 0         # 8 x 100 < 801: the sparse kernel
+    assert L.dsa_workspace_bytes(C.byref(_shape(B=2, T=3, topk=100, H=8, D=64, Hk=8, s_cap=700)),
+                                 b.OP_INDEX_BWD) == 0         # D != 128: the sparse kernel
 
 
 def _gpu_visible():

@@ -153,26 +153,38 @@ def _index_inputs(rng, B, T, S, H, D, Hk, k, dtype):
 
 
 INDEX_BWD_CASES = {
-    # name: (B, T, S, H, D, Hk, k, dtype)
-    "fp32_small": (2, 5, 60, 4, 32, 4, 10, "f32"),
-    "bf16_heads": (1, 6, 300, 32, 128, 32, 64, "bf16"),
-    "bf16_shared_key": (1, 6, 300, 32, 128, 1, 64, "bf16"),
-    "fp8_heads": (1, 5, 200, 32, 128, 32, 48, "fp8"),
-    "fp8_shared_key": (2, 3, 200, 32, 128, 1, 48, "fp8"),
-    "bf16_decode": (3, 1, 3000, 32, 128, 32, 2048, "bf16"),
+    # name: (B, T, S, H, D, Hk, k, dtype, dense): dense = the matrix-core path (bf16 / fp8,
+    # D = 128, 8 k >= S), else the vector kernel
+    "fp32_small": (2, 5, 60, 4, 32, 4, 10, "f32", False),
+    "bf16_heads": (1, 6, 300, 32, 128, 32, 64, "bf16", True),
+    "bf16_shared_key": (1, 6, 300, 32, 128, 1, 64, "bf16", True),
+    "fp8_heads": (1, 5, 200, 32, 128, 32, 48, "fp8", True),
+    "fp8_shared_key": (2, 3, 200, 32, 128, 1, 48, "fp8", True),
+    "bf16_decode": (3, 1, 3000, 32, 128, 32, 2048, "bf16", True),
+    # 300 queries = 2 full 128-query workgroups and a ragged one, 2000 keys = 31 key tiles
+    # and a 16-key tail, 512 slots per row
+    "bf16_dense_tiles": (1, 300, 2000, 32, 128, 32, 512, "bf16", True),
+    "fp8_dense_shared_key": (2, 130, 1000, 32, 128, 1, 256, "fp8", True),
+    # 8 x 64 < 5000 keys: the vector kernel
+    "bf16_sparse": (1, 4, 5000, 32, 128, 32, 64, "bf16", False),
+    "fp8_sparse_shared_key": (1, 3, 3000, 32, 128, 1, 96, "fp8", False),
 }
 
 
 @pytest.mark.parametrize("name", list(INDEX_BWD_CASES))
 def test_index_backward_matches_oracle(name):
-    B, T, S, H, D, Hk, k, dtype = INDEX_BWD_CASES[name]
+    B, T, S, H, D, Hk, k, dtype, dense = INDEX_BWD_CASES[name]
     rng = np.random.default_rng(200 + list(INDEX_BWD_CASES).index(name))
     (qd, kd, qsd, ksd), qh, kh, w, idx, dI = _index_inputs(rng, B, T, S, H, D, Hk, k, dtype)
     dq = torch.full((B, T, H, D), float("nan"), device="cuda")
     dk = torch.full((B, S, Hk, D), float("nan"), device="cuda")
     dw = torch.full((B, T, H), float("nan"), device="cuda")
+    shape = b.make_shape(B, T, S, H=H, D=D, Hk=Hk, topk=k)
+    nws = b.workspace_bytes(shape, b.OP_INDEX_BWD)
+    assert (nws > 0) == dense
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda") if nws else None  # stale contents
     b.index_backward(qd, kd, torch.from_numpy(w).cuda(), torch.from_numpy(idx).cuda(), torch.from_numpy(dI).cuda(),
-                     dq, dk, dw, q_scale=qsd, k_scale=ksd)
+                     dq, dk, dw, q_scale=qsd, k_scale=ksd, workspace=ws)
     torch.cuda.synchronize()
     rq, rk, rw = O.index_scores_backward_selected(qh, kh, w.astype(np.float64), idx, dI.astype(np.float64))
     for got, ref in ((dq, rq), (dk, rk), (dw, rw)):
