@@ -96,13 +96,16 @@ struct TrOff {
   }
 };
 
-// 8 bf16 at p[0..3] and p[8..11] (the two halves of a permuted fragment), 8-byte loads
-__device__ __forceinline__ bf16x8 ld_split8(const uint16_t* p) {
+// 8 bf16 at p[0..3] and p[8..11] (the two halves of a permuted fragment), 8-byte loads.
+// Kept as 32-bit words until the product: held as a bf16 vector, the fragment gets
+// element-wise no-op moves right after the loads, which make the wave wait for them (and
+// for everything issued before them) at once.
+__device__ __forceinline__ i32x4 ld_split8(const uint16_t* p) {
   const uint2 lo = *reinterpret_cast<const uint2*>(p);
   const uint2 hi = *reinterpret_cast<const uint2*>(p + 8);
-  const i32x4 v = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-  return __builtin_bit_cast(bf16x8, v);
+  return i32x4{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
 }
+__device__ __forceinline__ bf16x8 as_bf16(const i32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------- D = dout . o
 // grid = rows; wave w takes heads w, w + 4, ...; 8 values per lane
@@ -349,7 +352,7 @@ void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
   // A fragments of a tile (dz'^T and P^T, rows 32mb + lr, heads of k-step ks in the permuted
   // order): two 8-byte loads each from the [slot][head] arrays
   const int64_t hoff = hg * MHG + 4 * lg;
-  auto load_a = [&](int t, bf16x8 (&az)[2][4], bf16x8 (&ap)[2][4]) {
+  auto load_a = [&](int t, i32x4 (&az)[2][4], i32x4 (&ap)[2][4]) {
     const int64_t e0 = (int64_t)(t0 + t) * MT;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -360,7 +363,7 @@ void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
         ap[mb][ks] = ld_split8(w.p + o);
       }
   };
-  bf16x8 az0[2][4], ap0[2][4], az1[2][4], ap1[2][4];
+  i32x4 az0[2][4], ap0[2][4], az1[2][4], ap1[2][4];
   load_a(0, az0, ap0);
   wait_vmem();
   __syncthreads();  // the query and gradient copies are in LDS
@@ -368,8 +371,8 @@ void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
   float* dkv = p.dkv + b * s_cap * MROW;
   // one tile: its row indices into LDS, the next tile's A fragments requested, 68 products,
   // then the row gradients added to the latent rows
-  auto step = [&](int i, const bf16x8 (&az)[2][4], const bf16x8 (&ap)[2][4], bf16x8 (&nz)[2][4],
-                  bf16x8 (&np)[2][4]) {
+  auto step = [&](int i, const i32x4 (&az)[2][4], const i32x4 (&ap)[2][4], i32x4 (&nz)[2][4],
+                  i32x4 (&np)[2][4]) {
     if (tid < MT) {
       const int e = (t0 + i) * MT + tid;
       const int32_t v = e < topk ? gidx[e] : -1;
@@ -385,12 +388,12 @@ void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
         const bf16x8 bq = tr.read(qbuf, nb, rb), bg = tr.read(gbuf, nb, rb);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(az[mb][ks], bq, acc[4 * mb + j], 0, 0, 0);
-          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[mb][ks], bg, acc[4 * mb + j], 0, 0, 0);
+          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(az[mb][ks]), bq, acc[4 * mb + j], 0, 0, 0);
+          acc[4 * mb + j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(ap[mb][ks]), bg, acc[4 * mb + j], 0, 0, 0);
         }
       }
       const bf16x8 bq = tr.read(qbuf, rope_nb, rb);
-      acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(az[rope_mb][ks], bq, acc[8], 0, 0, 0);
+      acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(rope_mb ? az[1][ks] : az[0][ks]), bq, acc[8], 0, 0, 0);
     }
     lds_barrier();  // sidx of this tile is in place (no wait for the atomics or the prefetch)
     // accumulator (mb, nb) holds dim 32nb + lr of rows 32mb + 8(r/4) + 4lg + r%4
@@ -458,7 +461,7 @@ void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
       return gather_src(kvg, MRB, bm_valid(ent, s_cap) ? ent : 0, wave, lane);
     };
     // B fragments of a tile (dz'^T: heads 32hb + lr, slots of k-step ks in the permuted order)
-    auto load_b = [&](int t, bf16x8 (&bz)[2][4]) {
+    auto load_b = [&](int t, i32x4 (&bz)[2][4]) {
       const int64_t e0 = (int64_t)(t0 + t) * MT + 4 * lg;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -472,17 +475,30 @@ void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
     lds_barrier();
     gather_tile(tile_dst(0), tile_src(read_entry(0)));
     fetch_entries(2);
-    bf16x8 bz0[2][4], bz1[2][4];
+    // B fragments run two tiles ahead (a ring of three): they come from HBM, and waited for
+    // one tile ahead they held up every tile
+    i32x4 bz0[2][4], bz1[2][4], bz2[2][4];
     load_b(0, bz0);
+    if (ntiles > 1) load_b(1, bz1);
     const TrOff tr(lane);
-    // one tile: wait for its gather and B fragments, request the next tile's, 36 products
-    auto step = [&](int i, const bf16x8 (&bz)[2][4], bf16x8 (&nz)[2][4]) {
+    // one tile: wait for its gather and B fragments, request the next tile's gather and the B
+    // fragments of the tile after it, 36 products.  Loads complete in issue order; per lane a
+    // gather is 18 loads, an entry fetch 1, a fragment set 16.  Issued after tile i's
+    // gather: the entry fetch and, unless tile i is the last, the fragments of tile i + 1
+    // (for tile 0: its own fragments, then those of tile 1).
+    auto step = [&](int i, const i32x4 (&bz)[2][4], i32x4 (&nz)[2][4]) {
       const int bf = i & 1;
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // tile i and its B fragments landed
+      if (i == 0) {
+        if (ntiles > 1) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      } else {
+        if (i + 1 < ntiles) asm volatile("s_waitcnt vmcnt(17)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
+      }
       if (i + 1 < ntiles) {
         gather_tile(tile_dst(bf ^ 1), tile_src(read_entry(i + 1)));
         fetch_entries(i + 3);
-        load_b(i + 1, nz);
+        if (i + 2 < ntiles) load_b(i + 2, nz);
       }
       const unsigned char* tb = smem + bf * TILE_BYTES;
 #pragma unroll
@@ -491,16 +507,18 @@ void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x8 a = tr.read(tb, 4 * wv + j, rb);
-          acc[2 * j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[0][ks], acc[2 * j], 0, 0, 0);
-          acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[1][ks], acc[2 * j + 1], 0, 0, 0);
+          acc[2 * j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16(bz[0][ks]), acc[2 * j], 0, 0, 0);
+          acc[2 * j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16(bz[1][ks]), acc[2 * j + 1], 0, 0, 0);
         }
         const bf16x8 a = tr.read(tb, rope_nb, rb);
-        acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bz[rope_hb][ks], acc[8], 0, 0, 0);
+        // a select, not an index (rope_hb varies per wave: an index becomes indexed register moves)
+        acc[8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, as_bf16(rope_hb ? bz[1][ks] : bz[0][ks]), acc[8], 0, 0, 0);
       }
     };
-    for (int i = 0; i < ntiles; i += 2) {
-      step(i, bz0, bz1);
+    for (int i = 0; i < ntiles; i += 3) {
+      step(i, bz0, bz2);
       if (i + 1 < ntiles) step(i + 1, bz1, bz0);
+      if (i + 2 < ntiles) step(i + 2, bz2, bz1);
     }
   }
   // accumulator (nb, hb) holds, for head 32hb + lr, dims 32nb + 8(r/4) + 4lg + r%4
