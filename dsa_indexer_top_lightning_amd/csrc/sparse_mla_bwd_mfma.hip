@@ -226,11 +226,13 @@ void mla_bwd_pz(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
   uint32_t pp[8], pz[8];
   auto store_tile = [&](int t) {
     const int e0 = (t0 + t) * MT + 32 * vv;
+    if (w.p) {  // the [slot][head] arrays feed mla_bwd_dc only (the dense path recomputes P, dz')
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t e = e0 + 8 * (r >> 2) + 4 * lg + (r & 3);
-      wp[e * p.Hm] = (uint16_t)((r & 1) ? pp[r >> 1] >> 16 : pp[r >> 1]);
-      wz[e * p.Hm] = (uint16_t)((r & 1) ? pz[r >> 1] >> 16 : pz[r >> 1]);
+      for (int r = 0; r < 16; ++r) {
+        const int64_t e = e0 + 8 * (r >> 2) + 4 * lg + (r & 3);
+        wp[e * p.Hm] = (uint16_t)((r & 1) ? pp[r >> 1] >> 16 : pp[r >> 1]);
+        wz[e * p.Hm] = (uint16_t)((r & 1) ? pz[r >> 1] >> 16 : pz[r >> 1]);
+      }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(wzt + e0 + 8 * q + 4 * lg) = make_uint2(pz[2 * q], pz[2 * q + 1]);
@@ -416,6 +418,192 @@ void mla_bwd_dc(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
   }
 }
 
+// ---------------------------------------------------------------- dC, dense selections
+// When the selection covers a large share of the key range (8 topk >= s_cap), the latent-row
+// gradient is formed per latent row instead of per selected slot, with no atomics per slot:
+// a per-(query, row) multiplicity map (how many of the query's slots name the row) and a byte
+// per (query, 64-row tile) that holds any selection are scattered first; then a workgroup per
+// (64-row tile, chunk of DK_TC queries) keeps its rows as fragments in registers and walks
+// the chunk's queries that selected any of them:
+//   S = Q C^T, dP = dO V^T           (64 heads x 64 rows, the query's rows and gradients in LDS)
+//   P = m exp(z - lse), dz' = sm_scale P (dP - D)      (m: the row's multiplicity)
+//   dC += P^T [dO, 0] + dz'^T Q       (K = heads)
+// and adds its sums to the rows once at the end (one fp32 atomic per row value and chunk).
+struct BwDense {
+  int32_t* mult;  // [rows][ldm] multiplicity of each latent row in the query's selection
+  uint8_t* occ;   // [rows][nkt] any selected row in the 64-row tile
+  int64_t ldm;
+  int nkt;
+};
+constexpr int DK_TC = 256;                                   // queries per workgroup
+constexpr int DK_XB = 4 * 64 * 64;                           // P / dz' exchange: 64 bytes per lane
+constexpr int DK_LDS = TILE_BYTES + 8 * GROUP_BYTES + DK_XB + 2 * MHG * 4 + 256;  // + L2-request sink
+
+__global__ __launch_bounds__(256) void bm_dense_clear(int32_t* m, int64_t n, uint8_t* occ, int64_t nocc) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) m[i] = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nocc; i += stride) occ[i] = 0;
+}
+
+// one workgroup per query row
+__global__ __launch_bounds__(256) void bm_dense_scatter(MlaBwdParams p, BwDense d) {
+  const int64_t row = blockIdx.x;
+  const int32_t* idx = p.idx + row * p.topk;
+  for (int j = threadIdx.x; j < p.topk; j += 256) {
+    const int32_t e = idx[j];
+    if (!bm_valid(e, p.s_cap)) continue;
+    atomicAdd(d.mult + row * d.ldm + e, 1);
+    d.occ[row * d.nkt + e / MT] = 1;
+  }
+}
+
+// grid (nkt * nchunk, B).  Wave w: latent rows 32 (w & 1) .. of the tile as the S and dP
+// columns, heads 32 (w >> 1) .. as their rows; in the dC product rows 32 (w & 1) .. and dim
+// blocks [9 (w >> 1), +9).
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void mla_bwd_dkv(MlaBwdParams p, BwWs w, BwDense d, int nchunk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* qbuf = smem;
+  unsigned char* gbuf = smem + TILE_BYTES;
+  int32_t* xb = reinterpret_cast<int32_t*>(smem + TILE_BYTES + 8 * GROUP_BYTES);
+  float* lsev = reinterpret_cast<float*>(smem + TILE_BYTES + 8 * GROUP_BYTES + DK_XB);
+  float* dv = lsev + MHG;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lr = lane & 31, lg = lane >> 5, kb = wv & 1, hb = wv >> 1;
+  const int kx = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  const uint32_t sink = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(smem + DK_LDS - 256);
+  const int64_t b = blockIdx.y;
+  const int T = p.T, Hm = p.Hm;
+  const int64_t s_cap = p.s_cap;
+  const int64_t j0 = (int64_t)kx * MT;
+  const int tq0 = ch * DK_TC, tq1 = min(T, tq0 + DK_TC);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
+
+  // this wave's 32 latent rows: B fragments (dims 16 st + 8 lg .. +7 of row j0 + 32 kb + lr)
+  i32x4 cf[MROW / 16];
+  {
+    const int64_t jr = min<int64_t>(j0 + 32 * kb + lr, s_cap - 1);  // rows past s_cap: multiplicity 0
+    const unsigned char* crow = static_cast<const unsigned char*>(p.kv) + (b * s_cap + jr) * MRB;
+#pragma unroll
+    for (int st = 0; st < MROW / 16; ++st) cf[st] = *reinterpret_cast<const i32x4*>(crow + 32 * st + 16 * lg);
+  }
+  f32x16 acc[9];
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  const int nb0 = 9 * hb;
+  const float c1 = p.sm_scale * BM_LOG2E;
+  const TrOff tr(lane);
+  const int64_t jcol = j0 + 32 * kb + lr;
+  const int qr = 32 * hb + lr;  // head row of this lane's S and dP fragments
+
+  for (int t = tq0; t < tq1; ++t) {
+    const int64_t row = b * T + t;
+    if (!d.occ[row * d.nkt + kx]) continue;  // uniform
+    const float m = (float)d.mult[row * d.ldm + jcol];
+    for (int hg = 0; hg < Hm / MHG; ++hg) {
+      {
+        const unsigned char* qrows = static_cast<const unsigned char*>(p.q) + (row * Hm + hg * MHG) * MRB;
+        gather_tile(smem_lds + wv * (16 * SEG), gather_src(qrows, MRB, lane, wave, lane));
+        const unsigned char* grows = static_cast<const unsigned char*>(p.dout) + (row * Hm + hg * MHG) * (MDC * 2);
+        gather_tile<8>(smem_lds + TILE_BYTES + wv * (16 * SEG), gather_src(grows, MDC * 2, lane, wave, lane));
+        if (tid < MHG) {
+          lsev[tid] = p.lse[row * Hm + hg * MHG + tid] * BM_LOG2E;
+          dv[tid] = w.delta[row * Hm + hg * MHG + tid];
+        }
+      }
+      wait_vmem();
+      lds_barrier();
+      // L2 requests for the next query's rows (one 4-byte load per 128-byte line into a scratch
+      // word, 8.5 lines per lane); waited for only at the next gather, one query later
+      if (t + 1 < tq1) {
+        const int64_t nrow = row + 1;
+        const unsigned char* qn = static_cast<const unsigned char*>(p.q) + (nrow * Hm + hg * MHG) * MRB;
+        const unsigned char* gn = static_cast<const unsigned char*>(p.dout) + (nrow * Hm + hg * MHG) * (MDC * 2);
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+          const int ln = tid + 256 * u;  // line ln of Q's 576 (64 rows x 9), then dO's 512 (64 x 8)
+          if (ln < 576) dma4(qn + (ln / 9) * MRB + (ln % 9) * 128, sink);
+          else if (ln < 1088) dma4(gn + ((ln - 576) / 8) * (MDC * 2) + ((ln - 576) % 8) * 128, sink);
+        }
+      }
+      // S and dP: heads 32 hb + rows, this wave's latent rows as columns
+      f32x16 sz, gz;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sz[r] = 0.f;
+        gz[r] = 0.f;
+      }
+      {
+        const unsigned char* qt = qbuf + qr * SEG;
+        const unsigned char* gt = gbuf + qr * SEG;
+#pragma unroll
+        for (int st = 0; st < MROW / 16; ++st) {
+          const int o = (st >> 2) * GROUP_BYTES + 16 * ((2 * (st & 3) + lg) ^ perm(qr));
+          sz = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qt + o), as_bf16(cf[st]), sz, 0, 0, 0);
+          if (st < MDC / 16)
+            gz = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(gt + o), as_bf16(cf[st]), gz, 0, 0, 0);
+        }
+      }
+      // P and dz' of heads 32 hb + 16 c + {4 lg + e, 8 + 4 lg + e} (e = 0..3), this lane's row,
+      // as bf16 pairs: the A fragments (K = heads) of the dC product
+      {
+        uint32_t pw[8], zw[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float pv[2], zv[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int h = 32 * hb + 8 * ((r + u) >> 2) + 4 * lg + ((r + u) & 3);
+            const float P = m * __builtin_amdgcn_exp2f(fmaf(sz[r + u], c1, -lsev[h]));
+            pv[u] = P;
+            zv[u] = p.sm_scale * P * (gz[r + u] - dv[h]);
+          }
+          pw[r >> 1] = pack_bf16x2(pv[0], pv[1]);
+          zw[r >> 1] = pack_bf16x2(zv[0], zv[1]);
+        }
+        i32x4* mine = reinterpret_cast<i32x4*>(xb + (wv * 64 + lane) * 16);
+        mine[0] = i32x4{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]};
+        mine[1] = i32x4{(int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        mine[2] = i32x4{(int)zw[0], (int)zw[1], (int)zw[2], (int)zw[3]};
+        mine[3] = i32x4{(int)zw[4], (int)zw[5], (int)zw[6], (int)zw[7]};
+      }
+      lds_barrier();
+      // heads 16 ks .. +16 come from the wave with this kb and hb = ks / 2
+      i32x4 pf[4], zf[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const i32x4* src = reinterpret_cast<const i32x4*>(xb + ((2 * (ks >> 1) + kb) * 64 + lane) * 16);
+        pf[ks] = src[ks & 1];
+        zf[ks] = src[2 + (ks & 1)];
+      }
+      // dC: rows 32 kb + .., dims 32 nb + lr
+#pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        const int nb = nb0 + j;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int rb = 16 * ks;
+          if (nb < MDC / 32) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(pf[ks]), tr.read(gbuf, nb, rb), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16(zf[ks]), tr.read(qbuf, nb, rb), acc[j], 0, 0, 0);
+        }
+      }
+      lds_barrier();  // every wave is done with the buffers before the next gather
+    }
+  }
+  // accumulator j holds dims 32 (nb0 + j) + lr of rows 32 kb + 8 (r / 4) + 4 lg + r % 4
+  float* dkv = p.dkv + b * s_cap * MROW;
+#pragma unroll
+  for (int j = 0; j < 9; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t key = j0 + 32 * kb + 8 * (r >> 2) + 4 * lg + (r & 3);
+      if (key < s_cap && acc[j][r] != 0.f) unsafeAtomicAdd(dkv + key * MROW + 32 * (nb0 + j) + lr, acc[j][r]);
+    }
+}
+
 // ---------------------------------------------------------------- dq
 // Accumulators of wave w: dq^T blocks (dims 32nb, heads 32hb) for nb in [4w, 4w + 4), hb in
 // {0, 1}, and the rope block (nb = 16 + w / 2, hb = w & 1).
@@ -564,10 +752,24 @@ bool mla_bwd_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt) {
   return dt == BF16 && Dc == MDC && Dr == MROW - MDC && Hm % MHG == 0 && s_cap * (int64_t)MRB < (int64_t(1) << 32);
 }
 
+// Dense selections: the latent-row gradient per 64-row tile (mla_bwd_dkv) instead of per
+// selected slot (mla_bwd_dc).
+bool mla_bwd_dense(int B, int T, int topk, int64_t s_cap) {
+  if (B < 1 || T < 1 || s_cap < 1 || topk < 1) return false;
+  const int64_t ldm = (s_cap + MT - 1) / MT * MT;
+  return 8 * (int64_t)topk >= s_cap && (int64_t)B * T * ldm * 4 <= (int64_t(1) << 32);
+}
+
+// [delta][dz' slot-contiguous] then [P][dz'] (per-slot path) or [multiplicity][occupancy]
 size_t mla_bwd_workspace_bytes(int B, int T, int Hm, int Dc, int Dr, int topk, int64_t s_cap, Dtype dt) {
   if (!mla_bwd_uses_mfma(Hm, Dc, Dr, s_cap, dt)) return 0;
   const size_t rows = (size_t)B * T, Tp = (size_t)(topk + MT - 1) / MT * MT;
-  return bm_al(rows * Hm * 4) + 3 * bm_al(rows * Tp * Hm * 2);
+  const size_t head = bm_al(rows * Hm * 4) + bm_al(rows * Tp * Hm * 2);
+  if (mla_bwd_dense(B, T, topk, s_cap)) {
+    const size_t ldm = (size_t)((s_cap + MT - 1) / MT * MT), nkt = ldm / MT;
+    return head + bm_al(rows * ldm * 4) + bm_al(rows * nkt);
+  }
+  return head + 2 * bm_al(rows * Tp * Hm * 2);
 }
 
 hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws_bytes, hipStream_t st,
@@ -582,15 +784,26 @@ hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws
     if (n_launches) ++*n_launches;
   }
   if (rows == 0) return hipGetLastError();
+  const bool dense = mla_bwd_dense(p.B, p.T, p.topk, p.s_cap);
   char* base = static_cast<char*>(ws);
   BwWs w;
   w.delta = reinterpret_cast<float*>(base);
   base += bm_al((size_t)rows * p.Hm * 4);
   const size_t arr = bm_al((size_t)rows * Tp * p.Hm * 2);
-  w.p = reinterpret_cast<uint16_t*>(base);
-  w.dz = reinterpret_cast<uint16_t*>(base + arr);
-  w.dzt = reinterpret_cast<uint16_t*>(base + 2 * arr);
+  w.dzt = reinterpret_cast<uint16_t*>(base);
+  base += arr;
   w.Tp = Tp;
+  BwDense d{};
+  if (dense) {
+    w.p = w.dz = nullptr;
+    d.ldm = (p.s_cap + MT - 1) / MT * MT;
+    d.nkt = (int)(d.ldm / MT);
+    d.mult = reinterpret_cast<int32_t*>(base);
+    d.occ = reinterpret_cast<uint8_t*>(base + bm_al((size_t)rows * d.ldm * 4));
+  } else {
+    w.p = reinterpret_cast<uint16_t*>(base);
+    w.dz = reinterpret_cast<uint16_t*>(base + arr);
+  }
   const int groups = p.Hm / MHG;
   const BmPlan pl = bm_plan(rows, groups, p.topk);
   const int64_t nq = rows * p.Hm * MROW;
@@ -599,6 +812,13 @@ hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws
     if (n_launches) ++*n_launches;
   }
   hipLaunchKernelGGL(mla_bwd_delta, dim3((unsigned)rows), dim3(256), 0, st, p, w.delta);
+  if (dense) {
+    const int64_t nm = rows * d.ldm, nocc = rows * d.nkt;
+    hipLaunchKernelGGL(bm_dense_clear, dim3((unsigned)std::min<int64_t>((nm + 255) / 256, 8192)), dim3(256), 0, st,
+                       d.mult, nm, d.occ, nocc);
+    hipLaunchKernelGGL(bm_dense_scatter, dim3((unsigned)rows), dim3(256), 0, st, p, d);
+    if (n_launches) *n_launches += 2;
+  }
   const dim3 grid((unsigned)(rows * pl.nsplit), (unsigned)groups);
   hipError_t e;
   {
@@ -606,7 +826,13 @@ hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_pz), PZ_LDS, high)) != hipSuccess) return e;
     hipLaunchKernelGGL(mla_bwd_pz, grid, dim3(256), PZ_LDS, st, p, pl.nsplit, pl.tiles_per_split, w);
   }
-  {
+  if (dense) {
+    static std::atomic<size_t> high{0};
+    if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dkv), DK_LDS, high)) != hipSuccess) return e;
+    const int nchunk = (p.T + DK_TC - 1) / DK_TC;
+    hipLaunchKernelGGL(mla_bwd_dkv, dim3((unsigned)(d.nkt * nchunk), (unsigned)p.B), dim3(256), DK_LDS, st, p, w, d,
+                       nchunk);
+  } else {
     static std::atomic<size_t> high{0};
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dc), DC_LDS, high)) != hipSuccess) return e;
     hipLaunchKernelGGL(mla_bwd_dc, grid, dim3(256), DC_LDS, st, p, pl.nsplit, pl.tiles_per_split, w);

@@ -275,6 +275,11 @@ def test_backward_validation(L):
     assert args(mma) == 5
     assert args(mma, ws=FAKE, nws=need - 1) == 5
     assert L.dsa_workspace_bytes(C.byref(_shape(topk=8)), b.OP_SPARSE_MLA_BWD) == 0   # vector kernel
+    # dense selections (8 topk >= s_cap): D and dz' as before, then a multiplicity per (query,
+    # latent row) (rows of s_cap rounded up to 64) and a byte per (query, 64-row tile)
+    dn = _shape(B=2, T=3, topk=100, Hm=128, Dc=512, Dr=64, s_cap=700)
+    assert L.dsa_workspace_bytes(C.byref(dn), b.OP_SPARSE_MLA_BWD) == \
+        6 * 128 * 4 + 6 * 128 * 128 * 2 + 6 * 704 * 4 + 256
     # index backward: unsupported heads, NULL pointers, fp8 without scales
     g = L.dsa_index_backward
     call = lambda sh, dt=b.BF16, qs=None, dI=FAKE, ws=None, nws=0: g(C.byref(sh), dt, FAKE, qs, FAKE, FAKE, FAKE,

@@ -65,14 +65,17 @@ CASES = {
     # name: (B, T, S, Hm, Dc, Dr, k, dtype, tol)
     "fp32_small": (2, 5, 40, 8, 64, 16, 12, "f32", 1e-5),
     "fp32_odd_heads": (1, 4, 30, 3, 40, 8, 9, "f32", 1e-5),
-    # bf16 with 512 + 64 dims and heads in groups of 64: the matrix-core kernels
+    # bf16 with 512 + 64 dims and heads in groups of 64: the matrix-core kernels; with
+    # 8 k >= S the latent-row gradient is formed per 64-row tile (dense path), else per slot
     "bf16_mla_dims": (1, 24, 300, 64, 512, 64, 64, "bf16", 2e-2),
     "bf16_decode": (3, 1, 5000, 64, 512, 64, 2048, "bf16", 2e-2),
-    # two head groups, a partial last tile (200 = 3 x 64 + 8 slots), 40 queries
+    # per-slot path: two head groups, a partial last tile (200 = 3 x 64 + 8 slots), 40 queries
     "bf16_two_head_groups": (2, 20, 3000, 128, 512, 64, 200, "bf16", 2e-2),
     # 512 query rows: each workgroup walks 2 tiles of its selection (with fewer rows the
     # selection is split to one tile per workgroup)
     "bf16_two_tiles_per_workgroup": (1, 512, 2000, 64, 512, 64, 256, "bf16", 2e-2),
+    # dense path with two head groups, two 256-query chunks and a 1200-row tail tile
+    "bf16_dense_two_groups_chunks": (1, 300, 1200, 128, 512, 64, 256, "bf16", 2e-2),
     # 32 heads: the vector kernel
     "bf16_32_heads": (1, 8, 300, 32, 512, 64, 64, "bf16", 2e-2),
 }
