@@ -580,6 +580,11 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
     ach = flops / (t_mla * 1e-3) / 1e12
     iach = iflops / (t_idx * 1e-3) / 1e12
     dom_mla = t_mla >= t_idx
+    # the matrix-core paths (a workspace is asked for exactly when they run) against the bf16 MFMA
+    # peak, the vector kernels against the fp32 vector-ALU figure
+    mla_mfma, idx_mfma = nbws > 0, niws > 0
+    dom_mfma = mla_mfma if dom_mla else idx_mfma
+    dom_peak = PEAK_BF16_TFLOPS if dom_mfma else PEAK_VALU_F32_TFLOPS
     res = {
         "metric": "query tokens/s through one layer's backward (sparse MLA dq, dkv; index score dq, dk, dw)",
         "value": w.B * w.T / (elapsed / args.steps), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -590,11 +595,13 @@ def backward(args, w, inputs, dev, cache, torch, B, stream):
                    "prefix": w.S, "topk": w.topk, "index_heads": w.H, "index_dim": w.D, "index_key_heads": w.Hk,
                    "index_dtype": w.idx_dtype, "mla_heads": w.Hm, "latent": f"{w.Dc}+{w.Dr}",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": ach if dom_mla else iach, "peak": PEAK_VALU_F32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": (ach if dom_mla else iach) / PEAK_VALU_F32_TFLOPS, "traffic": None,
-                     "kernel": "mla_bwd" if dom_mla else "index_bwd",
+        "roofline": {"bound": "mfma" if dom_mfma else "alu", "achieved": ach if dom_mla else iach, "peak": dom_peak,
+                     "unit": "TFLOP/s", "frac": (ach if dom_mla else iach) / dom_peak, "traffic": None,
+                     "kernel": "sparse MLA backward" if dom_mla else "index-score backward",
                      "algorithmic_per_launch": flops if dom_mla else iflops},
-        "kernels": {"sparse_mla_bwd": {"ms": t_mla, "tflops": ach}, "index_bwd": {"ms": t_idx, "tflops": iach}},
+        "kernels": {"sparse_mla_bwd": {"ms": t_mla, "tflops": ach, "path": "matrix cores" if mla_mfma else "vector ALU"},
+                    "index_bwd": {"ms": t_idx, "tflops": iach,
+                                  "path": "matrix cores, dense selection" if idx_mfma else "vector ALU"}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
