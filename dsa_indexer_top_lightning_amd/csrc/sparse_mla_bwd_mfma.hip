@@ -435,7 +435,10 @@ struct BwDense {
   int64_t ldm;
   int nkt;
 };
-constexpr int DK_TC = 256;                                   // queries per workgroup
+// queries per workgroup: short chunks spread the causal triangle's uneven work over more
+// workgroups (4K prefill: 256 -> 32 queries, 10.4 -> 8.1 ms for the whole backward of the
+// attention), at the cost of more flushes of the row sums
+constexpr int DK_TC = 32;
 constexpr int DK_XB = 4 * 64 * 64;                           // P / dz' exchange: 64 bytes per lane
 constexpr int DK_LDS = TILE_BYTES + 8 * GROUP_BYTES + DK_XB + 2 * MHG * 4 + 256;  // + L2-request sink
 
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(256) void bm_dense_scatter(MlaBwdParams p, BwDense 
   }
 }
 
-// grid (nkt * nchunk, B).  Wave w: latent rows 32 (w & 1) .. of the tile as the S and dP
+// grid (nkt * nchunk, B), a tile's chunks consecutive.  Wave w: latent rows 32 (w & 1) .. of the tile as the S and dP
 // columns, heads 32 (w >> 1) .. as their rows; in the dC product rows 32 (w & 1) .. and dim
 // blocks [9 (w >> 1), +9).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))

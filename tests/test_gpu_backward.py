@@ -74,7 +74,8 @@ CASES = {
     # 512 query rows: each workgroup walks 2 tiles of its selection (with fewer rows the
     # selection is split to one tile per workgroup)
     "bf16_two_tiles_per_workgroup": (1, 512, 2000, 64, 512, 64, 256, "bf16", 2e-2),
-    # dense path with two head groups, two 256-query chunks and a 1200-row tail tile
+    # dense path with two head groups, 300 queries in 10 query chunks (the last one ragged) and a
+    # 1200-row tail tile
     "bf16_dense_two_groups_chunks": (1, 300, 1200, 128, 512, 64, 256, "bf16", 2e-2),
     # 32 heads: the vector kernel
     "bf16_32_heads": (1, 8, 300, 32, 512, 64, 64, "bf16", 2e-2),
