@@ -198,3 +198,97 @@ def test_index_backward_matches_oracle(name):
     for bb in range(B):
         sel[bb, idx[bb][idx[bb] >= 0]] = True
     assert np.all(dk.cpu().numpy()[~sel] == 0.0)     # keys nobody selected: exactly zero
+
+
+# ------------------------------------------------------------------ full size (4K prefill)
+
+def _prefill_selection(rng, T, k):
+    """The 4K prefill's selection structure: query t takes every key <= t while t + 1 <= k, then k of
+    its t + 1 keys; ascending, -1 padded."""
+    idx = np.full((1, T, k), -1, np.int32)
+    for t in range(T):
+        if t + 1 <= k:
+            idx[0, t, :t + 1] = np.arange(t + 1)
+        else:
+            idx[0, t] = np.sort(rng.choice(t + 1, size=k, replace=False))
+    return idx
+
+
+def _selecting(idx, j):
+    """Rows (queries) of batch item 0 whose selection names key j, and how many slots do."""
+    hits = (idx[0] == j).sum(axis=1)
+    return np.flatnonzero(hits), hits
+
+
+SAMPLED_QUERIES = [0, 1, 63, 64, 2046, 2047, 2048, 3001, 4095]
+SAMPLED_KEYS = [4090, 4032, 3990]   # selected by the last queries only: a few to a few dozen each
+
+
+def test_prefill4k_full_size_sparse_mla_backward_sampled():
+    # the shape bench.py --backward times on the 4K prefill: 4096 queries over 4096 keys, 64
+    # heads, 512 + 64 latent dims, topk 2048 (the dense latent-row path and the per-tile dq)
+    T, S, Hm, Dc, Dr, k = 4096, 4096, 64, 512, 64, 2048
+    R = Dc + Dr
+    rng = np.random.default_rng(4096)
+    idx = _prefill_selection(rng, T, k)
+    q = torch.from_numpy(rng.standard_normal((1, T, Hm, R), dtype=np.float32)).to(torch.bfloat16)
+    kv = torch.from_numpy(rng.standard_normal((1, S, R), dtype=np.float32)).to(torch.bfloat16)
+    dout = torch.from_numpy(rng.standard_normal((1, T, Hm, Dc), dtype=np.float32)).to(torch.bfloat16)
+    shape = b.make_shape(1, T, S, topk=k, Hm=Hm, Dc=Dc, Dr=Dr)
+    assert b.workspace_bytes(shape, b.OP_SPARSE_MLA_BWD) > 0
+    scale = float(np.float32(1.0 / np.sqrt(R)))
+    dq, dkv = _run(q, kv, dout, idx, Dc, scale, "bf16")
+    kvh = kv.to(torch.float64).numpy()[0]
+    qh = lambda t: q[0, t].to(torch.float64).numpy()
+    dh = lambda t: dout[0, t].to(torch.float64).numpy()
+    for t in SAMPLED_QUERIES:
+        rq, _, _ = O.sparse_mla_backward_row(qh(t), kvh, idx[0, t], scale, Dc, dh(t))
+        assert max_abs_rel(dq[0, t], rq) <= 2e-2, (t, max_abs_rel(dq[0, t], rq))
+    for j in SAMPLED_KEYS:
+        ts, _ = _selecting(idx, j)
+        ref = np.zeros(R)
+        for t in ts:
+            _, rows, dc = O.sparse_mla_backward_row(qh(t), kvh, idx[0, t], scale, Dc, dh(t))
+            ref += dc[rows == j].sum(axis=0)
+        assert len(ts) > 0
+        assert max_abs_rel(dkv[0, j], ref) <= 2e-2, (j, len(ts), max_abs_rel(dkv[0, j], ref))
+
+
+def test_prefill4k_full_size_index_backward_sampled():
+    # the 4K prefill's index heads: 32 per-head bf16 keys of 128 dims (the dense matrix-core path)
+    T, S, H, D, k = 4096, 4096, 32, 128, 2048
+    rng = np.random.default_rng(4097)
+    idx = _prefill_selection(rng, T, k)
+    q = torch.from_numpy(rng.standard_normal((1, T, H, D), dtype=np.float32)).to(torch.bfloat16)
+    kk = torch.from_numpy(rng.standard_normal((1, S, H, D), dtype=np.float32)).to(torch.bfloat16)
+    w = rng.random((1, T, H)).astype(np.float32)
+    dI = rng.standard_normal((1, T, k)).astype(np.float32)
+    qh, kh = q.to(torch.float64).numpy(), kk.to(torch.float64).numpy()
+    rows = sorted(set(SAMPLED_QUERIES) | {int(t) for j in SAMPLED_KEYS for t in _selecting(idx, j)[0]})
+    # slots of the checked rows whose score lies within rounding of the ReLU kink get no gradient
+    for t in rows:
+        sel = idx[0, t]
+        valid = sel >= 0
+        prod = qh[0, t][None, :, :] * kh[0, sel[valid]]            # [slots, H, D]
+        near = np.any(np.abs(prod.sum(axis=2)) <= 1e-4 * np.abs(prod).sum(axis=2), axis=1)
+        dI[0, t, np.flatnonzero(valid)[near]] = 0.0
+    shape = b.make_shape(1, T, S, H=H, D=D, Hk=H, topk=k)
+    nws = b.workspace_bytes(shape, b.OP_INDEX_BWD)
+    assert nws > 0
+    dq = torch.full((1, T, H, D), float("nan"), device="cuda")
+    dk = torch.full((1, S, H, D), float("nan"), device="cuda")
+    dw = torch.full((1, T, H), float("nan"), device="cuda")
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")
+    b.index_backward(q.cuda(), kk.cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(idx).cuda(),
+                     torch.from_numpy(dI).cuda(), dq, dk, dw, workspace=ws)
+    torch.cuda.synchronize()
+    dq, dk, dw = (x.cpu().numpy().astype(np.float64) for x in (dq, dk, dw))
+    r = np.asarray(rows)
+    rq, rk, rw = O.index_scores_backward_selected(qh[:, r], kh, w[:, r].astype(np.float64), idx[:, r],
+                                                  dI[:, r].astype(np.float64))
+    for i, t in enumerate(rows):
+        if t in SAMPLED_QUERIES:
+            assert max_abs_rel(dq[0, t], rq[0, i]) <= 1e-5, (t, max_abs_rel(dq[0, t], rq[0, i]))
+            assert max_abs_rel(dw[0, t], rw[0, i]) <= 1e-5, (t, max_abs_rel(dw[0, t], rw[0, i]))
+    for j in SAMPLED_KEYS:   # every query that names j is among the rows given to the oracle
+        assert max_abs_rel(dk[0, j], rk[0, j]) <= 1e-5, (j, max_abs_rel(dk[0, j], rk[0, j]))
