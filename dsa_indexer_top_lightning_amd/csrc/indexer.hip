@@ -655,7 +655,7 @@ constexpr int G8_DW = 4;                             // copy waves
 constexpr int G8_THREADS = 64 * (G8_CW + G8_DW);
 constexpr int G8_NST = 3;                            // tile stages in flight
 constexpr int G8_NV = 5;                             // per-row vector slots (heads h-1 .. h+3)
-constexpr int G8_PF = 6;                             // L2 requests run this many heads ahead
+constexpr int G8_PF = 3;                             // L2 requests run this many heads ahead
 constexpr int G8_QB = G8_BM * 128;                   // Q rows of one head
 constexpr int G8_STAGE = G8_QB + G8_BN * 128;        // + K rows: 48 KiB
 constexpr int G8_V_WQS = 0;                          // slot: per copy wave c, w then q scale of rows [32c, +32)
