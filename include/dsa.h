@@ -314,10 +314,15 @@ dsa_status dsa_group_stats_compute(const dsa_shape* shape, dsa_dtype idx_dtype,
  *   dkv [B,S,Dc+Dr] fp32, overwritten: zeroed by the call, then every selected row
  *       collects its contributions with fp32 atomics (their order is not fixed, so dkv
  *       is reproducible to fp32 rounding, not bit for bit)
- *   workspace  ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_SPARSE_MLA_BWD): nonzero only
- *       for bf16 with Dc = 512, Dr = 64 and Hm a multiple of 64, which runs on the matrix
- *       cores; the workspace then holds D per (query, head) and P and sm_scale dz per
- *       (query, selected slot, head) in bf16 (6 bytes per (query, slot, head))
+ *   workspace  ws_bytes >= dsa_workspace_bytes(shape, DSA_OP_SPARSE_MLA_BWD), device memory
+ *       the call may overwrite: nonzero only for bf16 with Dc = 512, Dr = 64 and Hm a
+ *       multiple of 64, which runs on the matrix cores.  It holds D per (query, head) and
+ *       sm_scale dz per (query, selected slot rounded up to 64, head) in bf16, then either
+ *       P and sm_scale dz once more per (query, slot, head) (the latent-row gradient formed
+ *       per selected slot), or, when 8 * topk >= s_cap (dense selections: the gradient
+ *       formed per 64-row tile of latent rows), an int32 multiplicity per (query, latent
+ *       row, s_cap rounded up to 64) and a byte per (query, 64-row tile).  Either way dkv
+ *       collects fp32 atomics.
  * Requires Hm <= 64, Dc <= 512, Dc + Dr <= 640, or the matrix-core shape above
  * (DSA_ERR_UNSUPPORTED otherwise); DSA_ERR_INVALID_ARG on NULL pointers or a bad sm_scale;
  * DSA_ERR_WORKSPACE_TOO_SMALL.
