@@ -5,15 +5,21 @@
 //   dz_j = P_j (dP_j - D),  D = dout . o                   dz'_j = sm_scale dz_j
 //   dq   = sum_j dz'_j c_j                                  dc_j += sum_h dz'_j q + [P_j dout, 0]
 //
-// as four launches, so that no kernel holds more than one head-major operand set:
+// as separate launches, so that no kernel holds more than one head-major operand set:
 //   mla_bwd_delta  D = dout . o per (query, head), fp32, into the workspace;
 //   mla_bwd_pz     per (query, split, head group): the forward's 64-row tiles gathered into
 //                  LDS; S^T = C Q^T and dP^T = C dO^T on v_mfma_f32_32x32x16_bf16 (query and
-//                  output-gradient fragments held in registers), then P and dz' as bf16 into
-//                  the workspace: [query][slot][head] and, for dq, [query][head][slot];
+//                  output-gradient fragments held in registers), then dz' as bf16 into the
+//                  workspace as [query][head][slot] for dq and, on the per-slot path, P and dz'
+//                  as [query][slot][head] for mla_bwd_dc;
+//   the latent-row gradient, one of:
 //   mla_bwd_dc     per (query, split, head group): the query's 64 head rows and output
 //                  gradients in LDS; per tile dC = dz'^T Q + P^T [dO, 0] (K = heads), added to
 //                  the selected latent rows with fp32 atomics;
+//   mla_bwd_dkv    dense selections (8 topk >= s_cap): per (64 latent rows, query chunk), S
+//                  and dP recomputed per query that selected any of the rows, dC summed over
+//                  the chunk in registers and added once (after bm_dense_clear and
+//                  bm_dense_scatter build the multiplicity map);
 //   mla_bwd_dq     per (query, split, head group): the tiles gathered again, dq^T += C^T dz'^T.
 // Slots past the last valid entry of a row are never touched; invalid slots inside that
 // range get P = dz' = 0, so the later kernels read whole tiles without masks.
