@@ -136,7 +136,9 @@ bool fused_shape(const dsa_shape* s, dsa_dtype dt) {
 }
 bool fused_any(const dsa_shape* s) { return fused_shape(s, DSA_BF16) || fused_shape(s, DSA_FP8_E4M3); }
 size_t indexer_topk_ws(const dsa_shape* s, bool fused) {
-  return dsa::indexer_topk_workspace_bytes(s->B, s->T, s->topk, s->s_cap, fused);
+  // the head-major vectors exist for fp8 only: sized for it whatever the call's dtype
+  const size_t vec = fused ? dsa::indexer_vectors_bytes(s->B, s->T, s->H, s->D, s->Hk, s->s_cap, dsa::FP8) : 0;
+  return dsa::indexer_topk_workspace_bytes(s->B, s->T, s->topk, s->s_cap, fused, vec);
 }
 // Inside a group only prefill chunks fuse (fp8 tile kernel, T >= 64): for decode rows the score
 // round trip is small beside the key stream and the fused passes cost more than it.

@@ -39,6 +39,13 @@ struct IndexerParams {
   int32_t* cand_pos = nullptr;
   float* cand_val = nullptr;
   int32_t cap = 0;
+  // Optional head-major copies of the per-head vectors (written by launch_indexer_vectors):
+  // ks_t [B][H][vec_s] = k_scale, wq_t [B][H][vec_t] = w * q_scale (one fp32 product), zero
+  // past s_cap and T.  With them the fp8 tile kernel loads a head's vectors of a tile as two
+  // contiguous runs instead of one 4-byte word per row and key.  Nullable.
+  const float* ks_t = nullptr;
+  const float* wq_t = nullptr;
+  int64_t vec_s = 0, vec_t = 0;
 };
 
 struct TopkParams {
@@ -122,14 +129,19 @@ hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int*
 // Whether the shape runs on a kernel with row masks, sampling and candidate mode (the fp8
 // tile kernel with one key head per query head, or the decode stream kernel).
 bool indexer_modes_supported(const IndexerParams& p, Dtype dt);
+// Bytes of the head-major vector copies for the shape (0 where the fp8 tile kernel does not
+// run it); launch_indexer_vectors writes them into `dst` and points p.ks_t / p.wq_t there.
+size_t indexer_vectors_bytes(int B, int T, int H, int D, int Hk, int64_t s_cap, Dtype dt);
+hipError_t launch_indexer_vectors(IndexerParams& p, Dtype dt, void* dst, hipStream_t st, int* n_launches);
 size_t topk_workspace_bytes(int B, int T, int topk, int64_t s_cap);
 hipError_t launch_topk(const TopkParams& p, void* ws, size_t ws_bytes, hipStream_t st, int* n_launches);
 // Fused indexer -> top-k.  Workspace: [rows * s_cap fp32 scores][top-k workspace], then,
-// when `fused`, the sample, threshold and candidate buffers.  The scores region is only
-// written for rows that fall back (or by the unfused path of shapes that cannot fuse).
+// when `fused`, the sample, threshold and candidate buffers and `vec_bytes` of head-major
+// vectors (indexer_vectors_bytes).  The scores region is only written for rows that fall
+// back (or by the unfused path of shapes that cannot fuse).
 bool indexer_topk_fused(const IndexerParams& p, Dtype dt, int topk);
 bool indexer_topk_stride_ok(int64_t stride);
-size_t indexer_topk_workspace_bytes(int B, int T, int topk, int64_t s_cap, bool fused);
+size_t indexer_topk_workspace_bytes(int B, int T, int topk, int64_t s_cap, bool fused, size_t vec_bytes);
 hipError_t launch_indexer_topk(const IndexerParams& p, Dtype dt, int topk, int64_t stride, int32_t* out, void* ws,
                                size_t ws_bytes, hipStream_t st, int* n_launches);
 bool mla_uses_mfma(int Hm, int Dc, int Dr, int64_t s_cap, Dtype dt);

@@ -697,6 +697,9 @@ struct G8Copy {
   const unsigned char* cbase[G8_CPW];  // source of copy i for head 0 (uniform)
   uint32_t coff[G8_CPW];               // per-lane byte offset from it
   uint32_t cdst[G8_CPW];               // LDS offset inside a stage (uniform)
+  bool tv;                             // head-major vectors (p.ks_t, p.wq_t) for this tile
+  const float* kvt;                    // head-major: k scale of key s0, head 0 (uniform)
+  const float* wvt;                    //             w * q scale of row t0, head 0 (uniform)
   const float* wqsrc;                  // this lane's w (lanes 0-31) or q scale (32-63) of head 0
   const float* kcbase;                 // k scale of key s0, head 0 (uniform)
   uint32_t kcoff;                      // this lane's byte offset from it
@@ -731,6 +734,9 @@ struct G8Copy {
       kcbase = p.k_scale + ((int64_t)b * S + s0) * H;
       kcoff = (uint32_t)(k * H * 4);
     }
+    tv = p.ks_t != nullptr && kst == 1;
+    kvt = tv ? p.ks_t + (int64_t)b * H * p.vec_s + s0 : nullptr;
+    wvt = tv ? p.wq_t + (int64_t)b * H * p.vec_t + t0 : nullptr;
     l2base = kg + ((int64_t)b * S + s0) * row_bytes;
 #pragma unroll
     for (int n = 0; n < G8_L2N; ++n) {
@@ -743,6 +749,19 @@ struct G8Copy {
 
   __device__ __forceinline__ void copy_vec(int h) {
     const uint32_t slot = smem_lds + G8_VBASE + (uint32_t)(h % G8_NV) * G8_VSLOT;
+    if (tv) {
+      // head-major: the tile's 256 key scales are 1 KiB in a row (copy wave 0, one 16-byte
+      // load per lane), its 128 row weights 512 B (copy wave 1, lanes 0-31); the vectors are
+      // padded to whole tiles, so neither reads past its head's run
+      if (c == 0) {
+        tile_dma16(kvt + (int64_t)h * p.vec_s, (uint32_t)lane * 16u, slot + G8_V_KC);
+        ++issued;
+      } else if (c == 1) {
+        if (lane < 32) tile_dma16(wvt + (int64_t)h * p.vec_t, (uint32_t)lane * 16u, slot + G8_V_WQ);
+        ++issued;
+      }
+      return;
+    }
     tile_dma4(wqsrc + h, slot + G8_V_WQS + 256 * c);
     tile_dma4_off(kcbase + h, kcoff, slot + G8_V_KC + 256 * c);
     issued += G8_VPW;
@@ -767,6 +786,7 @@ struct G8Copy {
   }
   // w * q scale of head h for rows [32c, +32) (this wave loaded both)
   __device__ __forceinline__ void prep(int h) const {
+    if (tv) return;  // the product came with the vectors
     float* v = reinterpret_cast<float*>(smem + G8_VBASE + (h % G8_NV) * G8_VSLOT);
     if (lane < 32) v[G8_V_WQ / 4 + 32 * c + lane] = v[G8_V_WQS / 4 + 64 * c + lane] * v[G8_V_WQS / 4 + 64 * c + 32 + lane];
   }
@@ -779,8 +799,10 @@ struct G8Copy {
       if (h + 1 < H) copy_vec(h + 1);
       copy_tiles(h);
     }
-    g8_wait_loads(issued - G8_VPW);  // head 0's vectors
-    prep(0);
+    if (!tv) {
+      g8_wait_loads(issued - G8_VPW);  // head 0's vectors
+      prep(0);
+    }
     if (lead)
       for (int h = 2; h < min(G8_PF, H); ++h) l2_request(h);
     for (int h = 0; h < H; ++h) {
@@ -1002,6 +1024,12 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
       }
     uint32_t base = 0u;
     if (mycnt) base = (uint32_t)atomicAdd(p.cand_cnt + (int64_t)b * T + t0 + own + lane, (int32_t)mycnt);
+    // The atomics' results, copied once into a plain register: read straight from the
+    // atomics' destination, every read below would first wait for every global access
+    // before it, the candidate stores of the earlier rows included (one counter for loads,
+    // stores and atomics, completed in order).
+    uint32_t slots;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(slots) : "v"(base));
     const uint64_t half = w.lg ? ~0xffffffffull : 0xffffffffull;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1011,7 +1039,8 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
         const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
         if ((m0 | m1) == 0) continue;
         const int l0 = 32 * i + 8 * (r >> 2) + (r & 3);
-        const uint32_t rb = w.lg ? __builtin_amdgcn_readlane(base, l0 + 4) : __builtin_amdgcn_readlane(base, l0);
+        const uint32_t rb0 = __builtin_amdgcn_readlane(slots, l0), rb1 = __builtin_amdgcn_readlane(slots, l0 + 4);
+        const uint32_t rb = w.lg ? rb1 : rb0;
         const uint32_t c0 = (uint32_t)__popcll(m0 & half);
         const int64_t row = (int64_t)b * T + t0 + own + l0 + 4 * w.lg;
         int32_t* pos = p.cand_pos + row * p.cap;
@@ -1087,6 +1116,36 @@ void indexer_fp8_groups(IndexerParams p, int nq, int nk, int xcd_order) {
   }
 }
 #pragma clang diagnostic pop
+
+// Head-major copies of the fp8 tile kernel's per-head vectors: ks_t[b][h][s] = k_scale[b][s][h]
+// and wq_t[b][h][t] = w[b][t][h] * q_scale[b][t][h] (the product the kernel forms otherwise),
+// zero in the padding past s_cap and T.  Block x < nks transposes keys [64x, +64) of batch item
+// y, the others rows [64 (x - nks), +64), through an LDS tile (H <= 128).
+constexpr int GV_N = 64;
+__global__ __launch_bounds__(256) void g8_vectors(IndexerParams p, float* ks_t, float* wq_t, int nks) {
+  __shared__ float tile[GV_N][129];
+  const int b = blockIdx.y, H = p.H, tid = threadIdx.x;
+  const bool keys = (int)blockIdx.x < nks;
+  const int64_t n = keys ? p.s_cap : p.T;       // valid columns
+  const int64_t ld = keys ? p.vec_s : p.vec_t;  // padded columns
+  const int64_t c0 = (int64_t)(keys ? blockIdx.x : blockIdx.x - nks) * GV_N;
+  for (int i = tid; i < GV_N * H; i += 256) {
+    const int r = i / H, h = i % H;
+    const int64_t c = c0 + r;
+    float v = 0.f;
+    if (c < n) {
+      const int64_t o = ((int64_t)b * n + c) * H + h;
+      v = keys ? p.k_scale[o] : p.w[o] * p.q_scale[o];
+    }
+    tile[r][h] = v;
+  }
+  __syncthreads();
+  float* dst = keys ? ks_t : wq_t;
+  for (int i = tid; i < GV_N * H; i += 256) {
+    const int h = i / GV_N, r = i % GV_N;
+    if (c0 + r < ld) dst[((int64_t)b * H + h) * ld + c0 + r] = tile[r][h];
+  }
+}
 
 // ----------------------------------------------------------------- decode streaming kernel
 // Few queries per batch item (decode): the work is one pass over the item's index
@@ -1239,6 +1298,33 @@ bool stream_path(const IndexerParams& p, Dtype dt) {
 }  // namespace
 
 bool indexer_modes_supported(const IndexerParams& p, Dtype dt) { return g8_path(p, dt) || stream_path(p, dt); }
+
+namespace {
+int64_t vec_cols_s(int64_t s_cap) { return (s_cap + G8_BN - 1) / G8_BN * G8_BN; }
+int64_t vec_cols_t(int64_t T) { return (T + G8_BM - 1) / G8_BM * G8_BM; }
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t indexer_vectors_bytes(int B, int T, int H, int D, int Hk, int64_t s_cap, Dtype dt) {
+  IndexerParams p{};
+  p.B = B; p.T = T; p.H = H; p.D = D; p.Hk = Hk; p.s_cap = s_cap; p.kstride = 1;
+  if (!g8_path(p, dt) || H > 128 || s_cap == 0) return 0;
+  return al256((size_t)B * H * vec_cols_s(s_cap) * 4) + al256((size_t)B * H * vec_cols_t(T) * 4);
+}
+
+hipError_t launch_indexer_vectors(IndexerParams& p, Dtype dt, void* dst, hipStream_t st, int* n_launches) {
+  if (!dst || indexer_vectors_bytes(p.B, p.T, p.H, p.D, p.Hk, p.s_cap, dt) == 0) return hipSuccess;
+  p.vec_s = vec_cols_s(p.s_cap);
+  p.vec_t = vec_cols_t(p.T);
+  float* ks = static_cast<float*>(dst);
+  float* wq = reinterpret_cast<float*>(static_cast<char*>(dst) + al256((size_t)p.B * p.H * p.vec_s * 4));
+  const int nks = (int)(p.vec_s / GV_N), nts = (int)(p.vec_t / GV_N);
+  hipLaunchKernelGGL(g8_vectors, dim3((unsigned)(nks + nts), (unsigned)p.B), dim3(256), 0, st, p, ks, wq, nks);
+  if (n_launches) ++*n_launches;
+  p.ks_t = ks;
+  p.wq_t = wq;
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer(const IndexerParams& p, Dtype dt, hipStream_t st, int* n_launches) {
   if ((int64_t)p.B * p.T == 0 || p.s_cap == 0) return hipSuccess;

@@ -310,10 +310,10 @@ constexpr int64_t FU_DEFAULT_STRIDE = 64;
 size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 struct Layout {
-  size_t scores, topk_ws, samples, lkey, live, fb, cnt, pos, val, end;
+  size_t scores, topk_ws, samples, lkey, live, fb, cnt, pos, val, vec, end;
 };
 
-Layout layout(int B, int T, int topk, int64_t s_cap) {
+Layout layout(int B, int T, int topk, int64_t s_cap, size_t vec_bytes) {
   const size_t rows = (size_t)B * T;
   Layout L;
   L.scores = 0;
@@ -325,7 +325,8 @@ Layout layout(int B, int T, int topk, int64_t s_cap) {
   L.cnt = L.fb + al(rows * 4);
   L.pos = L.cnt + al(rows * 4);
   L.val = L.pos + al(rows * (size_t)FU_CAP * 4);
-  L.end = L.val + al(rows * (size_t)FU_CAP * 4);
+  L.vec = L.val + al(rows * (size_t)FU_CAP * 4);
+  L.end = L.vec + al(vec_bytes);
   return L;
 }
 
@@ -341,8 +342,8 @@ bool indexer_topk_fused(const IndexerParams& p, Dtype dt, int topk) {
   return indexer_modes_supported(p, dt) && indexer_modes_supported(ps, dt);
 }
 
-size_t indexer_topk_workspace_bytes(int B, int T, int topk, int64_t s_cap, bool fused) {
-  const Layout L = layout(B, T, topk, s_cap);
+size_t indexer_topk_workspace_bytes(int B, int T, int topk, int64_t s_cap, bool fused, size_t vec_bytes) {
+  const Layout L = layout(B, T, topk, s_cap, vec_bytes);
   return fused ? L.end : L.samples;
 }
 
@@ -351,7 +352,8 @@ hipError_t launch_indexer_topk(const IndexerParams& p, Dtype dt, int topk, int64
   const int64_t rows = (int64_t)p.B * p.T;
   if (rows == 0) return hipSuccess;
   const bool fused = indexer_topk_fused(p, dt, topk) && p.s_cap > 0;
-  const Layout L = layout(p.B, p.T, topk, p.s_cap);
+  const size_t vec_bytes = fused ? indexer_vectors_bytes(p.B, p.T, p.H, p.D, p.Hk, p.s_cap, dt) : 0;
+  const Layout L = layout(p.B, p.T, topk, p.s_cap, vec_bytes);
   const size_t need = fused ? L.end : L.samples;
   if (ws_bytes < need || (need && !ws)) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -398,8 +400,10 @@ hipError_t launch_indexer_topk(const IndexerParams& p, Dtype dt, int topk, int64
   // 2. thresholds (and cleared counts)
   hipLaunchKernelGGL(fused_threshold, dim3((unsigned)rows), dim3(TH_THREADS), 0, st, a);
   if (n_launches) ++*n_launches;
-  // 3. candidates
-  IndexerParams pc = p;
+  // 3. candidates (head-major vectors first, where the kernel takes them)
+  IndexerParams pv = p;
+  if ((e = launch_indexer_vectors(pv, dt, vec_bytes ? base + L.vec : nullptr, st, n_launches)) != hipSuccess) return e;
+  IndexerParams pc = pv;
   pc.scores = nullptr;
   pc.ld = 0;
   pc.row_mask = a.live;
@@ -419,7 +423,7 @@ hipError_t launch_indexer_topk(const IndexerParams& p, Dtype dt, int topk, int64
   }
   if (n_launches) ++*n_launches;
   // 5. fall-back rows: full score rows, plain select
-  IndexerParams pf = p;
+  IndexerParams pf = pv;
   pf.scores = scores;
   pf.ld = p.s_cap;
   pf.row_mask = a.fb;

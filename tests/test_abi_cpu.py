@@ -177,10 +177,11 @@ def test_indexer_topk_errors(L):
 def test_indexer_topk_workspace_layout(L):
     # a 4096-query chunk over a 131072-key prefix (fp8 and one key head per query head can fuse):
     # score buffer for fall-back rows, no top-k histograms (many rows), samples sized for
-    # stride 16, four per-row words, 12288 candidate positions and values per row
+    # stride 16, four per-row words, 12288 candidate positions and values per row, then the
+    # head-major key scales [32][S] and row weights [32][rows] of the fp8 tile kernel
     rows, S = 4096, 131072
     s = _shape(B=1, T=rows, s_cap=S, H=32, D=128, Hk=32, topk=2048, Hm=64, Dc=512, Dr=64)
-    want = rows * S * 4 + rows * (S // 16) * 4 + 4 * rows * 4 + 2 * rows * 12288 * 4
+    want = rows * S * 4 + rows * (S // 16) * 4 + 4 * rows * 4 + 2 * rows * 12288 * 4 + 32 * S * 4 + 32 * rows * 4
     assert L.dsa_workspace_bytes(C.byref(s), b.OP_INDEXER_TOPK) == want
     # a group over rows this long runs the fused call in the same workspace
     assert L.dsa_workspace_bytes(C.byref(s), b.OP_GROUP) >= want
