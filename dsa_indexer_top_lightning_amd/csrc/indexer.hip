@@ -1031,6 +1031,11 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
     uint32_t slots;
     asm volatile("v_mov_b32 %0, %1" : "=v"(slots) : "v"(base));
     const uint64_t half = w.lg ? ~0xffffffffull : 0xffffffffull;
+    // the lists of the tile's rows from one uniform base: a cell goes to byte 4 (row * cap + slot)
+    // (row in the tile < 128, slot < cap: fits 32 bits), no 64-bit arithmetic per row
+    unsigned char* lpos = reinterpret_cast<unsigned char*>(p.cand_pos + ((int64_t)b * T + t0) * p.cap);
+    unsigned char* lval = reinterpret_cast<unsigned char*>(p.cand_val + ((int64_t)b * T + t0) * p.cap);
+    const uint32_t cap = (uint32_t)p.cap, lrow = (uint32_t)(own + 4 * w.lg) * cap;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1042,18 +1047,17 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
         const uint32_t rb0 = __builtin_amdgcn_readlane(slots, l0), rb1 = __builtin_amdgcn_readlane(slots, l0 + 4);
         const uint32_t rb = w.lg ? rb1 : rb0;
         const uint32_t c0 = (uint32_t)__popcll(m0 & half);
-        const int64_t row = (int64_t)b * T + t0 + own + l0 + 4 * w.lg;
-        int32_t* pos = p.cand_pos + row * p.cap;
-        float* val = p.cand_val + row * p.cap;
+        const uint32_t roff = lrow + (uint32_t)l0 * cap;  // the cells' row (own + l0 + 4 lg) times cap
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (!(j ? k1 : k0)) continue;
           const uint64_t mj = (j ? m1 : m0) & half;
           const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mj >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mj, 0u));
           const uint32_t slot = rb + (j ? c0 : 0u) + below;
-          if (slot < (uint32_t)p.cap) {
-            pos[slot] = (int32_t)(s0 + 64 * w.wn + 32 * j + w.lr);
-            val[slot] = w.tot[i][j][r] * up;
+          if (slot < cap) {
+            const uint32_t at = (roff + slot) * 4u;
+            *reinterpret_cast<int32_t*>(lpos + at) = (int32_t)(s0 + 64 * w.wn + 32 * j + w.lr);
+            *reinterpret_cast<float*>(lval + at) = w.tot[i][j][r] * up;
           }
         }
       }
