@@ -164,6 +164,24 @@ def test_decode_stream(dt):
         check_topk_row(got[key], r, sc, int(ks[key]), tau)
 
 
+def test_prefill_fp8_two_batch_items_ragged_ranges():
+    # two batch items, 200 queries (a ragged second query tile), 6000 keys (a ragged last key
+    # tile): the head-major key scales and row weights are laid out per batch item and padded to
+    # whole tiles; item 1 gets windows that start past 0 and rows whose range ends in the second
+    # key tile
+    w = PREFILL.with_(name="chunk6k_fp8_b2", B=2, T=200, S=6000, pos0=5800, topk=256)
+    L = _inputs(w)
+    ks, ke = _ranges(w)
+    ks[1, :50] = 1000 + 7 * np.arange(50)
+    ks[1, 150:] = 4400
+    ke[1, 120:130] = 300
+    ref, got, fell = _run(w, _upload(w, L), ks, ke)
+    _same(ref, got, "two batch items")
+    assert not fell.any(), f"{int(fell.sum())} rows fell back"
+    for key, sc, (r, tau) in _oracle_rows(w, L, ks, ke, [(0, 0), (0, 199), (1, 0), (1, 125), (1, 199)]):
+        check_topk_row(got[key], r, sc, int(ks[key]), tau)
+
+
 @pytest.mark.parametrize("name", ["chunk128k_fp8", "decode1m_b4_fp8"])
 def test_full_size_every_row(name):
     w = synth.WORKLOADS[name]
