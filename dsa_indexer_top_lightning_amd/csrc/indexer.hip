@@ -668,6 +668,7 @@ constexpr int G8_LDS = G8_SINK + 256;
 constexpr int G8_CPW = (G8_BM + G8_BN) / 8 / G8_DW;  // 1 KiB tile copies per copy wave per stage (12)
 constexpr int G8_VPW = 2;                            // per-row vector loads per copy wave per head
 constexpr int G8_L2N = 2;                            // L2 requests per copy wave per head (lead)
+constexpr int G8_KMAX_LOADS = 12;                    // key-scale loads in flight per thread (tile maximum)
 static_assert(G8_CPW * 8 * G8_DW == G8_BM + G8_BN, "tile copies must split evenly over the copy waves");
 static_assert(G8_DW * G8_L2N * 64 * 64 == G8_BN * 128, "L2 requests cover the key rows in 64 B steps");
 
@@ -950,11 +951,20 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
   {
     const float* ksrc = p.k_scale + ((int64_t)b * S + s0) * p.H;
     const int ncol = (int)min<int64_t>(G8_BN, (S - s0 + kst - 1) / kst);  // columns inside the prefix
+    // (every load of a round is issued before any is waited for: one loop step per load made
+    // each wait for the one before, a dozen global round trips per tile)
     float m = 0.f;
-    if (MODE != G8_SAMPLES)
-      for (int i = tid; i < ncol * p.H; i += G8_THREADS) m = fmaxf(m, ksrc[i]);
-    else
-      for (int i = tid; i < ncol * p.H; i += G8_THREADS) m = fmaxf(m, ksrc[(i / p.H) * kst * p.H + i % p.H]);
+    const int n = ncol * p.H;
+    for (int i0 = tid; i0 < n; i0 += G8_KMAX_LOADS * G8_THREADS) {
+      float v[G8_KMAX_LOADS];
+#pragma unroll
+      for (int u = 0; u < G8_KMAX_LOADS; ++u) {
+        const int i = i0 + u * G8_THREADS;
+        v[u] = i < n ? (MODE != G8_SAMPLES ? ksrc[i] : ksrc[(i / p.H) * kst * p.H + i % p.H]) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < G8_KMAX_LOADS; ++u) m = fmaxf(m, v[u]);
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     if (lane == 0) sh.wmax[wave] = m;
