@@ -132,7 +132,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows(TopkParams p) {
   const float* src = p.scores + row * p.ld + ks;
   const SelectLds L{hist, wcnt, sh};
   if constexpr (CACHE) {
-    for (int64_t i = tid; i < n; i += TK_THREADS) kcache[i] = order_key(src[i]);
+    // eight loads per thread in flight before any is waited for
+    for (int64_t i0 = tid; i0 < n; i0 += 8 * TK_THREADS) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = i0 + u * TK_THREADS < n ? src[i0 + u * TK_THREADS] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u * TK_THREADS < n) kcache[i0 + u * TK_THREADS] = order_key(v[u]);
+    }
     __syncthreads();
     finish_select([&](int64_t i) { return kcache[i]; }, n, ks, K, out, 0, 0u, 0u, (uint32_t)K, L);
   } else {
@@ -388,14 +396,11 @@ struct SplitArgs {
 // Finds, in the summed histogram gh of one digit, the digit value d that holds the
 // rem-th largest candidate and the rank of that candidate among the keys with digit
 // d.  Thread t owns bins 8t..8t+7; suffix sums over threads locate the owner.
-__device__ void sp_scan(const uint32_t* gh, uint32_t& rem, uint32_t& digit, uint32_t* sh) {
+__device__ void sp_scan(const uint32_t (&h)[8], uint32_t& rem, uint32_t& digit, uint32_t* sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t h[8], c = 0;
+  uint32_t c = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = gh[8 * tid + i];
-    c += h[i];
-  }
+  for (int i = 0; i < 8; ++i) c += h[i];
   uint32_t x = c;  // suffix sum inside the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -422,19 +427,31 @@ __device__ void sp_scan(const uint32_t* gh, uint32_t& rem, uint32_t& digit, uint
   __syncthreads();
 }
 
-// prefix / mask of the digits fixed by the first `passes` finished histograms
-__device__ void sp_prefix(const uint32_t* gh, int passes, uint32_t K, uint32_t& prefix, uint32_t& pmask,
-                          uint32_t& rem, uint32_t* sh) {
+// prefix / mask of the digits fixed by the first PASSES finished histograms (the bins of
+// every pass are loaded at once; the scans then run one after another)
+template <int PASSES>
+__device__ void sp_prefix(const uint32_t* gh, uint32_t K, uint32_t& prefix, uint32_t& pmask, uint32_t& rem,
+                          uint32_t* sh) {
   prefix = 0;
   pmask = 0;
   rem = K;
-  for (int q = 0; q < passes; ++q) {
-    uint32_t d;
-    sp_scan(gh + q * SP_BINS, rem, d, sh);
-    prefix |= d << sp_shift(q);
-    pmask |= sp_mask(q) << sp_shift(q);
+  if constexpr (PASSES > 0) {
+    uint32_t h[PASSES][8];
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[q][i] = gh[q * SP_BINS + 8 * threadIdx.x + i];
+#pragma unroll
+    for (int q = 0; q < PASSES; ++q) {
+      uint32_t d;
+      sp_scan(h[q], rem, d, sh);
+      prefix |= d << sp_shift(q);
+      pmask |= sp_mask(q) << sp_shift(q);
+    }
   }
 }
+
+
 
 struct SpRow {
   int64_t ks, ke, lo, hi;
@@ -451,6 +468,17 @@ __device__ __forceinline__ SpRow sp_row(const TopkParams& p) {
   return r;
 }
 
+// the chunk's scores, SP_PER per thread (position lo + tid + SP_THREADS u), all loaded before
+// any is used (one loop step per load waited for each in turn); `in` flags those inside it
+__device__ __forceinline__ void sp_load(const float* src, const SpRow& r, float (&v)[SP_PER], bool (&in)[SP_PER]) {
+#pragma unroll
+  for (int u = 0; u < SP_PER; ++u) {
+    const int64_t i = r.lo + threadIdx.x + (int64_t)u * SP_THREADS;
+    in[u] = i < r.hi;
+    v[u] = in[u] ? src[i] : 0.f;
+  }
+}
+
 __global__ __launch_bounds__(256) void topk_split_clear(uint32_t* hist, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
     hist[i] = 0u;
@@ -464,16 +492,20 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_hist(TopkParams p, Spli
   if (r.skip) return;
   const int64_t row = blockIdx.y;
   uint32_t* gh = a.hist + row * 3 * SP_BINS;
+  const float* src = p.scores + row * p.ld;
+  float v[SP_PER];
+  bool in[SP_PER];
+  sp_load(src, r, v, in);
   uint32_t prefix, pmask, rem;
-  sp_prefix(gh, PASS, (uint32_t)p.topk, prefix, pmask, rem, sh);
+  sp_prefix<PASS>(gh, (uint32_t)p.topk, prefix, pmask, rem, sh);
   for (int i = threadIdx.x; i < SP_BINS; i += SP_THREADS) lh[i] = 0u;
   __syncthreads();
-  const float* src = p.scores + row * p.ld;
   constexpr int shift = sp_shift(PASS);
   constexpr uint32_t dmask = sp_mask(PASS);
-  for (int64_t i = r.lo + threadIdx.x; i < r.hi; i += SP_THREADS) {
-    const uint32_t key = order_key(src[i]);
-    if ((key & pmask) == prefix) atomicAdd(&lh[(key >> shift) & dmask], 1u);
+#pragma unroll
+  for (int u = 0; u < SP_PER; ++u) {
+    const uint32_t key = order_key(v[u]);
+    if (in[u] && (key & pmask) == prefix) atomicAdd(&lh[(key >> shift) & dmask], 1u);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < SP_BINS; i += SP_THREADS) {
@@ -505,14 +537,18 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_count(TopkParams p, Spl
   const SpRow r = sp_row(p);
   if (r.skip) return;
   const int64_t row = blockIdx.y;
-  uint32_t tau, pmask, rem;
-  sp_prefix(a.hist + row * 3 * SP_BINS, 3, (uint32_t)p.topk, tau, pmask, rem, sh);
   const float* src = p.scores + row * p.ld;
+  float v[SP_PER];
+  bool in[SP_PER];
+  sp_load(src, r, v, in);
+  uint32_t tau, pmask, rem;
+  sp_prefix<3>(a.hist + row * 3 * SP_BINS, (uint32_t)p.topk, tau, pmask, rem, sh);
   uint32_t gt = 0, eq = 0;
-  for (int64_t i = r.lo + threadIdx.x; i < r.hi; i += SP_THREADS) {
-    const uint32_t key = order_key(src[i]);
-    gt += key > tau;
-    eq += key == tau;
+#pragma unroll
+  for (int u = 0; u < SP_PER; ++u) {
+    const uint32_t key = order_key(v[u]);
+    gt += in[u] && key > tau;
+    eq += in[u] && key == tau;
   }
   sp_block_sum2(gt, eq, sh);
   if (threadIdx.x == 0) {
@@ -538,8 +574,12 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_emit(TopkParams p, Spli
     return;
   }
   if (r.skip) return;
+  const float* src = p.scores + row * p.ld;
+  float v[SP_PER];
+  bool in[SP_PER];
+  sp_load(src, r, v, in);
   uint32_t tau, pmask, rem;
-  sp_prefix(a.hist + row * 3 * SP_BINS, 3, (uint32_t)K, tau, pmask, rem, sh);
+  sp_prefix<3>(a.hist + row * 3 * SP_BINS, (uint32_t)K, tau, pmask, rem, sh);
 
   // keys > tau and == tau in the chunks before this one
   const uint32_t* c = a.cnt + row * a.nchunk * 2;
@@ -553,9 +593,12 @@ __global__ __launch_bounds__(SP_THREADS) void topk_split_emit(TopkParams p, Spli
   if (my_gt == 0 && (my_eq == 0 || eqb >= rem)) return;  // nothing kept here (uniform)
 
   // stage the chunk's keys; thread t then walks positions lo + SP_PER t .. lo + SP_PER (t + 1) - 1
-  const float* src = p.scores + row * p.ld;
   const int len = (int)(r.hi - r.lo);
-  for (int i = tid; i < len; i += SP_THREADS) keys[i + i / SP_PER] = order_key(src[r.lo + i]);
+#pragma unroll
+  for (int u = 0; u < SP_PER; ++u) {
+    const int i = tid + u * SP_THREADS;
+    if (in[u]) keys[i + i / SP_PER] = order_key(v[u]);
+  }
   __syncthreads();
   const int i0 = tid * SP_PER, i1 = min(len, i0 + SP_PER);
   uint32_t g = 0, e = 0;
