@@ -907,10 +907,81 @@ enum G8Mode : int { G8_SCORES = 0, G8_SAMPLES = 1, G8_CANDIDATES = 2 };
 
 struct G8Shared {
   int32_t rks[G8_BM], rke[G8_BM];  // each row's key range (absolute; empty for masked rows)
-  int32_t clo[G8_BM], chi[G8_BM];  // candidate mode: the range as columns of the tile, in [0, 256]
   uint32_t lkey[G8_BM];            // candidate mode: each row's threshold (see below)
   float wmax[G8_CW + G8_DW];
 };
+
+// Candidate selection of a tile, by all 12 waves over the row-major LDS copy of its scores
+// ([128][G8_SROW] fp32, scores times 2^E): wave v takes rows v, v + 12, ...; a row's 256
+// columns are 4 per lane.  Pass 1 counts each row's cells at or above its threshold (inside
+// its range); lane k of the wave then reserves the slots of its k-th row with one atomic for
+// all of the wave's rows; pass 2 writes the cells to them (slots past cap are dropped: the
+// count still records them, and such a row falls back).
+constexpr int G8_SROW = G8_BN + 8;  // the +8 words put rows 4 apart 32 banks apart
+static_assert(G8_BM * G8_SROW * 4 <= G8_VBASE, "the row-major tile fits the stages");
+__device__ __forceinline__ void g8_select(const IndexerParams& p, unsigned char* smem, const G8Shared& sh, int b,
+                                          int t0, int64_t s0, float up, bool all_in, int wv, int lane) {
+  constexpr int NW = G8_CW + G8_DW;
+  const float* tl = reinterpret_cast<const float*>(smem);
+  const int T = p.T;
+  auto takes = [&](int m, bool (&tk)[4]) {
+    const float4 x = *reinterpret_cast<const float4*>(tl + m * G8_SROW + 4 * lane);
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+    const uint32_t lk = sh.lkey[m];
+    const int64_t rks = sh.rks[m], rke = sh.rke[m];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t v = __float_as_uint(xv[u]);
+      const uint32_t key = v ^ (uint32_t)(((int32_t)v >> 31) | (int32_t)0x80000000);
+      const int64_t s = s0 + 4 * lane + u;
+      tk[u] = key >= lk && (all_in || (s >= rks && s < rke));
+    }
+    return x;
+  };
+  uint32_t mycnt = 0u;
+  int k = 0;
+  for (int m = wv; m < G8_BM; m += NW, ++k) {
+    bool tk[4];
+    (void)takes(m, tk);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += (uint32_t)__popcll(__ballot(tk[u]));
+    mycnt = lane == k ? c : mycnt;
+  }
+  uint32_t base = 0u;
+  if (mycnt) base = (uint32_t)atomicAdd(p.cand_cnt + (int64_t)b * T + t0 + wv + NW * lane, (int32_t)mycnt);
+  // a plain-register copy of the atomics' results (read from their destination, each read
+  // below would also wait for every candidate store before it)
+  uint32_t slots;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(slots) : "v"(base));
+  unsigned char* lpos = reinterpret_cast<unsigned char*>(p.cand_pos + ((int64_t)b * T + t0) * p.cap);
+  unsigned char* lval = reinterpret_cast<unsigned char*>(p.cand_val + ((int64_t)b * T + t0) * p.cap);
+  const uint32_t cap = (uint32_t)p.cap;
+  k = 0;
+  for (int m = wv; m < G8_BM; m += NW, ++k) {
+    bool tk[4];
+    const float4 x = takes(m, tk);
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+    uint64_t bal[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) bal[u] = __ballot(tk[u]);
+    if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) continue;
+    uint32_t slot = __builtin_amdgcn_readlane(slots, k);
+    const uint32_t roff = (uint32_t)m * cap;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (tk[u]) {
+        const uint32_t sl = slot + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u], 0u));
+        if (sl < cap) {
+          const uint32_t at = (roff + sl) * 4u;
+          *reinterpret_cast<int32_t*>(lpos + at) = (int32_t)(s0 + 4 * lane + u);
+          *reinterpret_cast<float*>(lval + at) = xv[u];
+        }
+      }
+      slot += (uint32_t)__popcll(bal[u]);
+    }
+  }
+}
 
 // One tile: query tile qy (rows t0 = 128 qy ..), key tile kx, batch item b.  Every wave
 // returns from it (the copy waves once their loads have landed).
@@ -934,8 +1005,6 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
     sh.rke[tid] = (int32_t)ke;
     live = (ks < s0 + G8_BN * kst) && (ke > s0) && (ks < ke);
     if (MODE == G8_CANDIDATES) {
-      sh.clo[tid] = (int32_t)min<int64_t>(max<int64_t>(ks - s0, 0), G8_BN);
-      sh.chi[tid] = (int32_t)min<int64_t>(max<int64_t>(ke - s0, 0), G8_BN);
       inside = ks <= s0 && ke >= s0 + G8_BN;
       // The epilogue compares keys that do not fold -0.0 onto +0.0 (u ^ 0x80000000 or ~u); a
       // threshold of +0.0's key is lowered by one, to -0.0's: the same cells pass as with folding.
@@ -977,21 +1046,42 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
     tile_e = 25 + x;
   }
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform, so the role branches are too
+  const float up = ldexpf(1.f, tile_e);
   if (wv >= G8_CW) {
     G8Copy cw{p, smem, 0u, lane, wv - G8_CW, b, t0, p.H, T, s0, S, kst, lead};
     cw.setup();
-    cw.run();
-    return;  // every load it issued has landed (the last head waits for all)
+    cw.run();  // every load it issued has landed (the last head waits for all)
+    if constexpr (MODE == G8_CANDIDATES) {
+      g8_barrier();  // every product of the tile is done: the stages are free
+      g8_barrier();  // the compute waves' sums are in LDS
+      g8_select(p, smem, sh, b, t0, s0, up, all_in, wv, lane);
+    }
+    return;
   }
   G8Math w{smem, lane, wv, wv >> 2, wv >> 2, wv & 3, lane & 31, lane >> 5, p.H};
   w.down = ldexpf(1.f, -tile_e);
   w.setup();
   w.run();
+  if constexpr (MODE == G8_CANDIDATES) {
+    // the scores (times 2^E, exactly the stored values) into the tile's row-major LDS copy
+    g8_barrier();
+    float* tl = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 64 * w.wm + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) tl[m * G8_SROW + 64 * w.wn + 32 * j + w.lr] = w.tot[i][j][r] * up;
+      }
+    g8_barrier();
+    g8_select(p, smem, sh, b, t0, s0, up, all_in, wv, lane);
+    return;
+  }
 
-  // candidate cells of the wave's block: row 64wm + 32i + 8(r/4) + 4lg + r%4, column 64wn + 32j + lr
-  // (key s0 + kst * column); the sums carry 2^-E
-  const float up = ldexpf(1.f, tile_e);
-  if constexpr (MODE != G8_CANDIDATES) {
+  // the wave's cells: row 64wm + 32i + 8(r/4) + 4lg + r%4, column 64wn + 32j + lr (key s0 + kst *
+  // column); the sums carry 2^-E
+  {
     float* dst = p.scores + ((int64_t)b * T + t0) * p.ld + (int64_t)kx * G8_BN;  // row t0, column 0 of the tile
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1005,72 +1095,6 @@ __device__ __forceinline__ void g8_tile(const IndexerParams& p, unsigned char* s
           if (s >= sh.rks[m] && s < sh.rke[m]) dst[(int64_t)m * p.ld + c] = w.tot[i][j][r] * up;
         }
     }
-    return;
-  } else {
-    // Candidate mode.  Pass 1 marks the lane's candidate cells (bit 16 j + r of tb[i]) and
-    // counts them per row of the wave's 64-row block (lane l ends with row l's count); one
-    // atomic per lane reserves the slots of its row; pass 2 writes the cells to them.
-    const int own = 64 * w.wm;          // first row of the wave's block in the tile
-    uint32_t tb[2] = {0u, 0u}, mycnt = 0u;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = own + 32 * i + 8 * (r >> 2) + 4 * w.lg + (r & 3);
-        bool take[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int c = 64 * w.wn + 32 * j + w.lr;
-          const uint32_t u = __float_as_uint(w.tot[i][j][r] * up);
-          const uint32_t key = u ^ (uint32_t)(((int32_t)u >> 31) | (int32_t)0x80000000);
-          take[j] = key >= sh.lkey[m] && (all_in || (c >= sh.clo[m] && c < sh.chi[m]));
-        }
-        tb[i] |= ((uint32_t)take[0] << r) | ((uint32_t)take[1] << (16 + r));
-        const uint64_t m0 = __ballot(take[0]), m1 = __ballot(take[1]);
-        const int l0 = 32 * i + 8 * (r >> 2) + (r & 3);  // the half-waves' rows: l0 and l0 + 4
-        const uint32_t clo = (uint32_t)(__popcll(m0 & 0xffffffffull) + __popcll(m1 & 0xffffffffull));
-        const uint32_t chi = (uint32_t)(__popcll(m0 >> 32) + __popcll(m1 >> 32));
-        mycnt = lane == l0 ? clo : (lane == l0 + 4 ? chi : mycnt);
-      }
-    uint32_t base = 0u;
-    if (mycnt) base = (uint32_t)atomicAdd(p.cand_cnt + (int64_t)b * T + t0 + own + lane, (int32_t)mycnt);
-    // The atomics' results, copied once into a plain register: read straight from the
-    // atomics' destination, every read below would first wait for every global access
-    // before it, the candidate stores of the earlier rows included (one counter for loads,
-    // stores and atomics, completed in order).
-    uint32_t slots;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(slots) : "v"(base));
-    const uint64_t half = w.lg ? ~0xffffffffull : 0xffffffffull;
-    // the lists of the tile's rows from one uniform base: a cell goes to byte 4 (row * cap + slot)
-    // (row in the tile < 128, slot < cap: fits 32 bits), no 64-bit arithmetic per row
-    unsigned char* lpos = reinterpret_cast<unsigned char*>(p.cand_pos + ((int64_t)b * T + t0) * p.cap);
-    unsigned char* lval = reinterpret_cast<unsigned char*>(p.cand_val + ((int64_t)b * T + t0) * p.cap);
-    const uint32_t cap = (uint32_t)p.cap, lrow = (uint32_t)(own + 4 * w.lg) * cap;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool k0 = (tb[i] >> r) & 1u, k1 = (tb[i] >> (16 + r)) & 1u;
-        const uint64_t m0 = __ballot(k0), m1 = __ballot(k1);
-        if ((m0 | m1) == 0) continue;
-        const int l0 = 32 * i + 8 * (r >> 2) + (r & 3);
-        const uint32_t rb0 = __builtin_amdgcn_readlane(slots, l0), rb1 = __builtin_amdgcn_readlane(slots, l0 + 4);
-        const uint32_t rb = w.lg ? rb1 : rb0;
-        const uint32_t c0 = (uint32_t)__popcll(m0 & half);
-        const uint32_t roff = lrow + (uint32_t)l0 * cap;  // the cells' row (own + l0 + 4 lg) times cap
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if (!(j ? k1 : k0)) continue;
-          const uint64_t mj = (j ? m1 : m0) & half;
-          const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mj >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mj, 0u));
-          const uint32_t slot = rb + (j ? c0 : 0u) + below;
-          if (slot < cap) {
-            const uint32_t at = (roff + slot) * 4u;
-            *reinterpret_cast<int32_t*>(lpos + at) = (int32_t)(s0 + 64 * w.wn + 32 * j + w.lr);
-            *reinterpret_cast<float*>(lval + at) = w.tot[i][j][r] * up;
-          }
-        }
-      }
   }
 }
 
