@@ -8,14 +8,19 @@
 // follow the Megatron-Bridge pull request's naming of the indexer weights
 // (per-head index q/k projections and a per-head scalar `weights_proj`).
 //
-// Two kernels:
-//  * indexer_mfma: bf16 or fp8 (OCP e4m3fn) with D == 128.  A workgroup owns a
-//    64-query x 64-key tile of one batch item and loops over the heads: each head
-//    is a 64x64x128 contraction on the matrix cores (v_mfma_f32_32x32x16_bf16, or
-//    v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales) from LDS-staged
-//    tiles, followed by the fused ReLU * weight reduction in fp32 registers.
-//  * indexer_generic: any dtype / D, one thread per key, fp32 FMA.  Used for the
-//    fp32 inputs and for shapes the MFMA kernel does not cover.
+// Kernels (D == 128 unless noted; the launcher picks one per shape):
+//  * indexer_fp8_groups: fp8 (OCP e4m3fn) with one key head per query head, T >= 64 (the
+//    long-prefix prefill chunk): 128-query x 256-key tiles, copy waves and compute waves, with
+//    the sample, candidate and row-mask modes the fused indexer -> top-k uses;
+//  * indexer_tile: bf16 or fp8 prefill, T >= 32: 128 x 128 tiles, the copies and the epilogue
+//    of the previous head spread over each head's k-steps;
+//  * indexer_stream: decode rows (T <= 4): the keys streamed once from HBM on the vector ALUs,
+//    with the same modes;
+//  * indexer_mfma: the other bf16 / fp8 shapes: 64 x 64 tiles, one head at a time on the matrix
+//    cores (v_mfma_f32_32x32x16_bf16, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+//    scales) from LDS-staged tiles, then the ReLU * weight reduction in fp32 registers;
+//  * indexer_generic: any dtype / D (fp32 inputs), one thread per key, fp32 FMA;
+//  * g8_vectors: the head-major per-head vectors indexer_fp8_groups reads inside the fused call.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -633,9 +638,12 @@ void indexer_tile(IndexerParams p) {
 //    (128 bytes each) form one 48 KiB LDS stage, three stages are in flight, and the copies
 //    run two heads ahead.  A copy waits in the memory pipeline until its data lands, which
 //    would stall a wave that also has MFMAs or vector work to issue; here only the copy waves
-//    wait.  They also form each head's w * q scale a head early.
+//    wait.  They also copy each head's per-row and per-key vectors a head early (head-major
+//    runs where the caller's workspace holds them, else 4-byte loads and the w * q scale
+//    product formed in LDS).
 // One barrier per head: after it head h's stage and the per-row vectors of head h+1 are in
-// LDS, and the stage of head h-1 is free for head h+2's copies.
+// LDS, and the stage of head h-1 is free for head h+2's copies.  In candidate mode the tile's
+// sums then go to a row-major copy in the stages, and all 12 waves select its cells (g8_select).
 //
 // A tile's key rows are shared by the workgroups of an XCD that own its query tiles (four on
 // the 128K-prefix chunk), and a copy that misses the L2 takes several heads to land; so one of
