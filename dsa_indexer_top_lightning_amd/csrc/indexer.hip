@@ -1175,15 +1175,23 @@ __global__ __launch_bounds__(256) void g8_vectors(IndexerParams p, float* ks_t, 
   const int64_t n = keys ? p.s_cap : p.T;       // valid columns
   const int64_t ld = keys ? p.vec_s : p.vec_t;  // padded columns
   const int64_t c0 = (int64_t)(keys ? blockIdx.x : blockIdx.x - nks) * GV_N;
-  for (int i = tid; i < GV_N * H; i += 256) {
-    const int r = i / H, h = i % H;
-    const int64_t c = c0 + r;
-    float v = 0.f;
-    if (c < n) {
-      const int64_t o = ((int64_t)b * n + c) * H + h;
-      v = keys ? p.k_scale[o] : p.w[o] * p.q_scale[o];
+  // eight elements per thread in flight: every load of a round before any is used (clamped
+  // in-bounds addresses; the values past n are replaced by 0 afterwards)
+  const int64_t last = (int64_t)b * n * H + n * H - 1;  // the item's last element
+  for (int i0 = tid; i0 < GV_N * H; i0 += 8 * 256) {
+    float x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 256 * u;
+      const int64_t o = min(((int64_t)b * n + c0 + i / H) * H + i % H, last);
+      x[u] = keys ? p.k_scale[o] : p.w[o];
+      y[u] = keys ? 1.f : p.q_scale[o];
     }
-    tile[r][h] = v;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + 256 * u;
+      if (i < GV_N * H) tile[i / H][i % H] = c0 + i / H < n ? (keys ? x[u] : x[u] * y[u]) : 0.f;
+    }
   }
   __syncthreads();
   float* dst = keys ? ks_t : wq_t;
