@@ -1258,6 +1258,7 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
   const int g = (Hk == H) ? h : 0;
   const unsigned char* kg = static_cast<const unsigned char*>(p.k);
   const int64_t krow = (int64_t)Hk * HD * ESZ;
+  __shared__ float sv[KPB];  // the block's scores, stored by one wave at the end
 
   for (int j = wave; j < KPB; j += 4) {
     const int64_t col = sblk + j;
@@ -1299,7 +1300,7 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
     for (int off = LPH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
     if (lane == 0) {
       if constexpr (MODE != G8_CANDIDATES) {
-        p.scores[row * p.ld + col] = v;
+        sv[j] = v;
       } else if (order_key(v) >= lk) {
         const int32_t slot = atomicAdd(p.cand_cnt + row, 1);
         if (slot < p.cap) {
@@ -1308,6 +1309,12 @@ __global__ __launch_bounds__(256) void indexer_stream(IndexerParams p) {
         }
       }
     }
+  }
+  if constexpr (MODE != G8_CANDIDATES) {
+    // one 256-byte store per block instead of one 4-byte store per key
+    __syncthreads();
+    const int64_t col = sblk + lane;
+    if (wave == 0 && col * kst >= ks && col * kst < ke) p.scores[row * p.ld + col] = sv[lane];
   }
 }
 
