@@ -466,9 +466,12 @@ __global__ __launch_bounds__(256) void bm_dense_scatter(MlaBwdParams p, BwDense 
   }
 }
 
-// grid (nkt * nchunk, B), a tile's chunks consecutive.  Wave w: latent rows 32 (w & 1) .. of the tile as the S and dP
-// columns, heads 32 (w >> 1) .. as their rows; in the dC product rows 32 (w & 1) .. and dim
-// blocks [9 (w >> 1), +9).
+// grid (nkt * nchunk8, B), nchunk8 = nchunk rounded up to a multiple of 8.  Block x runs on XCD
+// x mod 8 (the dispatcher's round robin), so chunk ch goes to XCD ch mod 8 and each XCD walks all
+// tiles of one chunk before its next: the 32 compute units of an XCD read the same query and
+// output-gradient rows (held in its L2) while adding into different tiles of dkv.
+// Wave w: latent rows 32 (w & 1) .. of the tile as the S and dP columns, heads 32 (w >> 1) .. as
+// their rows; in the dC product rows 32 (w & 1) .. and dim blocks [9 (w >> 1), +9).
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void mla_bwd_dkv(MlaBwdParams p, BwWs w, BwDense d, int nchunk) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -480,13 +483,19 @@ void mla_bwd_dkv(MlaBwdParams p, BwWs w, BwDense d, int nchunk) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int lr = lane & 31, lg = lane >> 5, kb = wv & 1, hb = wv >> 1;
-  const int kx = blockIdx.x / nchunk, ch = blockIdx.x % nchunk;
+  const int xk = (int)(blockIdx.x >> 3);
+  const int kx = xk % d.nkt, ch = (xk / d.nkt) * 8 + (int)(blockIdx.x & 7);
+  if (ch >= nchunk) return;
   const uint32_t sink = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(smem + DK_LDS - 256);
   const int64_t b = blockIdx.y;
   const int T = p.T, Hm = p.Hm;
   const int64_t s_cap = p.s_cap;
   const int64_t j0 = (int64_t)kx * MT;
   const int tq0 = ch * DK_TC, tq1 = min(T, tq0 + DK_TC);
+  // which of the chunk's queries selected a row of the tile: one load per lane, all at once
+  static_assert(DK_TC <= 64, "one occupancy flag per lane");
+  const uint64_t live = __ballot(tq0 + lane < tq1 && d.occ[(b * T + tq0 + lane) * d.nkt + kx] != 0);
+  if (live == 0) return;  // the same on every wave
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)smem;
 
   // this wave's 32 latent rows: B fragments (dims 16 st + 8 lg .. +7 of row j0 + 32 kb + lr)
@@ -510,7 +519,7 @@ void mla_bwd_dkv(MlaBwdParams p, BwWs w, BwDense d, int nchunk) {
 
   for (int t = tq0; t < tq1; ++t) {
     const int64_t row = b * T + t;
-    if (!d.occ[row * d.nkt + kx]) continue;  // uniform
+    if (!((live >> (t - tq0)) & 1)) continue;  // uniform
     const float m = (float)d.mult[row * d.ldm + jcol];
     for (int hg = 0; hg < Hm / MHG; ++hg) {
       {
@@ -838,9 +847,9 @@ hipError_t launch_sparse_mla_bwd_mfma(const MlaBwdParams& p, void* ws, size_t ws
   if (dense) {
     static std::atomic<size_t> high{0};
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dkv), DK_LDS, high)) != hipSuccess) return e;
-    const int nchunk = (p.T + DK_TC - 1) / DK_TC;
-    hipLaunchKernelGGL(mla_bwd_dkv, dim3((unsigned)(d.nkt * nchunk), (unsigned)p.B), dim3(256), DK_LDS, st, p, w, d,
-                       nchunk);
+    const int nchunk = (p.T + DK_TC - 1) / DK_TC, nchunk8 = (nchunk + 7) / 8 * 8;
+    hipLaunchKernelGGL(mla_bwd_dkv, dim3((unsigned)((int64_t)d.nkt * nchunk8), (unsigned)p.B), dim3(256), DK_LDS, st,
+                       p, w, d, nchunk);
   } else {
     static std::atomic<size_t> high{0};
     if ((e = allow_dynamic_lds(reinterpret_cast<const void*>(mla_bwd_dc), DC_LDS, high)) != hipSuccess) return e;
