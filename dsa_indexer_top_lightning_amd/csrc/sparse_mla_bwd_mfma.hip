@@ -44,7 +44,10 @@ struct BwWs {
   float* delta;   // [rows][Hm]
   uint16_t* p;    // [rows][Tp][Hm]
   uint16_t* dz;   // [rows][Tp][Hm]   sm_scale * dz
-  uint16_t* dzt;  // [rows][Hm][Tp]   the same, slot-contiguous per head
+  // the same in mla_bwd_dq's fragment order: per (token, head group of 64, 64-slot tile) a block
+  // of 4096 values, entry ((hb * 4 + ks) * 64 + lane) holding, for head 32 hb + lane % 32, the
+  // slots 16 ks + 4 (lane / 32) + {0..3} and 8 more (the k-step's permuted B fragment)
+  uint16_t* dzt;
   int Tp;
 };
 
@@ -225,7 +228,7 @@ void mla_bwd_pz(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
   for (int u = 0; u < 4; ++u) koff[u] = mk * SEG + 16 * ((2 * u + lg) ^ perm(mk));
   uint16_t* wp = w.p + (tok * Tp) * p.Hm + myhead;
   uint16_t* wz = w.dz + (tok * Tp) * p.Hm + myhead;
-  uint16_t* wzt = w.dzt + (tok * p.Hm + myhead) * (int64_t)Tp;
+  uint16_t* wzt = w.dzt + (tok * (p.Hm / MHG) + hg) * (int64_t)Tp * MHG + lane * 8;
   // P and dz' of a tile as bf16 pairs (rows r, r + 1 of the accumulator), stored after the
   // next tile barrier: stores count in vmcnt, and stored right away they would hold up that
   // barrier's wait for the gather
@@ -240,8 +243,12 @@ void mla_bwd_pz(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
         wz[e * p.Hm] = (uint16_t)((r & 1) ? pz[r >> 1] >> 16 : pz[r >> 1]);
       }
     }
+    // slots 32 vv + 16 qq + 4 lg + {0..3, 8..11}: k-step 2 vv + qq of dq's B fragments
+    uint16_t* zt = wzt + (int64_t)(t0 + t) * (MT * MHG);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint2*>(wzt + e0 + 8 * q + 4 * lg) = make_uint2(pz[2 * q], pz[2 * q + 1]);
+    for (int qq = 0; qq < 2; ++qq)
+      *reinterpret_cast<uint4*>(zt + (hh * 4 + 2 * vv + qq) * 64 * 8) =
+          make_uint4(pz[4 * qq], pz[4 * qq + 1], pz[4 * qq + 2], pz[4 * qq + 3]);
   };
 
   for (int i = 0; i < ntiles; ++i) {
@@ -666,14 +673,15 @@ void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
     auto tile_src = [&](int32_t ent) -> GatherSrc {
       return gather_src(kvg, MRB, bm_valid(ent, s_cap) ? ent : 0, wave, lane);
     };
-    // B fragments of a tile (dz'^T: heads 32hb + lr, slots of k-step ks in the permuted order)
+    // B fragments of a tile (dz'^T: heads 32hb + lr, slots of k-step ks in the permuted order),
+    // stored by mla_bwd_pz in this order: one 16-byte load per lane and fragment
+    const uint16_t* zq = w.dzt + (tok * (p.Hm / MHG) + hg) * (int64_t)Tp * MHG + lane * 8;
     auto load_b = [&](int t, i32x4 (&bz)[2][4]) {
-      const int64_t e0 = (int64_t)(t0 + t) * MT + 4 * lg;
+      const uint16_t* zt = zq + (int64_t)(t0 + t) * (MT * MHG);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          bz[hb][ks] = ld_split8(w.dzt + (tok * p.Hm + hg * MHG + 32 * hb + lr) * (int64_t)Tp + e0 + 16 * ks);
+        for (int ks = 0; ks < 4; ++ks) bz[hb][ks] = *reinterpret_cast<const i32x4*>(zt + (hb * 4 + ks) * 64 * 8);
     };
     fetch_entries(0);
     fetch_entries(1);
@@ -689,16 +697,16 @@ void mla_bwd_dq(MlaBwdParams p, int nsplit, int tiles_per_split, BwWs w) {
     const TrOff tr(lane);
     // one tile: wait for its gather and B fragments, request the next tile's gather and the B
     // fragments of the tile after it, 36 products.  Loads complete in issue order; per lane a
-    // gather is 18 loads, an entry fetch 1, a fragment set 16.  Issued after tile i's
+    // gather is 18 loads, an entry fetch 1, a fragment set 8.  Issued after tile i's
     // gather: the entry fetch and, unless tile i is the last, the fragments of tile i + 1
     // (for tile 0: its own fragments, then those of tile 1).
     auto step = [&](int i, const i32x4 (&bz)[2][4], i32x4 (&nz)[2][4]) {
       const int bf = i & 1;
       if (i == 0) {
-        if (ntiles > 1) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+        if (ntiles > 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       } else {
-        if (i + 1 < ntiles) asm volatile("s_waitcnt vmcnt(17)\n\ts_barrier" ::: "memory");
+        if (i + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(1)\n\ts_barrier" ::: "memory");
       }
       if (i + 1 < ntiles) {
