@@ -247,18 +247,23 @@ __global__ __launch_bounds__(256, 2) void id_dq(IndexBwdParams p, DenseWs ws) {
   }
   __syncthreads();
   for (int i = 0; i < n; ++i) {
-    if (i + 1 < n) fetch(i + 1);
     const unsigned char* buf = smem + (i & 1) * ID_BUF;
     const int64_t j0 = (int64_t)list[i] * ID_T;
     const float* kv = ksv + (i & 1) * ID_T;
+    // DI of this lane's query at key rows 32 kb + 8 q + 4 lg + (0..3), issued before the next
+    // tile's loads so that using it does not wait for them (loads complete in issue order)
+    float4 dib[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dib[kb][q] = tin ? *reinterpret_cast<const float4*>(dirow + j0 + 32 * kb + 8 * q + 4 * lg) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i + 1 < n) fetch(i + 1);
     // one 32-key half at a time: S^T = K Q^T (keys 32 kb + rows, this wave's 32 queries as
     // columns), G^T and dw, then dq^T += K^T G^T over its two 16-key steps
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      float4 di[4];  // DI of this lane's query at key rows 32 kb + 8 q + 4 lg + (0..3)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        di[q] = tin ? *reinterpret_cast<const float4*>(dirow + j0 + 32 * kb + 8 * q + 4 * lg) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 (&di)[4] = dib[kb];
       f32x16 s;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -364,22 +369,35 @@ __global__ __launch_bounds__(256, 2) void id_dk(IndexBwdParams p, DenseWs ws) {
       vec[(i & 1) * 2 * ID_T + ID_T + tid] = wqn;
     }
   };
+  // DI at the accumulator's query rows 32 qh + 8 q + 4 lg + e of tile i, this lane's key
+  // column: loaded one tile ahead and before that tile's query rows, so that using it never
+  // waits for the newer loads (loads complete in issue order)
+  float dn[16];
+  auto fetch_di = [&](int i) {
+    const int64_t t0 = (int64_t)list[i % n] * ID_T;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + 32 * qh + 8 * (r >> 2) + 4 * lg + (r & 3);
+      const int64_t tc = t < T ? t : T - 1;
+      const float dv = ws.DI[((int64_t)b * T + tc) * ws.ldi + jcol];
+      dn[r] = t < T ? dv : 0.f;
+    }
+  };
   if (total > 0) {
+    fetch_di(0);
     fetch(0);
     put(0);
   }
   __syncthreads();
   for (int i = 0; i < total; ++i) {
-    if (i + 1 < total) fetch(i + 1);
-    const unsigned char* buf = smem + (i & 1) * ID_BUF;
-    const int64_t t0 = (int64_t)list[i % n] * ID_T;
-    // DI at the accumulator's query rows 32 qh + 8 q + 4 lg + e, this lane's key column
     float di[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + 32 * qh + 8 * (r >> 2) + 4 * lg + (r & 3);
-      di[r] = t < T ? ws.DI[((int64_t)b * T + t) * ws.ldi + jcol] : 0.f;
+    for (int r = 0; r < 16; ++r) di[r] = dn[r];
+    if (i + 1 < total) {
+      fetch_di(i + 1);
+      fetch(i + 1);
     }
+    const unsigned char* buf = smem + (i & 1) * ID_BUF;
     // S = Q K^T: queries 32 qh + rows, this wave's 32 keys as columns
     f32x16 s;
 #pragma unroll
