@@ -48,6 +48,12 @@ MEASURED_TRAFFIC = {
     ("chunk128k_fp8", "mla_mfma"): {
         "bytes": 3917845.3 * 1024 * 2.0 + 263168.0 * 1024 * 1.0,
         "source": "profiles/mla_mfma_chunk128k_fp8_hbm_counters.md"},
+    ("prefill4k_bf16", "mla_mfma"): {
+        "bytes": 314290.2 * 1024 * 2.0 + 263168.0 * 1024 * 1.0,
+        "source": "profiles/mla_mfma_prefill4k_bf16_hbm_counters.md"},
+    ("decode1m_b4_fp8", "indexer_stream"): {
+        "bytes": 8651439.6 * 1024 * 2.0 + 16384.0 * 1024 * 1.0,
+        "source": "profiles/indexer_stream_decode1m_b4_fp8_hbm_counters.md"},
     ("decode32k_b64_bf16", "indexer_stream"): {
         "bytes": 8393959.4 * 1024 * 2.0 + 8192.0 * 1024 * 1.0,
         "source": "profiles/indexer_stream_decode32k_b64_bf16_hbm_counters.md"},
