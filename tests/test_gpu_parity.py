@@ -134,6 +134,57 @@ def test_topk_short_prefix_example_on_gpu():
     assert np.array_equal(got[:256], np.arange(256)) and (got[256:] == -1).all()
 
 
+def test_empty_prefix_and_calls_without_rows():
+    # A prefix of length 0: every top-k row is padding only (also through the fused indexer ->
+    # top-k), and the attention of a selection with no valid entry is 0 with lse = -inf (the
+    # oracle's empty-selection values).  Calls with no query rows succeed and write nothing.
+    k, H, D, Hm = 16, 32, 128, 64
+    ref_idx, _ = O.topk(np.zeros((1, 3, 0)), np.zeros((1, 3), np.int32), np.zeros((1, 3), np.int32), k)
+    assert (ref_idx == -1).all()
+    out = torch.full((1, 3, k), -7, dtype=torch.int32, device="cuda")
+    b.topk_select(torch.zeros((1, 3, 1), device="cuda"), out, 0)
+    assert np.array_equal(out.cpu().numpy(), ref_idx)
+
+    q = torch.randn((1, 3, H, D), device="cuda").to(torch.bfloat16)
+    kk = torch.empty((1, 0, H, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.rand((1, 3, H), device="cuda")
+    nws = b.workspace_bytes(b.make_shape(1, 3, 0, H=H, D=D, Hk=H, topk=k), b.OP_INDEXER_TOPK)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    out.fill_(-7)
+    b.indexer_topk(q, kk, w, out, workspace=ws)
+    assert np.array_equal(out.cpu().numpy(), ref_idx)
+
+    km = 256  # 4 tiles of 64 slots: two query rows split their selection over workgroups
+    rq = np.random.default_rng(5).standard_normal((Hm, 576))
+    o_ref, lse_ref = O.sparse_mla_row(rq, np.zeros((0, 576)), np.full(km, -1), 0.05, 512)
+    assert not o_ref.any() and np.isneginf(lse_ref).all()
+    for T in (2, 1100):  # selection split over workgroups (then merged), one workgroup per query
+        mq = torch.randn((1, T, Hm, 576), device="cuda").to(torch.bfloat16)
+        kv = torch.empty((1, 0, 576), dtype=torch.bfloat16, device="cuda")
+        idx = torch.full((1, T, km), -1, dtype=torch.int32, device="cuda")
+        o = torch.full((1, T, Hm, 512), 7.0, device="cuda").to(torch.bfloat16)
+        lse = torch.full((1, T, Hm), 7.0, device="cuda")
+        shape = b.make_shape(1, T, 0, topk=km, Hm=Hm, Dc=512, Dr=64)
+        mws = torch.empty(max(b.workspace_bytes(shape, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+        b.sparse_mla_attention(mq, kv, idx, 0.05, o, lse, Dc=512, workspace=mws)
+        assert not o.float().cpu().numpy().any() and np.isneginf(lse.cpu().numpy()).all(), T
+
+    # no query rows: nothing is written, the calls succeed
+    out0 = torch.empty((1, 0, k), dtype=torch.int32, device="cuda")
+    b.topk_select(torch.zeros((1, 0, 100), device="cuda"), out0, 100)
+    b.indexer_scores(torch.empty((1, 0, H, D), dtype=torch.bfloat16, device="cuda"),
+                     torch.randn((1, 100, H, D), device="cuda").to(torch.bfloat16),
+                     torch.empty((1, 0, H), device="cuda"), torch.empty((1, 0, 100), device="cuda"))
+    shape0 = b.make_shape(1, 0, 100, topk=k, Hm=Hm, Dc=512, Dr=64)
+    mws0 = torch.empty(max(b.workspace_bytes(shape0, b.OP_SPARSE_MLA), 1), dtype=torch.uint8, device="cuda")
+    b.sparse_mla_attention(torch.empty((1, 0, Hm, 576), dtype=torch.bfloat16, device="cuda"),
+                           torch.randn((1, 100, 576), device="cuda").to(torch.bfloat16),
+                           torch.empty((1, 0, k), dtype=torch.int32, device="cuda"), 0.05,
+                           torch.empty((1, 0, Hm, 512), dtype=torch.bfloat16, device="cuda"), Dc=512,
+                           workspace=mws0)
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ sparse MLA
 
 def _mla_inputs(w, layer=0):
