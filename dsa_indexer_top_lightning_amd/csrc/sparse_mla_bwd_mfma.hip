@@ -10,8 +10,9 @@
 //   mla_bwd_pz     per (query, split, head group): the forward's 64-row tiles gathered into
 //                  LDS; S^T = C Q^T and dP^T = C dO^T on v_mfma_f32_32x32x16_bf16 (query and
 //                  output-gradient fragments held in registers), then dz' as bf16 into the
-//                  workspace as [query][head][slot] for dq and, on the per-slot path, P and dz'
-//                  as [query][slot][head] for mla_bwd_dc;
+//                  workspace in mla_bwd_dq's fragment order (per query, head group and
+//                  64-slot tile, one 16-byte B fragment per lane and k-step) and, on the
+//                  per-slot path, P and dz' as [query][slot][head] for mla_bwd_dc;
 //   the latent-row gradient, one of:
 //   mla_bwd_dc     per (query, split, head group): the query's 64 head rows and output
 //                  gradients in LDS; per tile dC = dz'^T Q + P^T [dO, 0] (K = heads), added to
@@ -19,7 +20,8 @@
 //   mla_bwd_dkv    dense selections (8 topk >= s_cap): per (64 latent rows, query chunk), S
 //                  and dP recomputed per query that selected any of the rows, dC summed over
 //                  the chunk in registers and added once (after bm_dense_clear and
-//                  bm_dense_scatter build the multiplicity map);
+//                  bm_dense_scatter build the multiplicity map); the chunks of an XCD take
+//                  all their tiles one chunk at a time;
 //   mla_bwd_dq     per (query, split, head group): the tiles gathered again, dq^T += C^T dz'^T.
 // Slots past the last valid entry of a row are never touched; invalid slots inside that
 // range get P = dz' = 0, so the later kernels read whole tiles without masks.
